@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer forward on one MI355X.
+
+A step is one forward of one layer (router -> top-k -> grouping by expert ->
+gate/up + SwiGLU -> down -> combine) for a batch of tokens. Steps walk through
+a stack of seeded layers (default 24), so that the experts a step reads were
+last read many steps (hundreds of MB) earlier and are not served from the
+256 MB Infinity Cache; every input is resident in HBM (or, for offloaded
+experts, in pinned host memory) before timing starts.
+
+Workloads (--workload):
+  decode    Qwen3-30B-A3B-shaped layer (H2048 I768 E128 k8 G128 bf16, Zipf bias
+            alpha 0.8), all experts in HBM; --batch 1 (default) or 4.
+  deepseek  H7168 I2048 E384 k6 G128 bf16, Zipf alpha 1.0, 70% of experts in HBM
+            and the coldest 30% read from host memory (--plan mixed | hbm | host).
+  prefill   the Qwen3 layer shape with 2048 (or --batch) tokens, bias-free routing.
+
+Prints one JSON line. value = layer-tokens/s over exactly --steps timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tokens/s + achieved HBM/host-link GB/s vs peak; prefill tok/s"
+HBM_PEAK_GBS = 8000.0
+HOST_LINK_PEAK_GBS = 63.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_dims(args):
+    if args.workload in ("decode", "prefill"):
+        return dict(H=2048, I=768, E=128, k=8, G=128, act="bf16", alpha=0.8 if args.workload == "decode" else 0.0,
+                    seed=1 if args.workload == "decode" else 4)
+    if args.workload == "deepseek":
+        return dict(H=7168, I=2048, E=384, k=6, G=128, act="bf16", alpha=1.0, seed=2)
+    raise SystemExit("unknown workload")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "deepseek", "prefill"])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--plan", default="mixed", choices=["mixed", "hbm", "host"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel sharding "
+              "is a design note, not code); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_offloaded_ffn_moe_amd as moe
+    import synth
+
+    d = workload_dims(args)
+    H, I, E, k, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "k", "G", "act", "alpha", "seed"))
+    B = args.batch or (2048 if args.workload == "prefill" else 1)
+    L = args.layers or {"decode": 24, "deepseek": 2, "prefill": 4}[args.workload]
+    eb = synth.expert_bytes(H, I, G)
+    if args.workload == "deepseek":
+        slots = {"mixed": int(round(0.7 * E)), "hbm": E, "host": 0}[args.plan]
+    else:
+        slots = E
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=slots)
+    plan = moe.Plan(cfg)
+    layers_host = []
+    t0 = time.time()
+    for l in range(L):
+        blobs = synth.expert_blobs(seed, l, 0, E, H, I, G)
+        Wr = synth.router_weight(seed, l, E, H, act)
+        b = synth.router_bias(seed, l, E, alpha)
+        res = None
+        if args.workload == "deepseek" and args.plan == "mixed":
+            res = synth.coldest_host_plan(seed, l, E, slots / E)
+        plan.load_layer(l, Wr, b, blobs, res)
+        layers_host.append((Wr, b, blobs if (not args.no_cpu and l < 2) else None))
+        log("layer %d/%d generated and loaded (%.1fs)" % (l + 1, L, time.time() - t0))
+
+    n_in = args.warmup + args.steps
+    xs_bits = [synth.activations(seed, 1000 + i, B, H, act) for i in range(min(n_in, 64))]
+    xs = [torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda() for xb in xs_bits]
+    y = torch.empty((B, H), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        plan.forward(i % L, xs[i % len(xs)], y, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan.reset_stats()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    st = plan.stats(-1)
+    log("timed %d steps in %.4fs" % (args.steps, elapsed))
+
+    # profiled pass: HIP events around each kernel on the launch stream
+    plan.profile(True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    kt = plan.kernel_times()
+    plan.profile(False)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = B * args.steps / elapsed
+    fwd = max(st["forwards"], 1)
+    bytes_hbm = st["bytes_hbm"] / fwd
+    bytes_host = st["bytes_host"] / fwd
+    expert_bytes_step = bytes_hbm + bytes_host
+
+    # dominant kernel and its algorithmic work per launch
+    per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0]) if v[0] else 0.0) for n, v in kt.items()
+                  if v[0]}
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
+    frac_bytes = {"gateup": 2.0 / 3.0, "down": 1.0 / 3.0}.get(dom, 0.0)
+    if dom in ("gateup", "down"):
+        alg = frac_bytes * expert_bytes_step
+        achieved = alg / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
+        if args.workload == "deepseek" and args.plan == "host":
+            peak, bound = HOST_LINK_PEAK_GBS, "host-link"
+        else:
+            peak, bound = HBM_PEAK_GBS, "hbm"
+        roof = dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=peak, unit="GB/s",
+                    frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(alg),
+                    avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
+    else:
+        roof = dict(bound="unknown", kernel=dom, achieved=None, peak=None, unit=None, frac=None, traffic=None)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s layer H%d I%d E%d k%d int4 G%d, batch %d, %d-layer rotation%s" % (
+            {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
+             "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload], H, I, E, k, G, B, L,
+            (", plan " + args.plan) if args.workload == "deepseek" else ""),
+            "hbm_slots": slots, "alpha": alpha, "seed": seed},
+        "roofline": roof,
+        "layer": {"expert_bytes_per_step_hbm": int(bytes_hbm), "expert_bytes_per_step_host": int(bytes_host),
+                  "unique_experts_per_step": round(expert_bytes_step / eb, 3),
+                  "layer_GBps_wall": round(expert_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+                  "hit_rate": round(st["hits"] / max(st["hits"] + st["misses"], 1), 5),
+                  "kernels_us": {n: round(v["avg_us"], 3) for n, v in per_kernel.items()}},
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args, d, B, L, layers_host, xs_bits)
+    print(json.dumps(out), flush=True)
+    plan.destroy()
+
+
+def cpu_baseline(args, d, B, L, layers_host, xs_bits):
+    """The CPU oracle (float64, unmodified) on a bounded sample of the same steps."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:
+        threads = 1
+    H, I, E, k, G, act = (d[n] for n in ("H", "I", "E", "k", "G", "act"))
+    n_layers = sum(1 for lh in layers_host if lh[2] is not None)
+    tokens, t0, i = 0, time.perf_counter(), 0
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        l = i % n_layers
+        Wr, b, blobs = layers_host[l]
+        x = O.bf16_bits_to_f64(xs_bits[i % len(xs_bits)])
+        O.layer_forward(x, O.bf16_bits_to_f64(Wr), b, blobs, H, I, E, k, G, act)
+        tokens += B
+        i += 1
+    el = time.perf_counter() - t0
+    log("cpu oracle: %d forwards in %.1fs" % (i, el))
+    return {"value": round(tokens / el, 4), "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d forwards of batch %d over %d of the %d layers (float64 NumPy oracle, %.1fs)" % (
+                i, B, n_layers, L, el)}
+
+
+if __name__ == "__main__":
+    main()

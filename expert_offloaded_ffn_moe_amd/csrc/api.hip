@@ -1,0 +1,601 @@
+// C ABI of the MoE offload library: plans, residency pools, forward dispatch and
+// the expert cache. See include/moe_offload.h for the contract of each call.
+//
+// Memory: per layer, one pinned device-mapped host pool holding every expert in
+// the internal layout (page "我在 32GB 单卡上跑两万四千专家的 MoE:分层放置实测与三个坑",
+// section "二、跑起来靠的是分层,不是激活": all experts pinned in host RAM), and
+// hbm_slots HBM slots holding copies of the resident experts. A per-layer device
+// table gives each expert's blob pointer: its HBM slot, or its host copy read in
+// place over the host link (page "763B MoE 塞进两张 96GB 显卡：闲置专家丢进主机内存",
+// sections "显存缺口从哪里来" and "同一个思路，vLLM 原生方案反而跑不通").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "host_logic.h"
+#include "kernels.h"
+#include "moe_offload.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                            \
+  do {                                                                                           \
+    hipError_t _e = (expr);                                                                      \
+    if (_e != hipSuccess)                                                                        \
+      return fail(MOE_E_HIP, std::string(#expr) + ": " + hipGetErrorString(_e));                 \
+  } while (0)
+
+struct Layer {
+  uint8_t* host_pool = nullptr;      // E * L.bytes, pinned, host VA
+  uint8_t* host_pool_dev = nullptr;  // device VA of host_pool
+  uint8_t* hbm = nullptr;            // hbm_slots * L.bytes
+  const uint8_t** d_wptr = nullptr;  // [E]
+  int32_t* d_is_host = nullptr;      // [E]
+  void* d_router_w = nullptr;        // [E][H]
+  float* d_router_b = nullptr;       // [E]
+  int64_t* d_counts_acc = nullptr;   // [E] since last cache update
+  int64_t* d_stats = nullptr;        // [ST_COUNT]
+  uint64_t* h_wptr_stage = nullptr;  // pinned [E] staging of the pointer table
+  int32_t* h_ishost_stage = nullptr; // pinned [E]
+  int64_t* h_counts_stage = nullptr; // pinned [E]
+  std::vector<int32_t> slot_of;      // host mirror
+  std::vector<double> score;
+  bool loaded = false;
+  int64_t bytes_copied = 0, promotions = 0, evictions = 0;
+};
+
+struct Workspace {
+  float* logits = nullptr;   // [Tmax][E]
+  float* xsum = nullptr;     // [Tmax][H/G]
+  int32_t* ids = nullptr;    // [Tmax*k]
+  float* wts = nullptr;      // [Tmax*k]
+  int32_t* counts = nullptr; // [E]
+  int32_t* offsets = nullptr;// [E+1]
+  int32_t* sorted = nullptr; // [Tmax*k]
+  int32_t* inv = nullptr;    // [Tmax*k]
+  int32_t* active = nullptr; // [E]
+  int32_t* n_active = nullptr;
+  void* h = nullptr;         // [Tmax*k][I] act dtype
+  float* hpart = nullptr;    // [Tmax*k][I/32]
+  float* o = nullptr;        // [Tmax*k][H]
+};
+
+}  // namespace
+
+struct moe_plan {
+  moe_config cfg{};
+  Layout L{};
+  int device = 0;
+  size_t act_size = 2;
+  std::vector<Layer> layers;
+  Workspace ws{};
+  bool profiling = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;           // recorded launches
+  std::vector<hipEvent_t> spare;   // reusable events
+  std::vector<void*> dev_allocs;   // freed with hipFree
+  std::vector<void*> host_allocs;  // freed with hipHostFree
+};
+
+namespace {
+
+moe_status dev_alloc(moe_plan* p, void** out, size_t bytes) {
+  *out = nullptr;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(out, bytes);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    (void)hipGetLastError();
+    return fail(MOE_E_NOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  p->dev_allocs.push_back(*out);
+  return MOE_OK;
+}
+
+moe_status host_alloc(moe_plan* p, void** out, size_t bytes, unsigned flags) {
+  *out = nullptr;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipHostMalloc(out, bytes, flags);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    (void)hipGetLastError();
+    return fail(MOE_E_HOST_NOMEM,
+                "hipHostMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  p->host_allocs.push_back(*out);
+  return MOE_OK;
+}
+
+void free_plan(moe_plan* p) {
+  if (!p) return;
+  (void)hipSetDevice(p->device);
+  (void)hipDeviceSynchronize();
+  for (auto& r : p->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  for (void* q : p->dev_allocs) (void)hipFree(q);
+  for (void* q : p->host_allocs) (void)hipHostFree(q);
+  delete p;
+}
+
+template <typename T>
+moe_status alloc_as(moe_plan* p, T** out, size_t count) {
+  void* v = nullptr;
+  moe_status s = dev_alloc(p, &v, count * sizeof(T));
+  *out = static_cast<T*>(v);
+  return s;
+}
+
+hipEvent_t take_event(moe_plan* p) {
+  if (!p->spare.empty()) {
+    hipEvent_t e = p->spare.back();
+    p->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with an event pair when profiling is on.
+struct KernelTimer {
+  moe_plan* p;
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  KernelTimer(moe_plan* p_, int kind_, hipStream_t s_) : p(p_), kind(kind_), s(s_) {
+    if (!p->profiling) return;
+    a = take_event(p);
+    b = take_event(p);
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~KernelTimer() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    p->recs.push_back({kind, a, b});
+  }
+};
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+// Upload the pointer table and host flags of a layer from its slot table.
+moe_status push_tables(moe_plan* p, Layer& ly, hipStream_t s) {
+  const int E = p->cfg.num_experts;
+  for (int e = 0; e < E; ++e) {
+    const int slot = ly.slot_of[e];
+    const uint8_t* ptr = slot >= 0 ? ly.hbm + (size_t)slot * p->L.bytes : ly.host_pool_dev + (size_t)e * p->L.bytes;
+    ly.h_wptr_stage[e] = reinterpret_cast<uint64_t>(ptr);
+    ly.h_ishost_stage[e] = slot >= 0 ? 0 : 1;
+  }
+  HIP_TRY(hipMemcpyAsync(ly.d_wptr, ly.h_wptr_stage, sizeof(uint64_t) * E, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(ly.d_is_host, ly.h_ishost_stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_INVALID: return "MOE_E_INVALID";
+    case MOE_E_NOMEM: return "MOE_E_NOMEM";
+    case MOE_E_HOST_NOMEM: return "MOE_E_HOST_NOMEM";
+    case MOE_E_HIP: return "MOE_E_HIP";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED";
+    case MOE_E_STATE: return "MOE_E_STATE";
+  }
+  return "MOE_E_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_expert_bytes(const moe_config* cfg, size_t* out) {
+  if (!cfg || !out) return fail(MOE_E_INVALID, "null argument");
+  const std::string why = check_config(*cfg);
+  if (!why.empty()) return fail(MOE_E_INVALID, why);
+  *out = (size_t)make_layout(cfg->hidden, cfg->inter, cfg->group_size).canonical_bytes;
+  return MOE_OK;
+}
+
+moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** out) {
+  if (!out) return fail(MOE_E_INVALID, "out is null");
+  *out = nullptr;
+  if (!cfg) return fail(MOE_E_INVALID, "cfg is null");
+  const std::string why = check_config(*cfg);
+  if (!why.empty()) return fail(MOE_E_INVALID, why);
+  (void)stream;
+
+  moe_plan* p = new moe_plan();
+  p->cfg = *cfg;
+  if (p->cfg.gemm_min_tokens == 0) p->cfg.gemm_min_tokens = 256;
+  p->L = make_layout(cfg->hidden, cfg->inter, cfg->group_size);
+  p->act_size = cfg->act_dtype == MOE_ACT_BF16 ? 2 : 4;
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return fail(MOE_E_HIP, "hipGetDevice failed");
+  }
+  const int E = cfg->num_experts, H = cfg->hidden, I = cfg->inter, k = cfg->top_k, G = cfg->group_size;
+  const size_t Tm = (size_t)cfg->max_tokens, A = Tm * k;
+  moe_status st = MOE_OK;
+#define TRY(x)          \
+  do {                  \
+    st = (x);           \
+    if (st != MOE_OK) { \
+      free_plan(p);     \
+      return st;        \
+    }                   \
+  } while (0)
+  p->layers.resize(cfg->num_layers);
+  for (auto& ly : p->layers) {
+    void* v;
+    TRY(host_alloc(p, &v, (size_t)E * p->L.bytes, hipHostMallocMapped | hipHostMallocNonCoherent));
+    ly.host_pool = static_cast<uint8_t*>(v);
+    void* dv = nullptr;
+    if (hipHostGetDevicePointer(&dv, ly.host_pool, 0) != hipSuccess) {
+      free_plan(p);
+      return fail(MOE_E_HIP, "hipHostGetDevicePointer failed");
+    }
+    ly.host_pool_dev = static_cast<uint8_t*>(dv);
+    if (cfg->hbm_slots > 0) {
+      TRY(dev_alloc(p, &v, (size_t)cfg->hbm_slots * p->L.bytes));
+      ly.hbm = static_cast<uint8_t*>(v);
+    }
+    TRY(dev_alloc(p, &v, sizeof(uint64_t) * E));
+    ly.d_wptr = static_cast<const uint8_t**>(v);
+    TRY(alloc_as(p, &ly.d_is_host, E));
+    TRY(dev_alloc(p, &ly.d_router_w, (size_t)E * H * p->act_size));
+    TRY(alloc_as(p, &ly.d_router_b, E));
+    TRY(alloc_as(p, &ly.d_counts_acc, E));
+    TRY(alloc_as(p, &ly.d_stats, ST_COUNT));
+    TRY(host_alloc(p, &v, sizeof(uint64_t) * E, 0));
+    ly.h_wptr_stage = static_cast<uint64_t*>(v);
+    TRY(host_alloc(p, &v, sizeof(int32_t) * E, 0));
+    ly.h_ishost_stage = static_cast<int32_t*>(v);
+    TRY(host_alloc(p, &v, sizeof(int64_t) * E, 0));
+    ly.h_counts_stage = static_cast<int64_t*>(v);
+    ly.slot_of.assign(E, -1);
+    ly.score.assign(E, 0.0);
+  }
+  Workspace& w = p->ws;
+  TRY(alloc_as(p, &w.logits, Tm * E));
+  TRY(alloc_as(p, &w.xsum, Tm * (H / G)));
+  TRY(alloc_as(p, &w.ids, A));
+  TRY(alloc_as(p, &w.wts, A));
+  TRY(alloc_as(p, &w.counts, E));
+  TRY(alloc_as(p, &w.offsets, E + 1));
+  TRY(alloc_as(p, &w.sorted, A));
+  TRY(alloc_as(p, &w.inv, A));
+  TRY(alloc_as(p, &w.active, E));
+  TRY(alloc_as(p, &w.n_active, 64));
+  TRY(dev_alloc(p, &w.h, A * I * p->act_size));
+  TRY(alloc_as(p, &w.hpart, A * (I / 32)));
+  TRY(alloc_as(p, &w.o, A * H));
+#undef TRY
+  if (hipDeviceSynchronize() != hipSuccess) {
+    free_plan(p);
+    return fail(MOE_E_HIP, "device synchronize after allocation failed");
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status moe_plan_load_layer(moe_plan* p, int32_t layer, const moe_layer_weights* w, moe_stream stream) {
+  if (!p || !w) return fail(MOE_E_INVALID, "null argument");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (!w->router_w || !w->experts) return fail(MOE_E_INVALID, "router_w and experts are required");
+  const int E = p->cfg.num_experts, H = p->cfg.hidden, S = p->cfg.hbm_slots;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Layer& ly = p->layers[layer];
+
+  std::vector<int32_t> slot_of(E, -1);
+  int used = 0;
+  for (int e = 0; e < E; ++e) {
+    const bool res = w->resident ? (w->resident[e] != 0) : (e < S);
+    if (res) {
+      if (used >= S) return fail(MOE_E_INVALID, "more resident experts than hbm_slots");
+      slot_of[e] = used++;
+    }
+  }
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipStreamSynchronize(s));  // no queued work may still read this layer
+
+  // repack every expert into the host pool, threads over experts
+  const Layout L = p->L;
+  const size_t cb = (size_t)L.canonical_bytes;
+  unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nth; ++t)
+    th.emplace_back([&, t] {
+      for (int e = (int)t; e < E; e += (int)nth)
+        repack_expert(L, w->experts + (size_t)e * cb, ly.host_pool + (size_t)e * L.bytes);
+    });
+  for (auto& x : th) x.join();
+
+  for (int e = 0; e < E; ++e)
+    if (slot_of[e] >= 0)
+      HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)slot_of[e] * L.bytes, ly.host_pool + (size_t)e * L.bytes, L.bytes,
+                             hipMemcpyHostToDevice, s));
+  ly.slot_of = slot_of;
+  ly.score.assign(E, 0.0);
+  moe_status st = push_tables(p, ly, s);
+  if (st != MOE_OK) return st;
+  HIP_TRY(hipMemcpyAsync(ly.d_router_w, w->router_w, (size_t)E * H * p->act_size, hipMemcpyHostToDevice, s));
+  if (w->router_b)
+    HIP_TRY(hipMemcpyAsync(ly.d_router_b, w->router_b, sizeof(float) * E, hipMemcpyHostToDevice, s));
+  else
+    HIP_TRY(hipMemsetAsync(ly.d_router_b, 0, sizeof(float) * E, s));
+  HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
+  HIP_TRY(hipMemsetAsync(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  ly.bytes_copied = ly.promotions = ly.evictions = 0;
+  ly.loaded = true;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
+                             const moe_routing* ro, moe_stream stream) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (T < 0 || T > p->cfg.max_tokens) return fail(MOE_E_INVALID, "T out of range 0..max_tokens");
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_E_INVALID, "x and y are required");
+  if (!aligned16(x) || !aligned16(y) || (logits_in && !aligned16(logits_in)))
+    return fail(MOE_E_INVALID, "x, y and logits_in must be 16-byte aligned");
+  Layer& ly = p->layers[layer];
+  if (!ly.loaded) return fail(MOE_E_INVALID, "layer not loaded");
+  const moe_config& c = p->cfg;
+  const int E = c.num_experts, H = c.hidden, I = c.inter, k = c.top_k, G = c.group_size;
+  const int bf16 = c.act_dtype == MOE_ACT_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace& w = p->ws;
+  const int A = T * k;
+
+  // router logits and per-group activation sums
+  RouterArgs ra{};
+  ra.x = x;
+  ra.w = ly.d_router_w;
+  ra.b = ly.d_router_b;
+  ra.logits = w.logits;
+  ra.xsum = bf16 ? w.xsum : nullptr;
+  ra.T = T;
+  ra.H = H;
+  ra.E = E;
+  ra.G = G;
+  ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
+  {
+    KernelTimer kt(p, MOE_K_ROUTER, s);
+    launch_router(ra, bf16, s);
+  }
+  const float* logits = logits_in ? logits_in : w.logits;
+
+  RouteArgs rt{};
+  rt.logits = logits;
+  rt.ids = w.ids;
+  rt.wts = w.wts;
+  rt.counts = w.counts;
+  rt.offsets = w.offsets;
+  rt.sorted = w.sorted;
+  rt.inv = w.inv;
+  rt.active = w.active;
+  rt.n_active = w.n_active;
+  rt.is_host = ly.d_is_host;
+  rt.counts_acc = ly.d_counts_acc;
+  rt.stats = ly.d_stats;
+  rt.expert_bytes = p->L.canonical_bytes;
+  rt.T = T;
+  rt.E = E;
+  rt.k = k;
+  {
+    KernelTimer kt(p, MOE_K_ROUTE, s);
+    if (A <= kRouteSmallMaxAssign && T <= 64) {
+      launch_route_small(rt, s);
+    } else {
+      launch_topk(rt, s);
+      launch_align(rt, s);
+    }
+  }
+
+  const int max_act = std::min(E, A);
+  GemvArgs ga{};
+  ga.wptr = ly.d_wptr;
+  ga.active = w.active;
+  ga.n_active = w.n_active;
+  ga.offsets = w.offsets;
+  ga.sorted = w.sorted;
+  ga.in = x;
+  ga.insum = w.xsum;
+  ga.out = w.h;
+  ga.outpart = w.hpart;
+  ga.off_codes = p->L.off_gu_codes;
+  ga.off_scales = p->L.off_gu_scales;
+  ga.chunks = (int)p->L.gu_chunks;
+  ga.gblocks = (int)p->L.gu_gblocks;
+  ga.tiles = (int)p->L.gu_tiles;
+  ga.H = H;
+  ga.I = I;
+  ga.G = G;
+  ga.k = k;
+  {
+    KernelTimer kt(p, MOE_K_GATEUP, s);
+    launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, s);
+  }
+
+  GemvArgs da = ga;
+  da.in = w.h;
+  da.insum = w.hpart;
+  da.out = w.o;
+  da.outpart = nullptr;
+  da.off_codes = p->L.off_dn_codes;
+  da.off_scales = p->L.off_dn_scales;
+  da.chunks = (int)p->L.dn_chunks;
+  da.gblocks = (int)p->L.dn_gblocks;
+  da.tiles = (int)p->L.dn_tiles;
+  {
+    KernelTimer kt(p, MOE_K_DOWN, s);
+    launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, s);
+  }
+
+  CombineArgs ca{};
+  ca.o = w.o;
+  ca.wts = w.wts;
+  ca.inv = w.inv;
+  ca.y = y;
+  ca.T = T;
+  ca.H = H;
+  ca.k = k;
+  {
+    KernelTimer kt(p, MOE_K_COMBINE, s);
+    launch_combine(ca, s);
+  }
+  HIP_TRY(hipGetLastError());
+
+  if (ro) {
+    if (ro->logits) HIP_TRY(hipMemcpyAsync(ro->logits, logits, sizeof(float) * T * E, hipMemcpyDeviceToDevice, s));
+    if (ro->topk_ids) HIP_TRY(hipMemcpyAsync(ro->topk_ids, w.ids, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, s));
+    if (ro->topk_w) HIP_TRY(hipMemcpyAsync(ro->topk_w, w.wts, sizeof(float) * A, hipMemcpyDeviceToDevice, s));
+    if (ro->counts) HIP_TRY(hipMemcpyAsync(ro->counts, w.counts, sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s));
+    if (ro->offsets)
+      HIP_TRY(hipMemcpyAsync(ro->offsets, w.offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, s));
+    if (ro->sorted) HIP_TRY(hipMemcpyAsync(ro->sorted, w.sorted, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, s));
+    if (ro->inv) HIP_TRY(hipMemcpyAsync(ro->inv, w.inv, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* pol, moe_stream stream) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (layer < -1 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (p->cfg.hbm_slots == 0) return fail(MOE_E_STATE, "plan has no HBM slots to cache experts in");
+  const double decay = pol ? pol->decay : 0.9;
+  const int maxp = pol ? pol->max_promotions : 8;
+  if (!(decay >= 0.0 && decay <= 1.0) || maxp < 0) return fail(MOE_E_INVALID, "bad policy");
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? p->cfg.num_layers : layer + 1;
+  for (int l = l0; l < l1; ++l)
+    if (!p->layers[l].loaded) return fail(MOE_E_INVALID, "layer not loaded");
+  const int E = p->cfg.num_experts;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(p->device));
+  for (int l = l0; l < l1; ++l) {
+    Layer& ly = p->layers[l];
+    HIP_TRY(hipMemcpyAsync(ly.h_counts_stage, ly.d_counts_acc, sizeof(int64_t) * E, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  std::vector<Promotion> promoted;
+  std::vector<int32_t> evicted;
+  for (int l = l0; l < l1; ++l) {
+    Layer& ly = p->layers[l];
+    cache_policy_step(E, p->cfg.hbm_slots, decay, maxp, ly.h_counts_stage, ly.score.data(), ly.slot_of.data(),
+                      &promoted, &evicted);
+    if (promoted.empty()) continue;
+    for (const Promotion& pr : promoted) {
+      HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)pr.slot * p->L.bytes, ly.host_pool + (size_t)pr.expert * p->L.bytes,
+                             p->L.bytes, hipMemcpyHostToDevice, s));
+      ly.bytes_copied += p->L.canonical_bytes;
+    }
+    ly.promotions += (int64_t)promoted.size();
+    ly.evictions += (int64_t)evicted.size();
+    moe_status st = push_tables(p, ly, s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_plan_stats(moe_plan* p, int32_t layer, moe_stats* out) {
+  if (!p || !out) return fail(MOE_E_INVALID, "null argument");
+  if (layer < -1 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipDeviceSynchronize());
+  std::memset(out, 0, sizeof(*out));
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? p->cfg.num_layers : layer + 1;
+  for (int l = l0; l < l1; ++l) {
+    Layer& ly = p->layers[l];
+    int64_t st[ST_COUNT];
+    HIP_TRY(hipMemcpy(st, ly.d_stats, sizeof(st), hipMemcpyDeviceToHost));
+    out->forwards += st[ST_FORWARDS];
+    out->tokens += st[ST_TOKENS];
+    out->hits += st[ST_HITS];
+    out->misses += st[ST_MISSES];
+    out->bytes_hbm += st[ST_BYTES_HBM];
+    out->bytes_host += st[ST_BYTES_HOST];
+    out->bytes_copied += ly.bytes_copied;
+    out->promotions += ly.promotions;
+    out->evictions += ly.evictions;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_plan_reset_stats(moe_plan* p) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipDeviceSynchronize());
+  for (Layer& ly : p->layers) {
+    HIP_TRY(hipMemset(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT));
+    ly.bytes_copied = ly.promotions = ly.evictions = 0;
+  }
+  HIP_TRY(hipDeviceSynchronize());
+  return MOE_OK;
+}
+
+moe_status moe_plan_residency(moe_plan* p, int32_t layer, int32_t* slot_of) {
+  if (!p || !slot_of) return fail(MOE_E_INVALID, "null argument");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  const auto& v = p->layers[layer].slot_of;
+  std::copy(v.begin(), v.end(), slot_of);
+  return MOE_OK;
+}
+
+moe_status moe_plan_profile(moe_plan* p, int32_t enable) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (enable) {
+    HIP_TRY(hipDeviceSynchronize());
+    for (auto& r : p->recs) {
+      p->spare.push_back(r.a);
+      p->spare.push_back(r.b);
+    }
+    p->recs.clear();
+  }
+  p->profiling = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_plan_kernel_times(moe_plan* p, moe_kernel_times* out) {
+  if (!p || !out) return fail(MOE_E_INVALID, "null argument");
+  std::memset(out, 0, sizeof(*out));
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipDeviceSynchronize());
+  for (auto& r : p->recs) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    if (r.kind >= 0 && r.kind < MOE_K_COUNT) {
+      out->launches[r.kind] += 1;
+      out->total_ms[r.kind] += ms;
+    }
+  }
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan* p) { free_plan(p); }
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+#include "host_logic.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+
+namespace moe {
+
+static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+Layout make_layout(int64_t H, int64_t I, int64_t G) {
+  Layout L;
+  L.H = H;
+  L.I = I;
+  L.G = G;
+  L.gu_tiles = I / 32;
+  L.gu_chunks = H / 32;
+  L.gu_gblocks = (H / G + 7) / 8;
+  L.dn_tiles = H / 64;
+  L.dn_chunks = I / 32;
+  L.dn_gblocks = (I / G + 7) / 8;
+  int64_t off = 0;
+  L.off_gu_codes = off;
+  off = round_up(off + L.gu_tiles * L.gu_chunks * 1024, 256);
+  L.off_gu_scales = off;
+  off = round_up(off + L.gu_tiles * L.gu_gblocks * 1024, 256);
+  L.off_dn_codes = off;
+  off = round_up(off + L.dn_tiles * L.dn_chunks * 1024, 256);
+  L.off_dn_scales = off;
+  off = round_up(off + L.dn_tiles * L.dn_gblocks * 1024, 256);
+  L.bytes = off;
+  L.canonical_bytes = 3 * H * I / 2 + 6 * H * I / G;
+  return L;
+}
+
+std::string check_config(const moe_config& c) {
+  if (c.hidden <= 0 || c.inter <= 0) return "hidden and inter must be positive";
+  if (c.group_size <= 0 || c.group_size % 32) return "group_size must be a positive multiple of 32";
+  if (c.hidden % 64) return "hidden must be a multiple of 64";
+  if (c.inter % 32) return "inter must be a multiple of 32";
+  if (c.hidden % c.group_size) return "hidden must be a multiple of group_size";
+  if (c.inter % c.group_size) return "inter must be a multiple of group_size";
+  if (c.num_experts < 1 || c.num_experts > 1024) return "num_experts must be in 1..1024";
+  if (c.top_k < 1 || c.top_k > c.num_experts || c.top_k > 32) return "top_k must be in 1..min(num_experts, 32)";
+  if (c.num_layers < 1) return "num_layers must be >= 1";
+  if (c.act_dtype != MOE_ACT_F32 && c.act_dtype != MOE_ACT_BF16) return "act_dtype must be MOE_ACT_F32 or MOE_ACT_BF16";
+  if (c.max_tokens < 1 || c.max_tokens > (1 << 20)) return "max_tokens must be in 1..2^20";
+  if ((int64_t)c.max_tokens * c.top_k > (1 << 22)) return "max_tokens * top_k must be <= 2^22";
+  if (c.hbm_slots < 0 || c.hbm_slots > c.num_experts) return "hbm_slots must be in 0..num_experts";
+  if (c.hidden > 65536 || c.inter > 65536) return "hidden and inter must be <= 65536";
+  return "";
+}
+
+// One internal dword from 4 canonical bytes (8 consecutive K values): canonical
+// byte j holds offsets 2j (low nibble) and 2j+1 (high nibble); the internal
+// dword wants offset 2j at bits [4j, 4j+4) and 2j+1 at bits [16+4j, 20+4j),
+// each as n = q + 8, which for a two's complement nibble is the nibble XOR 8.
+static inline uint32_t internal_dword(uint32_t w) {
+  uint32_t lo = w & 0x0F0F0F0Fu;
+  lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+  lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  hi = (hi | (hi >> 4)) & 0x00FF00FFu;
+  hi = (hi | (hi >> 8)) & 0x0000FFFFu;
+  return (lo | (hi << 16)) ^ 0x88888888u;
+}
+
+// 16 internal bytes from the 16 canonical bytes of one row's K chunk.
+static inline void chunk16(const uint8_t* src, uint8_t* dst) {
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w;
+    std::memcpy(&w, src + 4 * d, 4);
+    w = internal_dword(w);
+    std::memcpy(dst + 4 * d, &w, 4);
+  }
+}
+
+void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
+  const int64_t H = L.H, I = L.I, G = L.G;
+  const uint8_t* q_gate = canon;
+  const uint8_t* q_up = q_gate + I * H / 2;
+  const uint8_t* q_down = q_up + I * H / 2;
+  const uint16_t* s_gate = reinterpret_cast<const uint16_t*>(q_down + H * I / 2);
+  const uint16_t* s_up = s_gate + I * (H / G);
+  const uint16_t* s_down = s_up + I * (H / G);
+  std::memset(out, 0, (size_t)L.bytes);
+
+  // gate/up codes and scales
+  for (int64_t t = 0; t < L.gu_tiles; ++t) {
+    for (int lane = 0; lane < 64; ++lane) {
+      const bool up = lane >= 32;
+      const int64_t row = 32 * t + (lane & 31);
+      const uint8_t* src = (up ? q_up : q_gate) + row * (H / 2);
+      for (int64_t c = 0; c < L.gu_chunks; ++c)
+        chunk16(src + 16 * c, out + L.off_gu_codes + ((t * L.gu_chunks + c) * 64 + lane) * 16);
+      const uint16_t* srow = (up ? s_up : s_gate) + row * (H / G);
+      for (int64_t g = 0; g < H / G; ++g) {
+        uint8_t* dst = out + L.off_gu_scales + ((t * L.gu_gblocks + g / 8) * 64 + lane) * 16 + 2 * (g % 8);
+        std::memcpy(dst, srow + g, 2);
+      }
+    }
+  }
+  // down codes and scales
+  for (int64_t t = 0; t < L.dn_tiles; ++t) {
+    for (int lane = 0; lane < 64; ++lane) {
+      const int64_t row = 64 * t + lane;
+      const uint8_t* src = q_down + row * (I / 2);
+      for (int64_t c = 0; c < L.dn_chunks; ++c)
+        chunk16(src + 16 * c, out + L.off_dn_codes + ((t * L.dn_chunks + c) * 64 + lane) * 16);
+      const uint16_t* srow = s_down + row * (I / G);
+      for (int64_t g = 0; g < I / G; ++g) {
+        uint8_t* dst = out + L.off_dn_scales + ((t * L.dn_gblocks + g / 8) * 64 + lane) * 16 + 2 * (g % 8);
+        std::memcpy(dst, srow + g, 2);
+      }
+    }
+  }
+}
+
+void cache_policy_step(int32_t E, int32_t n_slots, double decay, int32_t max_promotions,
+                       const int64_t* counts, double* score, int32_t* slot_of,
+                       std::vector<Promotion>* promoted, std::vector<int32_t>* evicted) {
+  promoted->clear();
+  evicted->clear();
+  for (int32_t e = 0; e < E; ++e) score[e] = decay * score[e] + (double)counts[e];
+
+  std::vector<int32_t> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    if (score[a] != score[b]) return score[a] > score[b];
+    bool ra = slot_of[a] >= 0, rb = slot_of[b] >= 0;
+    if (ra != rb) return ra;
+    return a < b;
+  });
+  std::vector<char> wanted(E, 0);
+  for (int32_t i = 0; i < n_slots && i < E; ++i) wanted[order[i]] = 1;
+
+  std::vector<int32_t> promos, victims;
+  for (int32_t e = 0; e < E; ++e) {
+    if (wanted[e] && slot_of[e] < 0) promos.push_back(e);
+    if (!wanted[e] && slot_of[e] >= 0) victims.push_back(e);
+  }
+  std::sort(promos.begin(), promos.end(), [&](int32_t a, int32_t b) {
+    if (score[a] != score[b]) return score[a] > score[b];
+    return a < b;
+  });
+  std::sort(victims.begin(), victims.end(), [&](int32_t a, int32_t b) {
+    if (score[a] != score[b]) return score[a] < score[b];
+    return a > b;
+  });
+  std::vector<char> used(n_slots > 0 ? n_slots : 0, 0);
+  for (int32_t e = 0; e < E; ++e)
+    if (slot_of[e] >= 0 && slot_of[e] < n_slots) used[slot_of[e]] = 1;
+  int32_t next_free = 0;
+  size_t vi = 0;
+  int32_t n = 0;
+  for (int32_t p : promos) {
+    if (n >= max_promotions) break;
+    while (next_free < n_slots && used[next_free]) ++next_free;
+    int32_t slot;
+    if (next_free < n_slots) {
+      slot = next_free;
+      used[slot] = 1;
+    } else if (vi < victims.size()) {
+      int32_t v = victims[vi++];
+      slot = slot_of[v];
+      slot_of[v] = -1;
+      evicted->push_back(v);
+    } else {
+      break;
+    }
+    slot_of[p] = slot;
+    promoted->push_back({p, slot});
+    ++n;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+// Host-side logic of the MoE offload library that needs no GPU: configuration
+// checks, the internal expert layout and the canonical -> internal repack, and
+// the expert-cache policy. Built into the library and, on its own with g++,
+// into the CPU unit tests.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "moe_offload.h"
+
+namespace moe {
+
+// Internal expert layout (all regions 256-byte aligned inside one blob).
+//
+// Gate/up codes: tiles of 32 output positions; tile t, chunk c (32 values of K=H)
+// is a 1 KiB block of 64 lanes x 16 bytes. Lane l < 32 holds gate row 32t+l,
+// lane l >= 32 up row 32t+l-32, K range [32c, 32c+32).
+// Down codes: tiles of 64 output rows; tile t, chunk c (32 values of K=I) is a
+// 1 KiB block, lane l holds row 64t+l.
+// Inside a lane's 16 bytes, dword d covers K offsets [8d, 8d+8): the value at
+// offset 8d+2j sits in bits [4j, 4j+4), at 8d+2j+1 in bits [16+4j, 20+4j),
+// stored as n = q + 8 (0..15).
+// Scales: per tile, blocks of 8 groups: lane l's 16 bytes are the fp16 scales
+// of groups [8b, 8b+8) of its row (zero past the last group).
+struct Layout {
+  int64_t H = 0, I = 0, G = 0;
+  int64_t gu_tiles = 0, gu_chunks = 0, gu_gblocks = 0;
+  int64_t dn_tiles = 0, dn_chunks = 0, dn_gblocks = 0;
+  int64_t off_gu_codes = 0, off_gu_scales = 0, off_dn_codes = 0, off_dn_scales = 0;
+  int64_t bytes = 0;            // internal blob size (multiple of 256)
+  int64_t canonical_bytes = 0;  // 3*H*I/2 + 6*H*I/G
+};
+
+Layout make_layout(int64_t H, int64_t I, int64_t G);
+
+// Checks cfg; returns an empty string when valid, else the reason.
+std::string check_config(const moe_config& c);
+
+// canonical blob (layout documented in moe_offload.h) -> internal blob of L.bytes
+void repack_expert(const Layout& L, const uint8_t* canonical, uint8_t* internal);
+
+// One expert-cache update (frequency policy).
+//   score[e] <- decay * score[e] + counts[e]
+//   wanted: the first n_slots experts ordered by (score desc, resident first, id asc)
+//   promotions: wanted non-residents ordered by (score desc, id asc), at most
+//     max_promotions; each takes the lowest empty slot while one is left, else the
+//     slot of the next victim, victims being residents not wanted, ordered by
+//     (score asc, id desc).
+// slot_of[e] is the HBM slot of e or -1. Updates score and slot_of in place.
+struct Promotion {
+  int32_t expert, slot;
+};
+void cache_policy_step(int32_t E, int32_t n_slots, double decay, int32_t max_promotions,
+                       const int64_t* counts, double* score, int32_t* slot_of,
+                       std::vector<Promotion>* promoted, std::vector<int32_t>* evicted);
+
+}  // namespace moe

@@ -1,0 +1,74 @@
+// Internal kernel interface of the MoE offload library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+// Device counters per layer, int64 each.
+enum StatIndex { ST_FORWARDS = 0, ST_TOKENS, ST_HITS, ST_MISSES, ST_BYTES_HBM, ST_BYTES_HOST, ST_COUNT };
+
+struct RouterArgs {
+  const void* x;         // [T][H] act dtype
+  const void* w;         // [E][H] act dtype
+  const float* b;        // [E] or null
+  float* logits;         // [T][E]
+  float* xsum;           // [T][H/G] sums of x over each group (bf16 path), or null
+  int T, H, E, G;
+  int router_blocks;     // blocks [0, router_blocks) compute logits, the rest xsum
+};
+
+struct RouteArgs {
+  const float* logits;      // [T][E]
+  int32_t* ids;             // [T*k]
+  float* wts;               // [T*k]
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* sorted;          // [T*k]
+  int32_t* inv;             // [T*k]
+  int32_t* active;          // [E] experts with counts > 0: host-read ones first, then ascending id
+  int32_t* n_active;        // [1]
+  const int32_t* is_host;   // [E] 1 = expert read from host memory
+  int64_t* counts_acc;      // [E] per-layer assignment counts since the last cache update
+  int64_t* stats;           // [ST_COUNT]
+  int64_t expert_bytes;     // canonical bytes per expert (stats)
+  int T, E, k;
+};
+
+struct GemvArgs {
+  const uint8_t* const* wptr;  // [E] internal expert blobs (HBM slot or host-mapped copy)
+  const int32_t* active;       // [E]
+  const int32_t* n_active;     // [1]
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted;       // [T*k]
+  const void* in;              // gate/up: x [T][H]; down: h [T*k][I] (rows by sorted position)
+  const float* insum;          // gate/up: xsum [T][H/G]; down: hpart [T*k][I/32] (bf16 path)
+  void* out;                   // gate/up: h [T*k][I] act dtype; down: o [T*k][H] fp32
+  float* outpart;              // gate/up: hpart [T*k][I/32] (bf16 path); down: unused
+  int64_t off_codes, off_scales;
+  int chunks, gblocks;         // K chunks of 32 and scale blocks per tile
+  int tiles;                   // tiles per expert
+  int H, I, G, k;
+};
+
+struct CombineArgs {
+  const float* o;       // [T*k][H]
+  const float* wts;     // [T*k]
+  const int32_t* inv;   // [T*k]
+  float* y;             // [T][H]
+  int T, H, k;
+};
+
+void launch_router(const RouterArgs& a, int act_bf16, hipStream_t s);
+void launch_route_small(const RouteArgs& a, hipStream_t s);  // T*k small: one workgroup
+void launch_topk(const RouteArgs& a, hipStream_t s);         // any T: many workgroups
+void launch_align(const RouteArgs& a, hipStream_t s);        // after launch_topk
+void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, hipStream_t s);
+void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, hipStream_t s);
+void launch_combine(const CombineArgs& a, hipStream_t s);
+
+constexpr int kRouteSmallMaxAssign = 1024;  // T*k handled by launch_route_small
+
+}  // namespace moe

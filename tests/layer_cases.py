@@ -1,0 +1,104 @@
+"""Seeded layer cases shared by the GPU parity tests and the smoke check.
+
+Inputs come from the seeded generator (synth); expected values from the CPU
+oracle only. Nothing here calls the GPU library.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import synth
+from oracle import moe_oracle as O
+
+REL_L2_BAR = 1e-3
+MAX_ABS_BAR = 2e-2
+
+
+@dataclasses.dataclass
+class Case:
+    H: int
+    I: int
+    E: int
+    k: int
+    G: int
+    act: str
+    T: int
+    seed: int
+    alpha: float = 0.0
+    layer: int = 0
+    x_bits: np.ndarray = None    # [T, H] act storage (uint16 bf16 bits or float32)
+    x: np.ndarray = None         # [T, H] float64 values
+    Wr_store: np.ndarray = None  # [E, H] act storage
+    Wr: np.ndarray = None        # [E, H] float64 values
+    b: np.ndarray = None         # [E] float32
+    blobs: np.ndarray = None     # [E, expert_bytes] uint8
+
+
+def make_case(H, I, E, k, G, act, T, seed, alpha=0.0, layer=0, std=0.02, only_experts=None, x_stream=0):
+    """A seeded layer. only_experts: if given, only those experts get generated weights;
+    every other expert is filled with seeded random bytes (valid codes, finite scales)
+    so that reading a wrong expert changes the result."""
+    c = Case(H, I, E, k, G, act, T, seed, alpha, layer)
+    c.x_bits = synth.activations(seed, x_stream, T, H, act, sub=layer)
+    c.Wr_store = synth.router_weight(seed, layer, E, H, act)
+    if act == "bf16":
+        c.x = O.bf16_bits_to_f64(c.x_bits)
+        c.Wr = O.bf16_bits_to_f64(c.Wr_store)
+    else:
+        c.x = c.x_bits.astype(np.float64)
+        c.Wr = c.Wr_store.astype(np.float64)
+    c.b = synth.router_bias(seed, layer, E, alpha)
+    eb = synth.expert_bytes(H, I, G)
+    if only_experts is None:
+        c.blobs = synth.expert_blobs(seed, layer, 0, E, H, I, G, std)
+    else:
+        rng = np.random.default_rng(seed * 7919 + layer)
+        c.blobs = rng.integers(0, 256, size=(E, eb), dtype=np.uint8)
+        lay, _ = O.expert_layout(H, I, G)
+        # finite, small scales in the filler experts
+        a0 = lay["s_gate"][0]
+        c.blobs[:, a0:] = np.frombuffer(np.full((E * (eb - a0)) // 2, 0x2000, np.uint16).tobytes(),
+                                        np.uint8).reshape(E, eb - a0)
+        for e in sorted(set(int(v) for v in only_experts)):
+            c.blobs[e] = synth.expert_blobs(seed, layer, e, 1, H, I, G, std)[0]
+    return c
+
+
+def oracle_logits(c: Case) -> np.ndarray:
+    return O.router_logits(c.x, c.Wr, c.b)
+
+
+def oracle_forward(c: Case, logits_in=None, tokens=None):
+    return O.layer_forward(c.x, c.Wr, c.b, c.blobs, c.H, c.I, c.E, c.k, c.G, c.act, logits_in=logits_in,
+                           tokens=tokens)
+
+
+def rel_l2(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_abs(a, ref):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(ref, np.float64))))
+
+
+def routing_margins(logits: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the smallest gap among the k+1 largest logits (ordering and cut)."""
+    s = -np.sort(-np.asarray(logits, np.float64), axis=1)
+    kk = min(k + 1, s.shape[1])
+    return np.min(s[:, :kk - 1] - s[:, 1:kk], axis=1) if kk > 1 else np.full(s.shape[0], np.inf)
+
+
+def valid_topk(logits_row, ids, k, tol):
+    """ids (slot order) is the top-k of some logits within tol of logits_row."""
+    l = np.asarray(logits_row, np.float64)
+    sel = np.asarray(ids)
+    if len(set(sel.tolist())) != k:
+        return False
+    rest = np.setdiff1d(np.arange(l.size), sel)
+    if rest.size and l[sel].min() < l[rest].max() - 2 * tol:
+        return False
+    return bool(np.all(np.diff(l[sel]) <= 2 * tol))

@@ -1,0 +1,60 @@
+"""The C-ABI library loads and exports every symbol its header declares; calls
+that need no GPU (sizes, validation, status strings) work on the CPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_offloaded_ffn_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            txt = open(os.path.join(inc, f)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(moe_\w+)\s*\(", txt))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("library not built: run __graft_entry__.build()")
+    return moe.load_library(with_torch=False)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_expert_bytes_and_validation(lib):
+    for (H, I, G, want) in [(256, 128, 32, 55296), (2048, 768, 128, 2433024), (7168, 2048, 128, 22708224)]:
+        assert moe.expert_bytes(moe.make_config(H, I, 8, 2, G)) == want
+    bad = [moe.make_config(250, 128, 8, 2, 32), moe.make_config(256, 128, 8, 9, 32),
+           moe.make_config(256, 128, 8, 2, 48), moe.make_config(256, 128, 2000, 2, 32),
+           moe.make_config(256, 100, 8, 2, 32), moe.make_config(256, 128, 8, 2, 32, max_tokens=0),
+           moe.make_config(256, 128, 8, 2, 32, hbm_slots=9)]
+    for cfg in bad:
+        out = ctypes.c_size_t()
+        assert lib.moe_expert_bytes(ctypes.byref(cfg), ctypes.byref(out)) == moe.MOE_E_INVALID
+        h = ctypes.c_void_p(1)
+        assert lib.moe_plan_create(ctypes.byref(cfg), None, ctypes.byref(h)) == moe.MOE_E_INVALID
+        assert h.value is None
+        assert len(lib.moe_last_error()) > 0
+
+
+def test_status_strings_and_null_args(lib):
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(4) == b"MOE_E_HIP"
+    assert lib.moe_layer_forward(None, 0, 1, None, None, None, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_cache_update(None, 0, None, None) == moe.MOE_E_INVALID
+    lib.moe_plan_destroy(None)

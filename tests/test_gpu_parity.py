@@ -1,0 +1,221 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integers (ids, counts, offsets, permutation, counters) are compared bit-exactly,
+with the oracle's own logits fed to the library (logits_in) so both sides route
+from the same values. Floats: y within rel-L2 1e-3 and max-abs 2e-2 of the
+oracle's float64 result. With the library's own router, ids are compared where
+the oracle's routing margin exceeds the logit error, and checked for validity
+elsewhere.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import layer_cases as LC
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import expert_offloaded_ffn_moe_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.load_library()
+    return m
+
+
+def dev_x(c):
+    if c.act == "bf16":
+        return torch.from_numpy(c.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(c.x_bits.copy()).cuda()
+
+
+def make_plan(moe, c, hbm_slots=None, resident=None, max_tokens=None, layers=1, gemm_min_tokens=0):
+    cfg = moe.make_config(c.H, c.I, c.E, c.k, c.G, c.act, num_layers=layers,
+                          max_tokens=max_tokens or max(c.T, 1),
+                          hbm_slots=c.E if hbm_slots is None else hbm_slots, gemm_min_tokens=gemm_min_tokens)
+    plan = moe.Plan(cfg)
+    plan.load_layer(0, c.Wr_store, c.b, c.blobs, resident)
+    return plan
+
+
+def route_bufs(c):
+    A = c.T * c.k
+    z = lambda n, dt=torch.int32: torch.full((n,), -7, dtype=dt, device="cuda")
+    return dict(logits=torch.zeros(c.T * c.E, device="cuda"), topk_ids=z(A), topk_w=z(A, torch.float32),
+                counts=z(c.E), offsets=z(c.E + 1), sorted=z(A), inv=z(A))
+
+
+def run(plan, c, logits_in=None, route=None):
+    x = dev_x(c)
+    y = torch.full((c.T, c.H), float("nan"), device="cuda")
+    li = None if logits_in is None else torch.from_numpy(np.ascontiguousarray(logits_in, np.float32)).cuda()
+    plan.forward(0, x, y, logits_in=li, route=route)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def check_routing_exact(c, ref, rb):
+    A = c.T * c.k
+    np.testing.assert_array_equal(rb["topk_ids"].cpu().numpy().reshape(c.T, c.k), ref["ids"])
+    np.testing.assert_array_equal(rb["counts"].cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(rb["offsets"].cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(rb["sorted"].cpu().numpy(), ref["sorted"])
+    np.testing.assert_array_equal(rb["inv"].cpu().numpy(), ref["inv"])
+    w = rb["topk_w"].cpu().numpy().reshape(c.T, c.k).astype(np.float64)
+    np.testing.assert_allclose(w, ref["w"], rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    assert A == ref["sorted"].size
+
+
+def check_y(y, ref_y, label):
+    r, m = LC.rel_l2(y, ref_y), LC.max_abs(y, ref_y)
+    _say("  %s: rel_l2=%.3e max_abs=%.3e" % (label, r, m))
+    assert np.all(np.isfinite(y))
+    assert r <= LC.REL_L2_BAR, (label, r)
+    assert m <= LC.MAX_ABS_BAR, (label, m)
+
+
+# ----------------------------------------------------------------------------- shapes
+
+SMALL = [
+    # H, I, E, k, G, act, T, alpha, seed
+    (256, 128, 8, 2, 32, "f32", 16, 0.0, 0),     # the tiny reference layer
+    (384, 96, 12, 3, 32, "bf16", 13, 0.5, 11),   # several tiles, ragged group split, bf16
+    (384, 96, 12, 3, 32, "f32", 7, 0.5, 12),
+    (512, 256, 16, 16, 128, "bf16", 5, 0.0, 13),  # k = E
+    (256, 64, 5, 1, 64, "bf16", 9, 0.0, 14),     # k = 1
+    (2048, 768, 128, 8, 128, "bf16", 1, 0.8, 1),  # Qwen3-30B-A3B-shaped, decode batch 1
+    (2048, 768, 128, 8, 128, "bf16", 4, 0.8, 1),  # and batch 4
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,G,act,T,alpha,seed", SMALL)
+def test_layer_parity_oracle_logits(moe, H, I, E, k, G, act, T, alpha, seed):
+    _say("case", H, I, E, k, G, act, T, alpha, seed)
+    c = LC.make_case(H, I, E, k, G, act, T, seed, alpha)
+    lg = LC.oracle_logits(c)
+    ref = LC.oracle_forward(c, logits_in=lg)
+    plan = make_plan(moe, c)
+    rb = route_bufs(c)
+    y = run(plan, c, logits_in=lg, route=rb)
+    check_routing_exact(c, ref, rb)
+    np.testing.assert_array_equal(rb["logits"].cpu().numpy().reshape(T, E), lg)
+    check_y(y, ref["y"], "y")
+    plan.destroy()
+
+
+@pytest.mark.parametrize("H,I,E,k,G,act,T,alpha,seed", SMALL)
+def test_layer_parity_gpu_router(moe, H, I, E, k, G, act, T, alpha, seed):
+    _say("case", H, I, E, k, G, act, T, alpha, seed)
+    c = LC.make_case(H, I, E, k, G, act, T, seed, alpha)
+    ref = LC.oracle_forward(c)
+    plan = make_plan(moe, c)
+    rb = route_bufs(c)
+    y = run(plan, c, route=rb)
+    glog = rb["logits"].cpu().numpy().reshape(T, E).astype(np.float64)
+    err = np.abs(glog - ref["logits"]).max()
+    scale = np.abs(ref["logits"]).max()
+    _say("  logits max err %.3e (max |l| %.3f)" % (err, scale))
+    assert err <= 1e-5 * max(1.0, scale)
+    tol = 1e-5 * max(1.0, scale)
+    margins = LC.routing_margins(ref["logits"], k)
+    ids = rb["topk_ids"].cpu().numpy().reshape(T, k)
+    clear = margins > 2 * tol
+    np.testing.assert_array_equal(ids[clear], ref["ids"][clear])
+    for t in np.nonzero(~clear)[0]:
+        assert LC.valid_topk(ref["logits"][t], ids[t], k, tol)
+    check_y(y[clear], ref["y"][clear], "y (unambiguous tokens %d/%d)" % (clear.sum(), T))
+    plan.destroy()
+
+
+def test_all_tokens_one_expert_multi_pass(moe):
+    """Every token routed to the same k experts: one expert gets T > 8 tokens (several passes)."""
+    c = LC.make_case(384, 96, 12, 3, 32, "bf16", 21, 21)
+    lg = np.tile(np.array([0.0] * 9 + [3.0, 2.0, 1.0], np.float32), (c.T, 1))
+    ref = LC.oracle_forward(c, logits_in=lg)
+    plan = make_plan(moe, c)
+    rb = route_bufs(c)
+    y = run(plan, c, logits_in=lg, route=rb)
+    check_routing_exact(c, ref, rb)
+    check_y(y, ref["y"], "y")
+    plan.destroy()
+
+
+def test_t0_is_noop_and_bad_args(moe):
+    c = LC.make_case(256, 128, 8, 2, 32, "f32", 4, 0)
+    plan = make_plan(moe, c, max_tokens=4)
+    x = dev_x(c)
+    y = torch.full((4, 256), 5.0, device="cuda")
+    plan.forward(0, x[:0], y[:0])
+    torch.cuda.synchronize()
+    assert torch.all(y == 5.0)
+    big = torch.zeros((5, 256), device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(0, big, big)
+    assert ei.value.status == moe.MOE_E_INVALID
+    plan.destroy()
+
+
+def test_residency_invariance_bitwise(moe):
+    """all-HBM, 70/30 (cold start: experts 0..89 in the slots) and all-host plans give
+    bitwise equal y, before and after cache updates that move experts."""
+    c = LC.make_case(2048, 768, 128, 8, 128, "bf16", 4, 3, alpha=0.8)
+    lg = LC.oracle_logits(c)
+    y_router, y_given = [], []
+    for slots in (128, 90, 0):
+        plan = make_plan(moe, c, hbm_slots=slots)
+        y_router.append(run(plan, c))
+        y_given.append(run(plan, c, logits_in=lg))
+        if slots == 90:
+            for _ in range(3):
+                plan.cache_update(0, max_promotions=16)
+                y_router.append(run(plan, c))
+                y_given.append(run(plan, c, logits_in=lg))
+            assert plan.stats(0)["promotions"] > 0
+        plan.destroy()
+    for y in y_router[1:]:
+        np.testing.assert_array_equal(y, y_router[0])
+    for y in y_given[1:]:
+        np.testing.assert_array_equal(y, y_given[0])
+    ref = LC.oracle_forward(c, logits_in=lg)
+    check_y(y_given[0], ref["y"], "y")
+
+
+def test_counters_recount(moe):
+    import synth
+    c = LC.make_case(2048, 768, 128, 8, 128, "bf16", 4, 5, alpha=0.8)
+    res = synth.coldest_host_plan(5, 0, 128, 0.7)
+    plan = make_plan(moe, c, hbm_slots=int(res.sum()), resident=res)
+    lg = LC.oracle_logits(c)
+    ref = LC.oracle_forward(c, logits_in=lg)
+    run(plan, c, logits_in=lg)
+    run(plan, c, logits_in=lg)
+    st = plan.stats(0)
+    acc = O.link_accounting(ref["ids"], res, synth.expert_bytes(2048, 768, 128))
+    assert st["forwards"] == 2 and st["tokens"] == 8
+    assert st["hits"] == 2 * acc["hits"] and st["misses"] == 2 * acc["misses"]
+    assert st["bytes_hbm"] == 2 * acc["bytes_hbm"] and st["bytes_host"] == 2 * acc["bytes_host"]
+    slot_of = plan.residency(0)
+    assert np.array_equal(slot_of >= 0, res.astype(bool))
+    plan.destroy()
+
+
+def test_token_order_invariance_bitwise(moe):
+    c = LC.make_case(2048, 768, 128, 8, 128, "bf16", 4, 6, alpha=0.8)
+    plan = make_plan(moe, c)
+    y = run(plan, c)
+    perm = np.array([2, 0, 3, 1])
+    c2 = LC.make_case(2048, 768, 128, 8, 128, "bf16", 4, 6, alpha=0.8)
+    c2.x_bits = c.x_bits[perm].copy()
+    y2 = run(plan, c2)
+    np.testing.assert_array_equal(y2, y[perm])
+    plan.destroy()
