@@ -138,7 +138,8 @@ def main():
     # dominant kernel and its algorithmic work per launch
     per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0]) if v[0] else 0.0) for n, v in kt.items()
                   if v[0]}
-    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
+    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down") if n in per_kernel]
+    dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
     frac_bytes = {"gateup": 2.0 / 3.0, "down": 1.0 / 3.0}.get(dom, 0.0)
     if dom in ("gateup", "down"):
         alg = frac_bytes * expert_bytes_step

@@ -72,6 +72,7 @@ struct Workspace {
   void* h = nullptr;         // [Tmax*k][I] act dtype
   float* hpart = nullptr;    // [Tmax*k][I/32]
   float* o = nullptr;        // [Tmax*k][H]
+  unsigned* route_cnt = nullptr;  // [1] arrival counter of the fused decode routing kernel
 };
 
 }  // namespace
@@ -156,22 +157,20 @@ hipEvent_t take_event(moe_plan* p) {
   return e;
 }
 
-// Brackets one kernel launch with an event pair when profiling is on.
+// Event pair stamped by the dispatch of one kernel class when profiling is on;
+// the record is kept when the timer goes out of scope.
 struct KernelTimer {
   moe_plan* p;
   int kind;
-  hipStream_t s;
-  hipEvent_t a = nullptr, b = nullptr;
-  KernelTimer(moe_plan* p_, int kind_, hipStream_t s_) : p(p_), kind(kind_), s(s_) {
+  Timing tm;
+  KernelTimer(moe_plan* p_, int kind_) : p(p_), kind(kind_) {
     if (!p->profiling) return;
-    a = take_event(p);
-    b = take_event(p);
-    if (a && b) (void)hipEventRecord(a, s);
+    tm.start = take_event(p);
+    tm.stop = take_event(p);
+    if (!tm.start || !tm.stop) tm = Timing{};
   }
   ~KernelTimer() {
-    if (!a || !b) return;
-    (void)hipEventRecord(b, s);
-    p->recs.push_back({kind, a, b});
+    if (tm.start && tm.stop) p->recs.push_back({kind, tm.start, tm.stop});
   }
 };
 
@@ -291,7 +290,12 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(dev_alloc(p, &w.h, A * I * p->act_size));
   TRY(alloc_as(p, &w.hpart, A * (I / 32)));
   TRY(alloc_as(p, &w.o, A * H));
+  TRY(alloc_as(p, &w.route_cnt, 64));
 #undef TRY
+  if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
+    free_plan(p);
+    return fail(MOE_E_HIP, "clearing arrival counters failed");
+  }
   if (hipDeviceSynchronize() != hipSuccess) {
     free_plan(p);
     return fail(MOE_E_HIP, "device synchronize after allocation failed");
@@ -371,7 +375,6 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   Workspace& w = p->ws;
   const int A = T * k;
 
-  // router logits and per-group activation sums
   RouterArgs ra{};
   ra.x = x;
   ra.w = ly.d_router_w;
@@ -382,11 +385,6 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   ra.H = H;
   ra.E = E;
   ra.G = G;
-  ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
-  {
-    KernelTimer kt(p, MOE_K_ROUTER, s);
-    launch_router(ra, bf16, s);
-  }
   const float* logits = logits_in ? logits_in : w.logits;
 
   RouteArgs rt{};
@@ -406,14 +404,21 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.T = T;
   rt.E = E;
   rt.k = k;
-  {
-    KernelTimer kt(p, MOE_K_ROUTE, s);
-    if (A <= kRouteSmallMaxAssign && T <= 64) {
-      launch_route_small(rt, s);
-    } else {
-      launch_topk(rt, s);
-      launch_align(rt, s);
+
+  const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
+  if (decode) {
+    // router + group sums + top-k + grouping in one launch (8 expert rows per block)
+    ra.router_blocks = logits_in ? 0 : (E + 7) / 8;
+    KernelTimer kt(p, MOE_K_ROUTE);
+    launch_route_decode(rt, ra, bf16, w.route_cnt, kt.tm, s);
+  } else {
+    ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
+    {
+      KernelTimer kt(p, MOE_K_ROUTER);
+      launch_router(ra, bf16, kt.tm, s);
     }
+    KernelTimer kt(p, MOE_K_ROUTE);
+    launch_topk_align(rt, kt.tm, s);
   }
 
   const int max_act = std::min(E, A);
@@ -430,15 +435,16 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   ga.off_codes = p->L.off_gu_codes;
   ga.off_scales = p->L.off_gu_scales;
   ga.chunks = (int)p->L.gu_chunks;
-  ga.gblocks = (int)p->L.gu_gblocks;
+  ga.groups = (int)p->L.gu_groups;
   ga.tiles = (int)p->L.gu_tiles;
   ga.H = H;
   ga.I = I;
   ga.G = G;
   ga.k = k;
+  ga.T = T;
   {
-    KernelTimer kt(p, MOE_K_GATEUP, s);
-    launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, s);
+    KernelTimer kt(p, MOE_K_GATEUP);
+    launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, kt.tm, s);
   }
 
   GemvArgs da = ga;
@@ -449,24 +455,23 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   da.off_codes = p->L.off_dn_codes;
   da.off_scales = p->L.off_dn_scales;
   da.chunks = (int)p->L.dn_chunks;
-  da.gblocks = (int)p->L.dn_gblocks;
+  da.groups = (int)p->L.dn_groups;
   da.tiles = (int)p->L.dn_tiles;
   {
-    KernelTimer kt(p, MOE_K_DOWN, s);
-    launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, s);
+    KernelTimer kt(p, MOE_K_DOWN);
+    launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);
   }
-
-  CombineArgs ca{};
-  ca.o = w.o;
-  ca.wts = w.wts;
-  ca.inv = w.inv;
-  ca.y = y;
-  ca.T = T;
-  ca.H = H;
-  ca.k = k;
   {
-    KernelTimer kt(p, MOE_K_COMBINE, s);
-    launch_combine(ca, s);
+    CombineArgs ca{};
+    ca.o = w.o;
+    ca.wts = w.wts;
+    ca.inv = w.inv;
+    ca.y = y;
+    ca.T = T;
+    ca.H = H;
+    ca.k = k;
+    KernelTimer kt(p, MOE_K_COMBINE);
+    launch_combine(ca, kt.tm, s);
   }
   HIP_TRY(hipGetLastError());
 

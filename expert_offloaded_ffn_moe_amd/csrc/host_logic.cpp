@@ -15,19 +15,19 @@ Layout make_layout(int64_t H, int64_t I, int64_t G) {
   L.G = G;
   L.gu_tiles = I / 32;
   L.gu_chunks = H / 32;
-  L.gu_gblocks = (H / G + 7) / 8;
+  L.gu_groups = H / G;
   L.dn_tiles = H / 64;
   L.dn_chunks = I / 32;
-  L.dn_gblocks = (I / G + 7) / 8;
+  L.dn_groups = I / G;
   int64_t off = 0;
   L.off_gu_codes = off;
   off = round_up(off + L.gu_tiles * L.gu_chunks * 1024, 256);
   L.off_gu_scales = off;
-  off = round_up(off + L.gu_tiles * L.gu_gblocks * 1024, 256);
+  off = round_up(off + L.gu_tiles * L.gu_groups * 128, 256);
   L.off_dn_codes = off;
   off = round_up(off + L.dn_tiles * L.dn_chunks * 1024, 256);
   L.off_dn_scales = off;
-  off = round_up(off + L.dn_tiles * L.dn_gblocks * 1024, 256);
+  off = round_up(off + L.dn_tiles * L.dn_groups * 128, 256);
   L.bytes = off;
   L.canonical_bytes = 3 * H * I / 2 + 6 * H * I / G;
   return L;
@@ -35,7 +35,8 @@ Layout make_layout(int64_t H, int64_t I, int64_t G) {
 
 std::string check_config(const moe_config& c) {
   if (c.hidden <= 0 || c.inter <= 0) return "hidden and inter must be positive";
-  if (c.group_size <= 0 || c.group_size % 32) return "group_size must be a positive multiple of 32";
+  if (c.group_size != 32 && c.group_size != 64 && c.group_size != 128 && c.group_size != 256)
+    return "group_size must be 32, 64, 128 or 256";
   if (c.hidden % 64) return "hidden must be a multiple of 64";
   if (c.inter % 32) return "inter must be a multiple of 32";
   if (c.hidden % c.group_size) return "hidden must be a multiple of group_size";
@@ -95,7 +96,7 @@ void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
         chunk16(src + 16 * c, out + L.off_gu_codes + ((t * L.gu_chunks + c) * 64 + lane) * 16);
       const uint16_t* srow = (up ? s_up : s_gate) + row * (H / G);
       for (int64_t g = 0; g < H / G; ++g) {
-        uint8_t* dst = out + L.off_gu_scales + ((t * L.gu_gblocks + g / 8) * 64 + lane) * 16 + 2 * (g % 8);
+        uint8_t* dst = out + L.off_gu_scales + ((t * L.gu_groups + g) * 64 + lane) * 2;
         std::memcpy(dst, srow + g, 2);
       }
     }
@@ -109,7 +110,7 @@ void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
         chunk16(src + 16 * c, out + L.off_dn_codes + ((t * L.dn_chunks + c) * 64 + lane) * 16);
       const uint16_t* srow = s_down + row * (I / G);
       for (int64_t g = 0; g < I / G; ++g) {
-        uint8_t* dst = out + L.off_dn_scales + ((t * L.dn_gblocks + g / 8) * 64 + lane) * 16 + 2 * (g % 8);
+        uint8_t* dst = out + L.off_dn_scales + ((t * L.dn_groups + g) * 64 + lane) * 2;
         std::memcpy(dst, srow + g, 2);
       }
     }

@@ -23,12 +23,12 @@ namespace moe {
 // Inside a lane's 16 bytes, dword d covers K offsets [8d, 8d+8): the value at
 // offset 8d+2j sits in bits [4j, 4j+4), at 8d+2j+1 in bits [16+4j, 20+4j),
 // stored as n = q + 8 (0..15).
-// Scales: per tile, blocks of 8 groups: lane l's 16 bytes are the fp16 scales
-// of groups [8b, 8b+8) of its row (zero past the last group).
+// Scales: per tile, one 128-byte row per quantisation group: lane l's fp16
+// scale of that group for its row at bytes [2l, 2l+2).
 struct Layout {
   int64_t H = 0, I = 0, G = 0;
-  int64_t gu_tiles = 0, gu_chunks = 0, gu_gblocks = 0;
-  int64_t dn_tiles = 0, dn_chunks = 0, dn_gblocks = 0;
+  int64_t gu_tiles = 0, gu_chunks = 0, gu_groups = 0;
+  int64_t dn_tiles = 0, dn_chunks = 0, dn_groups = 0;
   int64_t off_gu_codes = 0, off_gu_scales = 0, off_dn_codes = 0, off_dn_scales = 0;
   int64_t bytes = 0;            // internal blob size (multiple of 256)
   int64_t canonical_bytes = 0;  // 3*H*I/2 + 6*H*I/G

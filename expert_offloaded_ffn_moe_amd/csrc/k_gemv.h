@@ -1,0 +1,287 @@
+// Grouped int4 dequant-GEMV for decode on gfx950: the per-expert SwiGLU FFN
+// of the routed MoE layer, reading each touched expert's weights once, from
+// its HBM slot or in place from its pinned host copy over the host link.
+//
+// Offloaded experts are dereferenced by the kernels directly, without staging
+// copies (page "763B MoE 塞进两张 96GB 显卡：闲置专家丢进主机内存", section
+// "显存缺口从哪里来"); which pointer an expert has is the per-expert plan of
+// section "同一个思路，vLLM 原生方案反而跑不通". The kernels do not know or care
+// which memory a pointer refers to, so results do not depend on residency.
+//
+// Work decomposition: a workgroup owns (active expert, row tile) and its W
+// waves split K by quantisation groups. Lane l owns one weight row and reads
+// 16 bytes (32 int4 values) per K chunk, so each wave load is one contiguous
+// KiB. A wave issues the loads of up to 16 chunks (and their group scales)
+// before any arithmetic. The activations of the tokens routed to the expert are
+// wave-uniform and come in through scalar loads. Partial sums of the W waves
+// are added in LDS in wave order, so the summation order is fixed.
+//
+// bf16 activations: a nibble n = q + 8 placed in the top mantissa bits of a
+// bf16 1.0 gives v = 1 + n/16 = 1.5 + q/16 exactly; v_dot2_f32_bf16 multiplies
+// two such values by two activations per instruction. Over a group,
+// sum q x = 16 * (sum v x - 1.5 * sum x), with sum x precomputed per group, so
+// the int4 weight is exact and only fp32 accumulation rounds.
+// fp32 activations: q is converted exactly to fp32 and used in fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// bf16 pair (1 + n_lo/16, 1 + n_hi/16) of pair j of a code dword
+static __device__ __forceinline__ uint32_t pair0(uint32_t d) { return ((d << 3) & 0x00780078u) | 0x3F803F80u; }
+static __device__ __forceinline__ uint32_t pair1(uint32_t d) { return ((d >> 1) & 0x00780078u) | 0x3F803F80u; }
+static __device__ __forceinline__ uint32_t pair2(uint32_t d) { return ((d >> 5) & 0x00780078u) | 0x3F803F80u; }
+static __device__ __forceinline__ uint32_t pair3(uint32_t d) { return ((d >> 9) & 0x00780078u) | 0x3F803F80u; }
+
+static __device__ __forceinline__ float half_bits(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+static __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// acc + sum_i v_i x_i over one 32-wide chunk, v = 1 + n/16 (bf16 path)
+static __device__ __forceinline__ float chunk_dot_bf16(const u32x4& wv, const uint32_t* __restrict__ xr, float acc) {
+  acc = dot2(pair0(wv.x), xr[0], acc);
+  acc = dot2(pair1(wv.x), xr[1], acc);
+  acc = dot2(pair2(wv.x), xr[2], acc);
+  acc = dot2(pair3(wv.x), xr[3], acc);
+  acc = dot2(pair0(wv.y), xr[4], acc);
+  acc = dot2(pair1(wv.y), xr[5], acc);
+  acc = dot2(pair2(wv.y), xr[6], acc);
+  acc = dot2(pair3(wv.y), xr[7], acc);
+  acc = dot2(pair0(wv.z), xr[8], acc);
+  acc = dot2(pair1(wv.z), xr[9], acc);
+  acc = dot2(pair2(wv.z), xr[10], acc);
+  acc = dot2(pair3(wv.z), xr[11], acc);
+  acc = dot2(pair0(wv.w), xr[12], acc);
+  acc = dot2(pair1(wv.w), xr[13], acc);
+  acc = dot2(pair2(wv.w), xr[14], acc);
+  acc = dot2(pair3(wv.w), xr[15], acc);
+  return acc;
+}
+
+// acc + sum_i q_i x_i, q = n - 8 exact in fp32 (fp32 path)
+static __device__ __forceinline__ float dword_dot_f32(uint32_t d, const float* __restrict__ xr, float acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float qlo = (float)(int)((d >> (4 * j)) & 0xFu) - 8.f;
+    const float qhi = (float)(int)((d >> (16 + 4 * j)) & 0xFu) - 8.f;
+    acc = fmaf(qlo, xr[2 * j], acc);
+    acc = fmaf(qhi, xr[2 * j + 1], acc);
+  }
+  return acc;
+}
+
+static __device__ __forceinline__ float chunk_dot_f32(const u32x4& wv, const float* __restrict__ xr, float acc) {
+  acc = dword_dot_f32(wv.x, xr, acc);
+  acc = dword_dot_f32(wv.y, xr + 8, acc);
+  acc = dword_dot_f32(wv.z, xr + 16, acc);
+  acc = dword_dot_f32(wv.w, xr + 24, acc);
+  return acc;
+}
+
+typedef __attribute__((address_space(1))) const u32x4 guint4;    // global-memory views, so
+typedef __attribute__((address_space(1))) const uint16_t gushort;  // loads are global_load, not flat
+
+constexpr int kBatch = 8;   // chunks whose loads are issued together
+constexpr int kMaxW = 16;   // waves per workgroup at most
+
+// K loop of one wave over groups [g0, g1) (CPG chunks each) for MT token rows.
+// rows[m]: element offset of token m's activation row in `in`; sum_rows[m]: offset
+// of its per-group (gate/up) or per-chunk (down) sums in insum (bf16 path).
+// Each batch issues kBatch code loads and their scale loads unconditionally,
+// indices clamped to the wave's last chunk/group (repeats hit in cache), then
+// computes on the groups that exist.
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK>
+static __device__ __forceinline__ void k_loop(guint4* codes, gushort* scales, const void* __restrict__ in,
+                                              const float* __restrict__ insum, const int64_t* rows,
+                                              const int64_t* sum_rows, int mc, int g0, int g1, float* acc) {
+  static_assert(kBatch % CPG == 0 || CPG > kBatch, "a batch holds whole groups");
+  constexpr int NB = CPG > kBatch ? CPG : kBatch;
+  constexpr int GB = NB / CPG;  // groups per batch
+  if (g1 <= g0) return;
+  const int c_last = g1 * CPG - 1;
+  for (int gb = g0; gb < g1; gb += GB) {
+    uint16_t sb[GB];
+    u32x4 wv[NB];
+#pragma unroll
+    for (int q = 0; q < GB; ++q) sb[q] = scales[(size_t)min(gb + q, g1 - 1) * 64];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) wv[i] = codes[(size_t)min(gb * CPG + i, c_last) * 64];
+#pragma unroll
+    for (int q = 0; q < GB; ++q) {
+      // groups past g1 repeat the last group (clamped loads) and count with weight 0;
+      // no branch here, so the loads above stay ahead of all the arithmetic
+      const int g = min(gb + q, g1 - 1);
+      const float keep = (gb + q < g1) ? 1.f : 0.f;
+      float accg[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) accg[m] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPG; ++cc) {
+        const int c = g * CPG + cc;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < mc) {
+            if (BF16) {
+              const uint32_t* xr = static_cast<const uint32_t*>(in) + rows[m] / 2 + c * 16;
+              accg[m] = chunk_dot_bf16(wv[q * CPG + cc], xr, accg[m]);
+            } else {
+              const float* xr = static_cast<const float*>(in) + rows[m] + c * 32;
+              accg[m] = chunk_dot_f32(wv[q * CPG + cc], xr, accg[m]);
+            }
+          }
+        }
+      }
+      const float s = keep * half_bits(sb[q]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < mc) {
+          if (BF16) {
+            float xs;
+            if (SUMS_PER_CHUNK) {
+              xs = 0.f;
+#pragma unroll
+              for (int cc = 0; cc < CPG; ++cc) xs += insum[sum_rows[m] + g * CPG + cc];
+            } else {
+              xs = insum[sum_rows[m] + g];
+            }
+            acc[m] = fmaf(16.f * s, accg[m] - 1.5f * xs, acc[m]);
+          } else {
+            acc[m] = fmaf(s, accg[m], acc[m]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- gate/up + SwiGLU
+
+template <int BF16, int MT, int CPG>
+__global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restrict__ wptr,
+                                                   const int32_t* __restrict__ active,
+                                                   const int32_t* __restrict__ n_active,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ sorted,
+                                                   const void* __restrict__ x, const float* __restrict__ xsum,
+                                                   void* __restrict__ h, float* __restrict__ hpart,
+                                                   int64_t off_codes, int64_t off_scales, int chunks, int groups,
+                                                   int tiles, int H, int I, int k) {
+  __shared__ float red[kMaxW][MT][64];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  if (slot >= *n_active) return;
+  const int e = active[slot];
+  const int p0 = offsets[e], M = offsets[e + 1] - p0;
+  const uint8_t* base = wptr[e];
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
+  const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
+
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    const int mc = min(MT, M - m0);
+    int64_t rows[MT], sum_rows[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = sorted[p0 + m0 + min(m, mc - 1)] / k;
+      rows[m] = (int64_t)t * H;
+      sum_rows[m] = (int64_t)t * groups;
+    }
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+    k_loop<BF16, MT, CPG, false>(codes, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    __syncthreads();
+    for (int i = threadIdx.x; i < MT * 32; i += blockDim.x) {  // whole 32-lane groups per m
+      const int m = i >> 5, j = i & 31;
+      float gs = 0.f, us = 0.f;
+      for (int w = 0; w < W; ++w) {
+        gs += red[w][m][j];
+        us += red[w][m][32 + j];
+      }
+      const float hv = gs / (1.f + __expf(-gs)) * us;
+      const int64_t p = p0 + m0 + m;
+      const int col = tile * 32 + j;
+      if (BF16) {
+        const uint16_t hb = f32_to_bf16_rne(hv);
+        if (m < mc) static_cast<uint16_t*>(h)[p * I + col] = hb;
+        float hr = __uint_as_float((uint32_t)hb << 16);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) hr += __shfl_xor(hr, off, 64);
+        if (j == 0 && m < mc) hpart[p * (I / 32) + tile] = hr;
+      } else {
+        if (m < mc) static_cast<float*>(h)[p * I + col] = hv;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------- down projection
+
+template <int BF16, int MT, int CPG>
+__global__ __launch_bounds__(1024) void k_down(const uint8_t* const* __restrict__ wptr,
+                                                 const int32_t* __restrict__ active,
+                                                 const int32_t* __restrict__ n_active,
+                                                 const int32_t* __restrict__ offsets, const void* __restrict__ h,
+                                                 const float* __restrict__ hpart, float* __restrict__ o,
+                                                 int64_t off_codes, int64_t off_scales, int chunks, int groups,
+                                                 int tiles, int H, int I) {
+  __shared__ float red[kMaxW][MT][64];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int n_act = *n_active;
+  if (slot >= n_act) return;
+  const int e = active[slot];
+  const int p0 = offsets[e], M = offsets[e + 1] - p0;
+  const uint8_t* base = wptr[e];
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
+  const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
+
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    const int mc = min(MT, M - m0);
+    int64_t rows[MT], sum_rows[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int64_t p = p0 + m0 + min(m, mc - 1);
+      rows[m] = p * I;
+      sum_rows[m] = p * (I / 32);
+    }
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+    k_loop<BF16, MT, CPG, true>(codes, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    __syncthreads();
+    for (int i = threadIdx.x; i < MT * 64; i += 64 * W) {
+      const int m = i >> 6, r = i & 63;
+      float s = 0.f;
+      for (int w = 0; w < W; ++w) s += red[w][m][r];
+      if (m < mc) o[(int64_t)(p0 + m0 + m) * H + tile * 64 + r] = s;
+    }
+    __syncthreads();
+  }
+}
+
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Instantiations of the decode dequant-GEMV kernels: gate/up + SwiGLU, bf16 activations.
+#include "k_gemv.h"
+
+namespace moe {
+
+// waves per workgroup: about kBatch chunks of K per wave, at most kMaxW waves
+static int waves_for(const GemvArgs& a) {
+  const int chunks = a.groups * (a.G / 32);
+  return std::max(1, std::min(std::min(kMaxW, a.groups), (chunks + kBatch - 1) / kBatch));
+}
+
+static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : max_tok <= 4 ? 4 : 8; }
+
+template <int MT, int CPG>
+static void gateup_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
+    launch_timed(k_gateup<1, MT, CPG>, dim3(grid), dim3(64 * W), 0, s, tm, a.wptr, a.active, a.n_active,
+                 a.offsets, a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
+                 a.groups, a.tiles, a.H, a.I, a.k);
+}
+
+template <int MT>
+static void gateup_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
+  switch (a.G / 32) {
+    case 1: return gateup_w<MT, 1>(a, W, grid, tm, s);
+    case 2: return gateup_w<MT, 2>(a, W, grid, tm, s);
+    case 4: return gateup_w<MT, 4>(a, W, grid, tm, s);
+    default: return gateup_w<MT, 8>(a, W, grid, tm, s);
+  }
+}
+
+void launch_gateup_bf16(const GemvArgs& a, int max_tok, int grid, const Timing& tm, hipStream_t s) {
+  const int W = waves_for(a);
+  switch (pick_mt(max_tok)) {
+    case 1: return gateup_cpg<1>(a, W, grid, tm, s);
+    case 2: return gateup_cpg<2>(a, W, grid, tm, s);
+    case 4: return gateup_cpg<4>(a, W, grid, tm, s);
+    default: return gateup_cpg<8>(a, W, grid, tm, s);
+  }
+}
+
+}  // namespace moe

@@ -2,16 +2,21 @@
 // gate choice, grouping of assignments by expert (counts, offsets, stable
 // permutation, active-expert list, link counters) and the gate-weighted combine.
 //
-// The routed choice itself follows page "763B MoE 塞进两张 96GB 显卡：闲置专家丢进
-// 主机内存", section "显存缺口从哪里来" (a few experts per token per layer, picked
-// at run time); softmax scores, ties to the lower id and renormalisation over
+// The routed choice follows page "763B MoE 塞进两张 96GB 显卡：闲置专家丢进主机内存",
+// section "显存缺口从哪里来" (a few experts per token per layer, picked at run
+// time); softmax scores, ties to the lower expert id and renormalisation over
 // the k chosen are the plain reading of it.
+//
+// Decode (T <= 64, T*k <= 1024) runs as one launch: router blocks compute the
+// logits, and the last block to finish (an atomic arrival counter, no waiting)
+// does the top-k and the grouping. Larger T uses separate launches.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
 #include <climits>
 
 #include "kernels.h"
+#include "wave.h"
 
 namespace moe {
 
@@ -25,150 +30,193 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // ----------------------------------------------------------------------------- router
 
-// Blocks [0, router_blocks): one wave per expert row, lanes stride over 16-byte
-// chunks of H, tokens in passes of 16; fp32 sums, then a fixed wave tree.
-// Blocks past router_blocks: one thread per (token, group) sums x over the group.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+
+__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, float s, bool bf16) {
+  if (bf16) {
+    s = dot2_bf16(w.x, x.x, s);
+    s = dot2_bf16(w.y, x.y, s);
+    s = dot2_bf16(w.z, x.z, s);
+    s = dot2_bf16(w.w, x.w, s);
+  } else {
+    s = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), s);
+    s = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), s);
+    s = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), s);
+    s = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), s);
+  }
+  return s;
+}
+
+// One wave: logits of expert row e for every token. Lane l owns the 16-byte
+// chunks l, l+64, ... of the row (at most NCH of them, held in registers); for
+// each token the matching x chunks are all loaded before the dot products.
+// fp32 sums in chunk order, then a fixed DPP tree across lanes.
+template <int BF16, int NCH>
+__device__ void router_row(const RouterArgs& a, int e, int lane) {
+  const int esz = BF16 ? 2 : 4;
+  const int nchunk = a.H * esz / 16;
+  gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
+  const float bias = a.b ? a.b[e] : 0.f;
+  u32x4 wv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) wv[i] = wrow[min(lane + 64 * i, nchunk - 1)];
+  for (int t = 0; t < a.T; ++t) {
+    gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)t * a.H * esz);
+    u32x4 xv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) xv[i] = xrow[min(lane + 64 * i, nchunk - 1)];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float d = dot16(wv[i], xv[i], 0.f, BF16);
+      s += (lane + 64 * i < nchunk) ? d : 0.f;
+    }
+    const float v = wave_sum(s);
+    if (lane == 0) a.logits[(size_t)t * a.E + e] = v + bias;
+  }
+}
+
+// Rows longer than 64 * 16 chunks: plain strided loop.
+template <int BF16>
+__device__ void router_row_long(const RouterArgs& a, int e, int lane) {
+  const int esz = BF16 ? 2 : 4;
+  const int nchunk = a.H * esz / 16;
+  gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
+  const float bias = a.b ? a.b[e] : 0.f;
+  for (int t = 0; t < a.T; ++t) {
+    gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)t * a.H * esz);
+    float s = 0.f;
+    for (int c = lane; c < nchunk; c += 64) {
+      const u32x4 wv = wrow[c], xv = xrow[c];
+      s = dot16(wv, xv, s, BF16);
+    }
+    const float v = wave_sum(s);
+    if (lane == 0) a.logits[(size_t)t * a.E + e] = v + bias;
+  }
+}
+
+template <int BF16>
+__device__ void router_row_any(const RouterArgs& a, int e, int lane) {
+  const int nch = (a.H * (BF16 ? 2 : 4) / 16 + 63) / 64;
+  if (nch <= 1)
+    router_row<BF16, 1>(a, e, lane);
+  else if (nch <= 2)
+    router_row<BF16, 2>(a, e, lane);
+  else if (nch <= 4)
+    router_row<BF16, 4>(a, e, lane);
+  else if (nch <= 8)
+    router_row<BF16, 8>(a, e, lane);
+  else if (nch <= 16)
+    router_row<BF16, 16>(a, e, lane);
+  else
+    router_row_long<BF16>(a, e, lane);
+}
+
+// sum of x[t][g*G .. (g+1)*G) for flat index gid = t * (H/G) + g (bf16 x)
+__device__ void xsum_one(const RouterArgs& a, int gid) {
+  const int ng = a.H / a.G;
+  const int t = gid / ng, g = gid % ng;
+  const uint4* src =
+      reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H + (size_t)g * a.G);
+  float s = 0.f;
+  for (int c = 0; c < a.G / 8; ++c) {
+    const uint4 v = src[c];
+    s += bf16_lo(v.x);
+    s += bf16_hi(v.x);
+    s += bf16_lo(v.y);
+    s += bf16_hi(v.y);
+    s += bf16_lo(v.z);
+    s += bf16_hi(v.z);
+    s += bf16_lo(v.w);
+    s += bf16_hi(v.w);
+  }
+  a.xsum[gid] = s;
+}
+
+// Any T: blocks [0, router_blocks) do 4 expert rows each, the rest the group sums.
 template <int BF16>
 __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if ((int)blockIdx.x < a.router_blocks) {
     const int e = blockIdx.x * 4 + wave;
-    if (e >= a.E) return;
-    const int esz = BF16 ? 2 : 4;
-    const int nchunk = a.H * esz / 16;
-    const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
-    const float bias = a.b ? a.b[e] : 0.f;
-    for (int t0 = 0; t0 < a.T; t0 += 16) {
-      const int nt = min(16, a.T - t0);
-      float acc[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      for (int c = lane; c < nchunk; c += 64) {
-        const uint4 wv = wrow[c];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i < nt) {
-            const uint4 xv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) +
-                                                            (size_t)(t0 + i) * a.H * esz)[c];
-            if (BF16) {
-              float s = acc[i];
-              s = dot2_bf16(wv.x, xv.x, s);
-              s = dot2_bf16(wv.y, xv.y, s);
-              s = dot2_bf16(wv.z, xv.z, s);
-              s = dot2_bf16(wv.w, xv.w, s);
-              acc[i] = s;
-            } else {
-              float s = acc[i];
-              s = fmaf(__uint_as_float(wv.x), __uint_as_float(xv.x), s);
-              s = fmaf(__uint_as_float(wv.y), __uint_as_float(xv.y), s);
-              s = fmaf(__uint_as_float(wv.z), __uint_as_float(xv.z), s);
-              s = fmaf(__uint_as_float(wv.w), __uint_as_float(xv.w), s);
-              acc[i] = s;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i < nt) {
-          const float v = wave_sum(acc[i]);
-          if (lane == 0) a.logits[(size_t)(t0 + i) * a.E + e] = v + bias;
-        }
-      }
-    }
+    if (e < a.E) router_row_any<BF16>(a, e, lane);
   } else if (BF16) {
-    const int ng = a.H / a.G;
     const int gid = (blockIdx.x - a.router_blocks) * 256 + threadIdx.x;
-    if (gid >= a.T * ng) return;
-    const int t = gid / ng, g = gid % ng;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H +
-                                                      (size_t)g * a.G);
-    float s = 0.f;
-    for (int c = 0; c < a.G / 8; ++c) {
-      const uint4 v = src[c];
-      s += bf16_lo(v.x);
-      s += bf16_hi(v.x);
-      s += bf16_lo(v.y);
-      s += bf16_hi(v.y);
-      s += bf16_lo(v.z);
-      s += bf16_hi(v.z);
-      s += bf16_lo(v.w);
-      s += bf16_hi(v.w);
-    }
-    a.xsum[gid] = s;
+    if (gid < a.T * (a.H / a.G)) xsum_one(a, gid);
   }
 }
 
-void launch_router(const RouterArgs& a0, int act_bf16, hipStream_t s) {
-  RouterArgs a = a0;
+void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s) {
   const int xs_blocks = (act_bf16 && a.xsum) ? (a.T * (a.H / a.G) + 255) / 256 : 0;
   const int grid = a.router_blocks + xs_blocks;
   if (grid == 0) return;
   if (act_bf16)
-    hipLaunchKernelGGL(k_router<1>, dim3(grid), dim3(256), 0, s, a);
+    launch_timed(k_router<1>, dim3(grid), dim3(256), 0, s, tm, a);
   else
-    hipLaunchKernelGGL(k_router<0>, dim3(grid), dim3(256), 0, s, a);
+    launch_timed(k_router<0>, dim3(grid), dim3(256), 0, s, tm, a);
 }
 
 // ----------------------------------------------------------------------------- top-k
 
-// One wave chooses the k experts of one token: k rounds of a wave-wide arg-max
-// under the order (logit descending, id ascending); lane j keeps slot j. The
-// weights are the softmax of the chosen logits: exp(l_j - l_0) / sum.
-__device__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
-                          float* __restrict__ w_out, int32_t* lds_ids) {
-  float v[16];
+// One wave chooses the k experts of one token: k rounds of a DPP arg-max under
+// (logit descending, id ascending); lane j keeps slot j. Lane l holds the logits
+// of experts l, l+64, ... (NV of them); a chosen or missing one is set to -inf
+// with id INT_MAX, which never wins while a real candidate is left (k <= E).
+// Weights: the softmax of the chosen logits, exp(l_j - l_0) / sum over the chosen.
+template <int NV>
+__device__ void topk_wave_nv(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
+                             float* __restrict__ w_out, int32_t* lds_ids) {
+  float v[NV];
+  int id[NV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? lrow[e] : -FLT_MAX;
+    const bool ok = e < E;
+    v[i] = ok ? lrow[min(e, E - 1)] : -INFINITY;
+    id[i] = ok ? e : INT_MAX;
   }
-  uint32_t taken = 0;
   float my_v = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = INT_MAX;
+    float bv = v[0];
+    int be = id[0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u)) {
-        if (v[i] > bv || (v[i] == bv && e < be)) {
-          bv = v[i];
-          be = e;
-        }
-      }
-    }
+    for (int i = 1; i < NV; ++i) better(bv, be, v[i], id[i]);
+    wave_argmax(bv, be);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
+    for (int i = 0; i < NV; ++i) {
+      const bool hit = id[i] == be;
+      v[i] = hit ? -INFINITY : v[i];
+      id[i] = hit ? INT_MAX : id[i];
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
+    my_v = (lane == j) ? bv : my_v;
+    my_e = (lane == j) ? be : my_e;
   }
-  const float m = __shfl(my_v, 0, 64);
+  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float ex = (lane < k) ? __expf(my_v - m) : 0.f;
   const float sum = wave_sum(ex);
   if (lane < k) {
     ids_out[lane] = my_e;
     w_out[lane] = ex / sum;
     if (lds_ids) lds_ids[lane] = my_e;
+  }
+}
+
+__device__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
+                          float* __restrict__ w_out, int32_t* lds_ids) {
+  switch ((E + 63) >> 6) {
+    case 1: return topk_wave_nv<1>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    case 2: return topk_wave_nv<2>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    case 3: return topk_wave_nv<3>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    case 4: return topk_wave_nv<4>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    case 5:
+    case 6: return topk_wave_nv<6>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    case 7:
+    case 8: return topk_wave_nv<8>(lrow, E, k, lane, ids_out, w_out, lds_ids);
+    default: return topk_wave_nv<16>(lrow, E, k, lane, ids_out, w_out, lds_ids);
   }
 }
 
@@ -185,29 +233,24 @@ struct AlignShared {
   int cnt[1024];
   int off[1025];
   int running[1024];
+  int is_host[1024];
   int wave_cnt[16][1024];
-  int wave_tot[16];
   int scan_tmp[16];
   int stat[4];  // hits, misses, unique hbm, unique host
-  int ids_small[kRouteSmallMaxAssign];
+  int last;
 };
 
-// Exclusive scan of one int per thread over a 1024-thread block; returns the
-// exclusive prefix, *total gets the sum.
+// Exclusive scan of one int per thread over a 1024-thread block; *total = sum.
 __device__ int block_exscan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   int base = 0, tot = 0;
+#pragma unroll
   for (int w = 0; w < 16; ++w) {
     const int tw = tmp[w];
-    if (w < wave) base += tw;
+    base += (w < wave) ? tw : 0;
     tot += tw;
   }
   __syncthreads();
@@ -215,19 +258,25 @@ __device__ int block_exscan(int v, int* tmp, int* total) {
   return base + incl - v;
 }
 
+__device__ __forceinline__ void load_is_host(const RouteArgs& a, AlignShared& sh) {
+  const int tid = threadIdx.x;
+  sh.is_host[tid] = tid < a.E ? a.is_host[tid] : 0;
+}
+
 // Counts, offsets, stable permutation, active list and counters for the n = T*k
-// assignments of ids (global memory, or sh.ids_small when from_lds).
-// Must be called by all 1024 threads of the block.
-__device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) {
+// assignments of a.ids.
+// Called by all 1024 threads; sh.is_host must be loaded and visible.
+__device__ void align_block(const RouteArgs& a, AlignShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.T * a.k, E = a.E;
   sh.cnt[tid] = 0;
   sh.running[tid] = 0;
+#pragma unroll
   for (int w = 0; w < 16; ++w) sh.wave_cnt[w][tid] = 0;
   if (tid < 4) sh.stat[tid] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int e = from_lds ? sh.ids_small[i] : a.ids[i];
+    const int e = a.ids[i];
     atomicAdd(&sh.cnt[e], 1);
   }
   __syncthreads();
@@ -250,7 +299,7 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) 
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
     const bool valid = i < n;
-    const int e = valid ? (from_lds ? sh.ids_small[i] : a.ids[i]) : 0;
+    const int e = valid ? (a.ids[i]) : 0;
     unsigned long long peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 10; ++b) {
@@ -258,8 +307,7 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) 
       peers &= ((e >> b) & 1) ? bm : ~bm;
     }
     const int rank = __popcll(peers & lt_mask);
-    const bool leader = valid && ((peers & lt_mask) == 0);
-    if (leader) sh.wave_cnt[wave][e] = __popcll(peers);
+    if (valid && (peers & lt_mask) == 0) sh.wave_cnt[wave][e] = __popcll(peers);
     __syncthreads();
     if (valid) {
       int before = 0;
@@ -271,6 +319,7 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) 
     __syncthreads();
     if (tid < E) {
       int s = 0;
+#pragma unroll
       for (int w = 0; w < 16; ++w) {
         s += sh.wave_cnt[w][tid];
         sh.wave_cnt[w][tid] = 0;
@@ -285,7 +334,7 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) 
   auto flag = [&](int it) -> int {
     if (it >= 2 * E) return 0;
     const int e = it < E ? it : it - E;
-    const bool host = a.is_host[e] != 0;
+    const bool host = sh.is_host[e] != 0;
     return (sh.cnt[e] > 0 && (it < E ? host : !host)) ? 1 : 0;
   };
   const int f0 = flag(i0), f1 = flag(i1);
@@ -296,48 +345,194 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh, bool from_lds) 
   if (tid == 0) *a.n_active = n_act;
 
   if (tid < E && c > 0) {
-    const bool host = a.is_host[tid] != 0;
+    const bool host = sh.is_host[tid] != 0;
     atomicAdd(&sh.stat[host ? 1 : 0], c);
     atomicAdd(&sh.stat[host ? 3 : 2], 1);
-    a.counts_acc[tid] += c;
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + tid), (unsigned long long)c);
   }
   __syncthreads();
   if (tid == 0) {
-    a.stats[ST_FORWARDS] += 1;
-    a.stats[ST_TOKENS] += a.T;
-    a.stats[ST_HITS] += sh.stat[0];
-    a.stats[ST_MISSES] += sh.stat[1];
-    a.stats[ST_BYTES_HBM] += (int64_t)sh.stat[2] * a.expert_bytes;
-    a.stats[ST_BYTES_HOST] += (int64_t)sh.stat[3] * a.expert_bytes;
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
+    atomicAdd(st + ST_FORWARDS, 1ull);
+    atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
+    atomicAdd(st + ST_HITS, (unsigned long long)sh.stat[0]);
+    atomicAdd(st + ST_MISSES, (unsigned long long)sh.stat[1]);
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)sh.stat[2] * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)sh.stat[3] * a.expert_bytes));
+  }
+}
+
+struct DecodeShared {
+  int cnt[1024];
+  int off[1025];
+  int running[1024];
+  int is_host[1024];
+  int ids_small[kRouteSmallMaxAssign];
+  int last;
+};
+
+// The same grouping done by one wave, for n = T*k <= kRouteSmallMaxAssign
+// assignments with ids in sh.ids_small and sh.is_host loaded: no block
+// barriers, only wave-level scans. Lane l handles experts [16l, 16l+16) for
+// counts, offsets and the active list.
+__device__ void align_wave(const RouteArgs& a, DecodeShared& sh) {
+  const int lane = threadIdx.x & 63;
+  const int n = a.T * a.k, E = a.E;
+  for (int e = lane; e < 1024; e += 64) {
+    sh.cnt[e] = 0;
+    sh.running[e] = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int i = lane; i < n; i += 64) atomicAdd(&sh.cnt[sh.ids_small[i]], 1);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  const int e0 = lane * 16;
+  int c[16], loc = 0, nh = 0, nb = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = e0 + j;
+    c[j] = (e < E) ? sh.cnt[e] : 0;
+    loc += c[j];
+    const bool host = (e < E) && sh.is_host[e] != 0;
+    nh += (c[j] > 0 && host) ? 1 : 0;
+    nb += (c[j] > 0 && !host) ? 1 : 0;
+  }
+  const int incl = wave_incl_scan(loc);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int run = incl - loc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = e0 + j;
+    if (e < E) {
+      sh.off[e] = run;
+      a.offsets[e] = run;
+      a.counts[e] = c[j];
+    }
+    run += c[j];
+  }
+  if (lane == 0) {
+    sh.off[E] = total;
+    a.offsets[E] = total;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // stable positions, 64 assignments per round in ascending order
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < n;
+    const int e = valid ? sh.ids_small[i] : 0;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const unsigned long long bm = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? bm : ~bm;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid) {
+      const int pos = sh.off[e] + sh.running[e] + rank;
+      a.sorted[pos] = i;
+      a.inv[i] = pos;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (valid && (peers & lt_mask) == 0) sh.running[e] += __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+
+  // active experts: host-read ones first, then the HBM ones, ascending id in each
+  const int ih = wave_incl_scan(nh), ib = wave_incl_scan(nb);
+  const int tot_h = __builtin_amdgcn_readlane(ih, 63), tot_b = __builtin_amdgcn_readlane(ib, 63);
+  int ph = ih - nh, pb = tot_h + ib - nb, hits = 0, misses = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = e0 + j;
+    if (e < E && c[j] > 0) {
+      if (sh.is_host[e] != 0) {
+        a.active[ph++] = e;
+        misses += c[j];
+      } else {
+        a.active[pb++] = e;
+        hits += c[j];
+      }
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)c[j]);
+    }
+  }
+  hits = wave_sum_i(hits);
+  misses = wave_sum_i(misses);
+  if (lane == 0) {
+    *a.n_active = tot_h + tot_b;
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
+    atomicAdd(st + ST_FORWARDS, 1ull);
+    atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
+    atomicAdd(st + ST_HITS, (unsigned long long)hits);
+    atomicAdd(st + ST_MISSES, (unsigned long long)misses);
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)tot_b * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)tot_h * a.expert_bytes));
   }
 }
 
 __global__ __launch_bounds__(1024) void k_align(RouteArgs a) {
   __shared__ AlignShared sh;
-  align_block(a, sh, false);
+  load_is_host(a, sh);
+  __syncthreads();
+  align_block(a, sh);
 }
 
-// Decode-sized routing in one workgroup: top-k of every token (one wave per
-// token), then the grouping by expert.
-__global__ __launch_bounds__(1024) void k_route_small(RouteArgs a) {
-  __shared__ AlignShared sh;
+// Decode routing in one launch. Blocks [0, router_blocks): 8 expert rows each
+// (one per wave); then xsum blocks; every block then arrives on the counter,
+// and the last one (which sees every other block's logits after the
+// device-scope fences) picks the top-k of every token (one wave per token) and
+// groups the assignments in one wave.
+template <int BF16>
+__global__ __launch_bounds__(512) void k_route_decode(RouteArgs a, RouterArgs r, unsigned* counter) {
+  __shared__ DecodeShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = wave; t < a.T; t += 16)
+  const int bid = blockIdx.x;
+  if (bid < r.router_blocks) {
+    const int e = bid * 8 + wave;
+    if (e < r.E) router_row_any<BF16>(r, e, lane);
+  } else if (BF16 && r.xsum) {
+    const int gid = (bid - r.router_blocks) * 512 + threadIdx.x;
+    if (gid < r.T * (r.H / r.G)) xsum_one(r, gid);
+  }
+  // every wave drains its stores; one thread publishes the block's writes with a
+  // device-scope release and arrives; the last arrival acquires
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned prev = atomicAdd(counter, 1u);
+    sh.last = (prev == gridDim.x - 1) ? 1 : 0;
+    if (sh.last) __threadfence();
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  for (int e = threadIdx.x; e < a.E; e += 512) sh.is_host[e] = a.is_host[e];
+  if (threadIdx.x == 0) *counter = 0u;  // ready for the next launch on this stream
+  for (int t = wave; t < a.T; t += 8)
     topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, lane, a.ids + (size_t)t * a.k, a.wts + (size_t)t * a.k,
               sh.ids_small + t * a.k);
   __syncthreads();
-  align_block(a, sh, true);
+  if (threadIdx.x < 64) align_wave(a, sh);
 }
 
-void launch_route_small(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, a);
+void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,
+                         const Timing& tm, hipStream_t s) {
+  const int xs_blocks = (act_bf16 && r.xsum) ? (r.T * (r.H / r.G) + 511) / 512 : 0;
+  const int grid = std::max(1, r.router_blocks + xs_blocks);
+  if (act_bf16)
+    launch_timed(k_route_decode<1>, dim3(grid), dim3(512), 0, s, tm, a, r, counter);
+  else
+    launch_timed(k_route_decode<0>, dim3(grid), dim3(512), 0, s, tm, a, r, counter);
 }
 
-void launch_topk(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((a.T + 15) / 16), dim3(1024), 0, s, a);
+void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s) {
+  Timing t1 = tm, t2 = tm;
+  t1.stop = nullptr;
+  t2.start = nullptr;
+  launch_timed(k_topk, dim3((a.T + 15) / 16), dim3(1024), 0, s, t1, a);
+  launch_timed(k_align, dim3(1), dim3(1024), 0, s, t2, a);
 }
-
-void launch_align(const RouteArgs& a, hipStream_t s) { hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), 0, s, a); }
 
 // ----------------------------------------------------------------------------- combine
 
@@ -359,8 +554,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   reinterpret_cast<float4*>(a.y + (size_t)t * a.H)[n4] = acc;
 }
 
-void launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, s, a);
+void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s) {
+  launch_timed(k_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, s, tm, a);
 }
 
 }  // namespace moe

@@ -1,14 +1,30 @@
 // Internal kernel interface of the MoE offload library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 namespace moe {
 
 // Device counters per layer, int64 each.
 enum StatIndex { ST_FORWARDS = 0, ST_TOKENS, ST_HITS, ST_MISSES, ST_BYTES_HBM, ST_BYTES_HOST, ST_COUNT };
+
+// Optional events stamped by the dispatch itself at kernel start and end.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, const Timing& tm,
+                         Args... args) {
+  if (tm.start || tm.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, tm.start, tm.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 struct RouterArgs {
   const void* x;         // [T][H] act dtype
@@ -17,7 +33,7 @@ struct RouterArgs {
   float* logits;         // [T][E]
   float* xsum;           // [T][H/G] sums of x over each group (bf16 path), or null
   int T, H, E, G;
-  int router_blocks;     // blocks [0, router_blocks) compute logits, the rest xsum
+  int router_blocks;     // blocks computing logits (the rest compute xsum)
 };
 
 struct RouteArgs {
@@ -48,9 +64,9 @@ struct GemvArgs {
   void* out;                   // gate/up: h [T*k][I] act dtype; down: o [T*k][H] fp32
   float* outpart;              // gate/up: hpart [T*k][I/32] (bf16 path); down: unused
   int64_t off_codes, off_scales;
-  int chunks, gblocks;         // K chunks of 32 and scale blocks per tile
+  int chunks, groups;          // K chunks of 32 and quantisation groups per row
   int tiles;                   // tiles per expert
-  int H, I, G, k;
+  int H, I, G, k, T;
 };
 
 struct CombineArgs {
@@ -61,14 +77,15 @@ struct CombineArgs {
   int T, H, k;
 };
 
-void launch_router(const RouterArgs& a, int act_bf16, hipStream_t s);
-void launch_route_small(const RouteArgs& a, hipStream_t s);  // T*k small: one workgroup
-void launch_topk(const RouteArgs& a, hipStream_t s);         // any T: many workgroups
-void launch_align(const RouteArgs& a, hipStream_t s);        // after launch_topk
-void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, hipStream_t s);
-void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, hipStream_t s);
-void launch_combine(const CombineArgs& a, hipStream_t s);
+constexpr int kRouteSmallMaxAssign = 256;   // T*k handled by launch_route_decode
+constexpr int kRouteSmallMaxTokens = 64;
 
-constexpr int kRouteSmallMaxAssign = 1024;  // T*k handled by launch_route_small
+void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s);
+void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,
+                         const Timing& tm, hipStream_t s);
+void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s);
+void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
+void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
+void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s);
 
 }  // namespace moe

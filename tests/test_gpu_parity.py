@@ -219,3 +219,20 @@ def test_token_order_invariance_bitwise(moe):
     y2 = run(plan, c2)
     np.testing.assert_array_equal(y2, y[perm])
     plan.destroy()
+
+
+@pytest.mark.parametrize("T", [40, 2048])
+def test_large_batch_routing_and_sampled_outputs(moe, T):
+    """T*k > 256: multi-block top-k and the block grouping path. Routing is compared
+    bit-exactly for every token; y on a seeded sample of tokens (the whole batch for T=40)."""
+    c = LC.make_case(2048, 768, 128, 8, 128, "bf16", T, 4)
+    lg = LC.oracle_logits(c)
+    rng = np.random.default_rng(T)
+    toks = np.arange(T) if T <= 64 else np.sort(rng.choice(T, 48, replace=False))
+    ref = LC.oracle_forward(c, logits_in=lg, tokens=toks)
+    plan = make_plan(moe, c)
+    rb = route_bufs(c)
+    y = run(plan, c, logits_in=lg, route=rb)
+    check_routing_exact(c, ref, rb)
+    check_y(y[toks], ref["y"], "y (%d sampled tokens)" % len(toks))
+    plan.destroy()
