@@ -47,7 +47,7 @@ def workload_dims(args):
     raise SystemExit("unknown workload")
 
 
-def main():
+def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -56,51 +56,45 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--plan", default="mixed", choices=["mixed", "hbm", "host"])
+    ap.add_argument("--sweep", default=None,
+                    help="comma list of plan:batch runs on the same generated layers, one JSON line each")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    args = ap.parse_args()
+    return ap.parse_args()
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel sharding "
-              "is a design note, not code); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
+def make_layers(d, L, keep_blobs):
+    import synth
+    H, I, E, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "G", "act", "alpha", "seed"))
+    layers, t0 = [], time.time()
+    for l in range(L):
+        blobs = synth.expert_blobs(seed, l, 0, E, H, I, G)
+        Wr = synth.router_weight(seed, l, E, H, act)
+        b = synth.router_bias(seed, l, E, alpha)
+        layers.append(dict(Wr=Wr, b=b, blobs=blobs))
+        log("layer %d/%d generated (%.1fs)" % (l + 1, L, time.time() - t0))
+    return layers
+
+
+def run_one(args, d, layers, B, plan_kind, steps, warmup):
+    """Time `steps` forwards (layer i mod L) at batch B under one residency plan."""
     import numpy as np
     import torch
 
     import expert_offloaded_ffn_moe_amd as moe
     import synth
 
-    d = workload_dims(args)
     H, I, E, k, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "k", "G", "act", "alpha", "seed"))
-    B = args.batch or (2048 if args.workload == "prefill" else 1)
-    L = args.layers or {"decode": 24, "deepseek": 2, "prefill": 4}[args.workload]
+    L = len(layers)
     eb = synth.expert_bytes(H, I, G)
-    if args.workload == "deepseek":
-        slots = {"mixed": int(round(0.7 * E)), "hbm": E, "host": 0}[args.plan]
-    else:
-        slots = E
-
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    torch.cuda.set_device(0)
+    slots = {"mixed": int(round(0.7 * E)), "hbm": E, "host": 0}[plan_kind]
     cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=slots)
     plan = moe.Plan(cfg)
-    layers_host = []
-    t0 = time.time()
-    for l in range(L):
-        blobs = synth.expert_blobs(seed, l, 0, E, H, I, G)
-        Wr = synth.router_weight(seed, l, E, H, act)
-        b = synth.router_bias(seed, l, E, alpha)
-        res = None
-        if args.workload == "deepseek" and args.plan == "mixed":
-            res = synth.coldest_host_plan(seed, l, E, slots / E)
-        plan.load_layer(l, Wr, b, blobs, res)
-        layers_host.append((Wr, b, blobs if (not args.no_cpu and l < 2) else None))
-        log("layer %d/%d generated and loaded (%.1fs)" % (l + 1, L, time.time() - t0))
-
-    n_in = args.warmup + args.steps
-    xs_bits = [synth.activations(seed, 1000 + i, B, H, act) for i in range(min(n_in, 64))]
+    for l, ly in enumerate(layers):
+        res = synth.coldest_host_plan(seed, l, E, slots / E) if plan_kind == "mixed" else None
+        plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], res)
+    n_in = min(warmup + steps, 64)
+    xs_bits = [synth.activations(seed, 1000 + i, B, H, act) for i in range(n_in)]
     xs = [torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda() for xb in xs_bits]
     y = torch.empty((B, H), device="cuda")
     stream = torch.cuda.current_stream()
@@ -108,82 +102,97 @@ def main():
     def step(i):
         plan.forward(i % L, xs[i % len(xs)], y, stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     plan.reset_stats()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     st = plan.stats(-1)
-    log("timed %d steps in %.4fs" % (args.steps, elapsed))
+    log("timed %d steps in %.4fs (plan %s, batch %d)" % (steps, elapsed, plan_kind, B))
 
-    # profiled pass: HIP events around each kernel on the launch stream
+    # profiled pass: per-kernel times from events stamped by each dispatch
     plan.profile(True)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     kt = plan.kernel_times()
     plan.profile(False)
+    plan.destroy()
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = B * args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
     fwd = max(st["forwards"], 1)
-    bytes_hbm = st["bytes_hbm"] / fwd
-    bytes_host = st["bytes_host"] / fwd
-    expert_bytes_step = bytes_hbm + bytes_host
-
-    # dominant kernel and its algorithmic work per launch
-    per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0]) if v[0] else 0.0) for n, v in kt.items()
-                  if v[0]}
+    bytes_hbm, bytes_host = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
+    per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
     ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down") if n in per_kernel]
     dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
     frac_bytes = {"gateup": 2.0 / 3.0, "down": 1.0 / 3.0}.get(dom, 0.0)
-    if dom in ("gateup", "down"):
-        alg = frac_bytes * expert_bytes_step
-        achieved = alg / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
-        if args.workload == "deepseek" and args.plan == "host":
-            peak, bound = HOST_LINK_PEAK_GBS, "host-link"
-        else:
-            peak, bound = HBM_PEAK_GBS, "hbm"
-        roof = dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=peak, unit="GB/s",
-                    frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(alg),
-                    avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
-    else:
-        roof = dict(bound="unknown", kernel=dom, achieved=None, peak=None, unit=None, frac=None, traffic=None)
-
-    out = {
+    host_only = bytes_hbm == 0 and bytes_host > 0
+    alg = frac_bytes * (bytes_hbm + bytes_host)
+    achieved = alg / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
+    peak, bound = (HOST_LINK_PEAK_GBS, "host-link") if host_only else (HBM_PEAK_GBS, "hbm")
+    roof = dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=peak, unit="GB/s",
+                frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(alg),
+                avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
+    name = {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
+            "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload]
+    return {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(B * steps / elapsed, 2),
         "unit": "layer-tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s layer H%d I%d E%d k%d int4 G%d, batch %d, %d-layer rotation%s" % (
-            {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
-             "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload], H, I, E, k, G, B, L,
-            (", plan " + args.plan) if args.workload == "deepseek" else ""),
-            "hbm_slots": slots, "alpha": alpha, "seed": seed},
+        "config": {"workload": "%s layer H%d I%d E%d k%d int4 G%d, batch %d, %d-layer rotation, plan %s" % (
+            name, H, I, E, k, G, B, L, plan_kind), "hbm_slots": slots, "alpha": alpha, "seed": seed},
         "roofline": roof,
         "layer": {"expert_bytes_per_step_hbm": int(bytes_hbm), "expert_bytes_per_step_host": int(bytes_host),
-                  "unique_experts_per_step": round(expert_bytes_step / eb, 3),
-                  "layer_GBps_wall": round(expert_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+                  "unique_experts_per_step": round((bytes_hbm + bytes_host) / eb, 3),
+                  "layer_GBps_wall": round((bytes_hbm + bytes_host) / (ms_per_step * 1e-3) / 1e9, 1),
+                  "host_link_GBps_wall": round(bytes_host / (ms_per_step * 1e-3) / 1e9, 2),
                   "hit_rate": round(st["hits"] / max(st["hits"] + st["misses"], 1), 5),
                   "kernels_us": {n: round(v["avg_us"], 3) for n, v in per_kernel.items()}},
+        "_xs_bits": xs_bits,
     }
 
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args, d, B, L, layers_host, xs_bits)
-    print(json.dumps(out), flush=True)
-    plan.destroy()
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel sharding "
+              "is a design note, not code); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    d = workload_dims(args)
+    L = args.layers or {"decode": 24, "deepseek": 3, "prefill": 4}[args.workload]
+    layers = make_layers(d, L, keep_blobs=True)
+    default_plan = args.plan if args.workload == "deepseek" else "hbm"
+    if args.sweep:
+        runs = []
+        for item in args.sweep.split(","):
+            pk, bs = item.split(":")
+            runs.append((pk, int(bs)))
+    else:
+        runs = [(default_plan, args.batch or (2048 if args.workload == "prefill" else 1))]
+    for i, (pk, B) in enumerate(runs):
+        out = run_one(args, d, layers, B, pk, args.steps, args.warmup)
+        xs_bits = out.pop("_xs_bits")
+        if not args.no_cpu and i == 0:
+            out["cpu_baseline"] = cpu_baseline(args, d, B, L, layers, xs_bits)
+        print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(args, d, B, L, layers_host, xs_bits):
@@ -199,11 +208,11 @@ def cpu_baseline(args, d, B, L, layers_host, xs_bits):
     except Exception:
         threads = 1
     H, I, E, k, G, act = (d[n] for n in ("H", "I", "E", "k", "G", "act"))
-    n_layers = sum(1 for lh in layers_host if lh[2] is not None)
+    n_layers = min(2, len(layers_host))
     tokens, t0, i = 0, time.perf_counter(), 0
     while time.perf_counter() - t0 < args.cpu_seconds:
         l = i % n_layers
-        Wr, b, blobs = layers_host[l]
+        Wr, b, blobs = layers_host[l]["Wr"], layers_host[l]["b"], layers_host[l]["blobs"]
         x = O.bf16_bits_to_f64(xs_bits[i % len(xs_bits)])
         O.layer_forward(x, O.bf16_bits_to_f64(Wr), b, blobs, H, I, E, k, G, act)
         tokens += B

@@ -72,6 +72,8 @@ struct Workspace {
   void* h = nullptr;         // [Tmax*k][I] act dtype
   float* hpart = nullptr;    // [Tmax*k][I/32]
   float* o = nullptr;        // [Tmax*k][H]
+  int2* tiles = nullptr;     // [Tmax*k/64 + E] prefill GEMM row tiles
+  int32_t* n_tiles = nullptr;
   unsigned* route_cnt = nullptr;  // [1] arrival counter of the fused decode routing kernel
 };
 
@@ -291,6 +293,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(alloc_as(p, &w.hpart, A * (I / 32)));
   TRY(alloc_as(p, &w.o, A * H));
   TRY(alloc_as(p, &w.route_cnt, 64));
+  TRY(alloc_as(p, &w.tiles, A / kGemmRows + E + 1));
+  TRY(alloc_as(p, &w.n_tiles, 64));
 #undef TRY
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
     free_plan(p);
@@ -406,7 +410,68 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.k = k;
 
   const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
-  if (decode) {
+  const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
+  if (prefill) {
+    {
+      KernelTimer kt(p, MOE_K_ROUTER);
+      if (!logits_in) launch_router_mfma(ra, kt.tm, s);
+    }
+    rt.tiles = w.tiles;
+    rt.n_tiles = w.n_tiles;
+    {
+      KernelTimer kt(p, MOE_K_ROUTE);
+      launch_topk_align(rt, kt.tm, s);
+    }
+    GemmArgs gg{};
+    gg.wptr = ly.d_wptr;
+    gg.tiles = w.tiles;
+    gg.n_tiles = w.n_tiles;
+    gg.offsets = w.offsets;
+    gg.sorted = w.sorted;
+    gg.a_src = static_cast<const uint16_t*>(x);
+    gg.out = w.h;
+    gg.off_codes = p->L.off_gu_codes;
+    gg.off_scales = p->L.off_gu_scales;
+    gg.chunks = (int)p->L.gu_chunks;
+    gg.groups = (int)p->L.gu_groups;
+    gg.ntiles_n = (int)p->L.gu_tiles;
+    gg.K = H;
+    gg.out_ld = I;
+    gg.k = k;
+    gg.G = G;
+    gg.max_tiles = A / kGemmRows + std::min(E, A);
+    {
+      KernelTimer kt(p, MOE_K_GEMM_GATEUP);
+      launch_gemm_gateup(gg, kt.tm, s);
+    }
+    GemmArgs gd = gg;
+    gd.a_src = static_cast<const uint16_t*>(w.h);
+    gd.out = w.o;
+    gd.off_codes = p->L.off_dn_codes;
+    gd.off_scales = p->L.off_dn_scales;
+    gd.chunks = (int)p->L.dn_chunks;
+    gd.groups = (int)p->L.dn_groups;
+    gd.ntiles_n = (int)p->L.dn_tiles;
+    gd.K = I;
+    gd.out_ld = H;
+    {
+      KernelTimer kt(p, MOE_K_GEMM_DOWN);
+      launch_gemm_down(gd, kt.tm, s);
+    }
+    CombineArgs ca{};
+    ca.o = w.o;
+    ca.wts = w.wts;
+    ca.inv = w.inv;
+    ca.y = y;
+    ca.T = T;
+    ca.H = H;
+    ca.k = k;
+    {
+      KernelTimer kt(p, MOE_K_COMBINE);
+      launch_combine(ca, kt.tm, s);
+    }
+    HIP_TRY(hipGetLastError());
+  } else if (decode) {
     // router + group sums + top-k + grouping in one launch (8 expert rows per block)
     ra.router_blocks = logits_in ? 0 : (E + 7) / 8;
     KernelTimer kt(p, MOE_K_ROUTE);
@@ -421,59 +486,61 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     launch_topk_align(rt, kt.tm, s);
   }
 
-  const int max_act = std::min(E, A);
-  GemvArgs ga{};
-  ga.wptr = ly.d_wptr;
-  ga.active = w.active;
-  ga.n_active = w.n_active;
-  ga.offsets = w.offsets;
-  ga.sorted = w.sorted;
-  ga.in = x;
-  ga.insum = w.xsum;
-  ga.out = w.h;
-  ga.outpart = w.hpart;
-  ga.off_codes = p->L.off_gu_codes;
-  ga.off_scales = p->L.off_gu_scales;
-  ga.chunks = (int)p->L.gu_chunks;
-  ga.groups = (int)p->L.gu_groups;
-  ga.tiles = (int)p->L.gu_tiles;
-  ga.H = H;
-  ga.I = I;
-  ga.G = G;
-  ga.k = k;
-  ga.T = T;
-  {
-    KernelTimer kt(p, MOE_K_GATEUP);
-    launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, kt.tm, s);
-  }
+  if (!prefill) {  // decode / small-batch path: dequant-GEMVs over the active experts
+    const int max_act = std::min(E, A);
+    GemvArgs ga{};
+    ga.wptr = ly.d_wptr;
+    ga.active = w.active;
+    ga.n_active = w.n_active;
+    ga.offsets = w.offsets;
+    ga.sorted = w.sorted;
+    ga.in = x;
+    ga.insum = w.xsum;
+    ga.out = w.h;
+    ga.outpart = w.hpart;
+    ga.off_codes = p->L.off_gu_codes;
+    ga.off_scales = p->L.off_gu_scales;
+    ga.chunks = (int)p->L.gu_chunks;
+    ga.groups = (int)p->L.gu_groups;
+    ga.tiles = (int)p->L.gu_tiles;
+    ga.H = H;
+    ga.I = I;
+    ga.G = G;
+    ga.k = k;
+    ga.T = T;
+    {
+      KernelTimer kt(p, MOE_K_GATEUP);
+      launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, kt.tm, s);
+    }
 
-  GemvArgs da = ga;
-  da.in = w.h;
-  da.insum = w.hpart;
-  da.out = w.o;
-  da.outpart = nullptr;
-  da.off_codes = p->L.off_dn_codes;
-  da.off_scales = p->L.off_dn_scales;
-  da.chunks = (int)p->L.dn_chunks;
-  da.groups = (int)p->L.dn_groups;
-  da.tiles = (int)p->L.dn_tiles;
-  {
-    KernelTimer kt(p, MOE_K_DOWN);
-    launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);
+    GemvArgs da = ga;
+    da.in = w.h;
+    da.insum = w.hpart;
+    da.out = w.o;
+    da.outpart = nullptr;
+    da.off_codes = p->L.off_dn_codes;
+    da.off_scales = p->L.off_dn_scales;
+    da.chunks = (int)p->L.dn_chunks;
+    da.groups = (int)p->L.dn_groups;
+    da.tiles = (int)p->L.dn_tiles;
+    {
+      {
+        KernelTimer kt(p, MOE_K_DOWN);
+        launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);
+      }
+      CombineArgs ca{};
+      ca.o = w.o;
+      ca.wts = w.wts;
+      ca.inv = w.inv;
+      ca.y = y;
+      ca.T = T;
+      ca.H = H;
+      ca.k = k;
+      KernelTimer kt(p, MOE_K_COMBINE);
+      launch_combine(ca, kt.tm, s);
+    }
+    HIP_TRY(hipGetLastError());
   }
-  {
-    CombineArgs ca{};
-    ca.o = w.o;
-    ca.wts = w.wts;
-    ca.inv = w.inv;
-    ca.y = y;
-    ca.T = T;
-    ca.H = H;
-    ca.k = k;
-    KernelTimer kt(p, MOE_K_COMBINE);
-    launch_combine(ca, kt.tm, s);
-  }
-  HIP_TRY(hipGetLastError());
 
   if (ro) {
     if (ro->logits) HIP_TRY(hipMemcpyAsync(ro->logits, logits, sizeof(float) * T * E, hipMemcpyDeviceToDevice, s));

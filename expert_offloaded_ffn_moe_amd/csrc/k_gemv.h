@@ -53,7 +53,8 @@ static __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // acc + sum_i v_i x_i over one 32-wide chunk, v = 1 + n/16 (bf16 path)
-static __device__ __forceinline__ float chunk_dot_bf16(const u32x4& wv, const uint32_t* __restrict__ xr, float acc) {
+template <typename P>
+static __device__ __forceinline__ float chunk_dot_bf16(const u32x4& wv, const P& xr, float acc) {
   acc = dot2(pair0(wv.x), xr[0], acc);
   acc = dot2(pair1(wv.x), xr[1], acc);
   acc = dot2(pair2(wv.x), xr[2], acc);
@@ -74,7 +75,8 @@ static __device__ __forceinline__ float chunk_dot_bf16(const u32x4& wv, const ui
 }
 
 // acc + sum_i q_i x_i, q = n - 8 exact in fp32 (fp32 path)
-static __device__ __forceinline__ float dword_dot_f32(uint32_t d, const float* __restrict__ xr, float acc) {
+template <typename P>
+static __device__ __forceinline__ float dword_dot_f32(uint32_t d, const P& xr, float acc) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float qlo = (float)(int)((d >> (4 * j)) & 0xFu) - 8.f;
@@ -85,11 +87,12 @@ static __device__ __forceinline__ float dword_dot_f32(uint32_t d, const float* _
   return acc;
 }
 
-static __device__ __forceinline__ float chunk_dot_f32(const u32x4& wv, const float* __restrict__ xr, float acc) {
-  acc = dword_dot_f32(wv.x, xr, acc);
-  acc = dword_dot_f32(wv.y, xr + 8, acc);
-  acc = dword_dot_f32(wv.z, xr + 16, acc);
-  acc = dword_dot_f32(wv.w, xr + 24, acc);
+template <typename P>
+static __device__ __forceinline__ float chunk_dot_f32(const u32x4& wv, const P& xr, float acc) {
+  acc = dword_dot_f32(wv.x, &xr[0], acc);
+  acc = dword_dot_f32(wv.y, &xr[8], acc);
+  acc = dword_dot_f32(wv.z, &xr[16], acc);
+  acc = dword_dot_f32(wv.w, &xr[24], acc);
   return acc;
 }
 
@@ -105,73 +108,134 @@ constexpr int kMaxW = 16;   // waves per workgroup at most
 // Each batch issues kBatch code loads and their scale loads unconditionally,
 // indices clamped to the wave's last chunk/group (repeats hit in cache), then
 // computes on the groups that exist.
-template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK>
-static __device__ __forceinline__ void k_loop(guint4* codes, gushort* scales, const void* __restrict__ in,
-                                              const float* __restrict__ insum, const int64_t* rows,
-                                              const int64_t* sum_rows, int mc, int g0, int g1, float* acc) {
-  static_assert(kBatch % CPG == 0 || CPG > kBatch, "a batch holds whole groups");
-  constexpr int NB = CPG > kBatch ? CPG : kBatch;
-  constexpr int GB = NB / CPG;  // groups per batch
-  if (g1 <= g0) return;
-  const int c_last = g1 * CPG - 1;
-  for (int gb = g0; gb < g1; gb += GB) {
-    uint16_t sb[GB];
-    u32x4 wv[NB];
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// Activation chunk c of row `row` (element offset): XS == 0 reads it from global
+// memory (wave-uniform address, scalar loads), XS == 1 from the LDS copy.
+template <int XS>
+static __device__ __forceinline__ float chunk_dot_bf16_src(const u32x4& wv, const void* in, int64_t row, int c,
+                                                           float acc) {
+  if (XS) {
+    lds_u32* xr = (lds_u32*)in + row / 2 + c * 16;
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = xr[i];
+    return chunk_dot_bf16(wv, v, acc);
+  }
+  return chunk_dot_bf16(wv, static_cast<const uint32_t*>(in) + row / 2 + c * 16, acc);
+}
+
+template <int XS>
+static __device__ __forceinline__ float chunk_dot_f32_src(const u32x4& wv, const void* in, int64_t row, int c,
+                                                          float acc) {
+  if (XS) {
+    lds_f32* xr = (lds_f32*)in + row + c * 32;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = xr[i];
+    return chunk_dot_f32(wv, v, acc);
+  }
+  return chunk_dot_f32(wv, static_cast<const float*>(in) + row + c * 32, acc);
+}
+
+// One batch: kBatch code chunks (GB groups) and their scales, loaded unconditionally
+// with indices clamped to the wave's last chunk/group (repeats hit in cache).
+template <int CPG>
+struct Batch {
+  static constexpr int NB = CPG > kBatch ? CPG : kBatch;
+  static constexpr int GB = NB / CPG;
+  u32x4 wv[NB];
+  uint16_t sb[GB];
+  __device__ __forceinline__ void load(guint4* codes, gushort* scales, int gb, int g1) {
+    const int c_last = g1 * CPG - 1;
 #pragma unroll
     for (int q = 0; q < GB; ++q) sb[q] = scales[(size_t)min(gb + q, g1 - 1) * 64];
 #pragma unroll
     for (int i = 0; i < NB; ++i) wv[i] = codes[(size_t)min(gb * CPG + i, c_last) * 64];
+  }
+};
+
+// Arithmetic of one batch starting at group gb: groups past g1 repeat the last
+// group and count with weight 0 (no branch, so loads issued earlier stay ahead).
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS>
+static __device__ __forceinline__ void batch_math(const Batch<CPG>& bt, const void* __restrict__ in,
+                                                  const float* __restrict__ insum, const int64_t* rows,
+                                                  const int64_t* sum_rows, int mc, int gb, int g1, float* acc) {
 #pragma unroll
-    for (int q = 0; q < GB; ++q) {
-      // groups past g1 repeat the last group (clamped loads) and count with weight 0;
-      // no branch here, so the loads above stay ahead of all the arithmetic
-      const int g = min(gb + q, g1 - 1);
-      const float keep = (gb + q < g1) ? 1.f : 0.f;
-      float accg[MT];
+  for (int q = 0; q < Batch<CPG>::GB; ++q) {
+    const int g = min(gb + q, g1 - 1);
+    const float keep = (gb + q < g1) ? 1.f : 0.f;
+    float accg[MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) accg[m] = 0.f;
+    for (int m = 0; m < MT; ++m) accg[m] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < CPG; ++cc) {
-        const int c = g * CPG + cc;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m < mc) {
-            if (BF16) {
-              const uint32_t* xr = static_cast<const uint32_t*>(in) + rows[m] / 2 + c * 16;
-              accg[m] = chunk_dot_bf16(wv[q * CPG + cc], xr, accg[m]);
-            } else {
-              const float* xr = static_cast<const float*>(in) + rows[m] + c * 32;
-              accg[m] = chunk_dot_f32(wv[q * CPG + cc], xr, accg[m]);
-            }
-          }
-        }
-      }
-      const float s = keep * half_bits(sb[q]);
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = g * CPG + cc;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < mc) {
-          if (BF16) {
-            float xs;
-            if (SUMS_PER_CHUNK) {
-              xs = 0.f;
+          if (BF16)
+            accg[m] = chunk_dot_bf16_src<XS>(bt.wv[q * CPG + cc], in, rows[m], c, accg[m]);
+          else
+            accg[m] = chunk_dot_f32_src<XS>(bt.wv[q * CPG + cc], in, rows[m], c, accg[m]);
+        }
+      }
+    }
+    const float s = keep * half_bits(bt.sb[q]);
 #pragma unroll
-              for (int cc = 0; cc < CPG; ++cc) xs += insum[sum_rows[m] + g * CPG + cc];
-            } else {
-              xs = insum[sum_rows[m] + g];
-            }
-            acc[m] = fmaf(16.f * s, accg[m] - 1.5f * xs, acc[m]);
+    for (int m = 0; m < MT; ++m) {
+      if (m < mc) {
+        if (BF16) {
+          float xs;
+          if (SUMS_PER_CHUNK) {
+            xs = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc) xs += insum[sum_rows[m] + g * CPG + cc];
           } else {
-            acc[m] = fmaf(s, accg[m], acc[m]);
+            xs = insum[sum_rows[m] + g];
           }
+          acc[m] = fmaf(16.f * s, accg[m] - 1.5f * xs, acc[m]);
+        } else {
+          acc[m] = fmaf(s, accg[m], acc[m]);
         }
       }
     }
   }
 }
 
+// K loop of one wave over groups [g0, g1) (CPG chunks each) for MT token rows.
+// rows[m]: element offset of token m's activation row in `in`; sum_rows[m]: offset
+// of its per-group (gate/up) or per-chunk (down) sums in insum (bf16 path).
+// Each batch issues all of its loads before its arithmetic. (Issuing the next
+// batch's loads ahead of the current batch's arithmetic measured slower here:
+// the second register set costs more occupancy than the overlap gains.)
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS>
+static __device__ __forceinline__ void k_loop(guint4* codes, gushort* scales, const void* __restrict__ in,
+                                              const float* __restrict__ insum, const int64_t* rows,
+                                              const int64_t* sum_rows, int mc, int g0, int g1, float* acc) {
+  constexpr int GB = Batch<CPG>::GB;
+  for (int gb = g0; gb < g1; gb += GB) {
+    Batch<CPG> A;
+    A.load(codes, scales, gb, g1);
+    batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
+  }
+}
+
 // ----------------------------------------------------------------------------- gate/up + SwiGLU
 
-template <int BF16, int MT, int CPG>
+// Activation rows of the current token pass staged in dynamic LDS (XS == 1).
+extern __shared__ uint4 moe_dyn_lds[];
+
+// Copy MT rows of `len16` 16-byte units (rows[m] / elements given by idx) to LDS.
+static __device__ __forceinline__ void stage_rows(const void* __restrict__ src, const int64_t* src_rows16,
+                                                  int mc, int len16) {
+  const uint4* s4 = static_cast<const uint4*>(src);
+  for (int m = 0; m < mc; ++m)
+    for (int i = threadIdx.x; i < len16; i += blockDim.x) moe_dyn_lds[m * len16 + i] = s4[src_rows16[m] + i];
+}
+
+template <int BF16, int MT, int CPG, int XS>
 __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restrict__ wptr,
                                                    const int32_t* __restrict__ active,
                                                    const int32_t* __restrict__ n_active,
@@ -205,7 +269,20 @@ __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restric
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-    k_loop<BF16, MT, CPG, false>(codes, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
+    if (XS) {
+      const int len16 = H * (BF16 ? 2 : 4) / 16;
+      int64_t src16[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        src16[m] = rows[m] * (BF16 ? 2 : 4) / 16;
+        rows[m] = (int64_t)m * H;
+      }
+      stage_rows(x, src16, mc, len16);
+      __syncthreads();
+      k_loop<BF16, MT, CPG, false, XS>(codes, scales, moe_dyn_lds, xsum, rows, sum_rows, mc, g0, g1, acc);
+    } else {
+      k_loop<BF16, MT, CPG, false, XS>(codes, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
     __syncthreads();
@@ -236,7 +313,7 @@ __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restric
 
 // ----------------------------------------------------------------------------- down projection
 
-template <int BF16, int MT, int CPG>
+template <int BF16, int MT, int CPG, int XS>
 __global__ __launch_bounds__(1024) void k_down(const uint8_t* const* __restrict__ wptr,
                                                  const int32_t* __restrict__ active,
                                                  const int32_t* __restrict__ n_active,
@@ -269,7 +346,20 @@ __global__ __launch_bounds__(1024) void k_down(const uint8_t* const* __restrict_
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-    k_loop<BF16, MT, CPG, true>(codes, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
+    if (XS) {
+      const int len16 = I * (BF16 ? 2 : 4) / 16;
+      int64_t src16[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        src16[m] = rows[m] * (BF16 ? 2 : 4) / 16;
+        rows[m] = (int64_t)m * I;
+      }
+      stage_rows(h, src16, mc, len16);
+      __syncthreads();
+      k_loop<BF16, MT, CPG, true, XS>(codes, scales, moe_dyn_lds, hpart, rows, sum_rows, mc, g0, g1, acc);
+    } else {
+      k_loop<BF16, MT, CPG, true, XS>(codes, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
     __syncthreads();

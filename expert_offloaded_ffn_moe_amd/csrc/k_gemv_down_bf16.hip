@@ -9,12 +9,21 @@ static int waves_for(const GemvArgs& a) {
   return std::max(1, std::min(std::min(kMaxW, a.groups), (chunks + kBatch - 1) / kBatch));
 }
 
+// Activations from an LDS copy when an expert carries several tokens or K is
+// long (measured faster there), and the rows fit in 64 KiB; else scalar loads.
+static bool use_lds(size_t bytes, int mt, int K) { return bytes <= 65536 && (mt >= 2 || K >= 4096); }
+
 static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : max_tok <= 4 ? 4 : 8; }
 
 template <int MT, int CPG>
 static void down_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
   float* o = static_cast<float*>(a.out);
-    launch_timed(k_down<1, MT, CPG>, dim3(grid), dim3(64 * W), 0, s, tm, a.wptr, a.active, a.n_active,
+  const size_t lds = (size_t)MT * a.I * 2;
+  if (use_lds(lds, MT, a.I))
+    launch_timed(k_down<1, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.wptr, a.active, a.n_active,
+                 a.offsets, a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
+  else
+    launch_timed(k_down<1, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.wptr, a.active, a.n_active,
                  a.offsets, a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
 }
 

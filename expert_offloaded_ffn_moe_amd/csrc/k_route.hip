@@ -161,42 +161,42 @@ void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStrea
 
 // ----------------------------------------------------------------------------- top-k
 
-// One wave chooses the k experts of one token: k rounds of a DPP arg-max under
-// (logit descending, id ascending); lane j keeps slot j. Lane l holds the logits
-// of experts l, l+64, ... (NV of them); a chosen or missing one is set to -inf
-// with id INT_MAX, which never wins while a real candidate is left (k <= E).
-// Weights: the softmax of the chosen logits, exp(l_j - l_0) / sum over the chosen.
+// One wave chooses the k experts of one token, in k rounds. Lane l holds the
+// logits of experts l, l+64, ... (NV of them; missing ones are -inf). A round
+// takes the wave maximum m (DPP), then the lowest expert id whose logit equals m
+// (ballots, lowest set bit), so ties go to the lower id and -0.0 ties +0.0;
+// that logit is then set to -inf, which never wins while a real candidate is
+// left (k <= E). Lane j keeps slot j. Weights: the softmax of the chosen logits,
+// exp(l_j - l_0) / sum over the chosen.
 template <int NV>
 __device__ void topk_wave_nv(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
                              float* __restrict__ w_out, int32_t* lds_ids) {
   float v[NV];
-  int id[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    const bool ok = e < E;
-    v[i] = ok ? lrow[min(e, E - 1)] : -INFINITY;
-    id[i] = ok ? e : INT_MAX;
+    v[i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
   }
   float my_v = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = v[0];
-    int be = id[0];
+    float m = v[0];
 #pragma unroll
-    for (int i = 1; i < NV; ++i) better(bv, be, v[i], id[i]);
-    wave_argmax(bv, be);
+    for (int i = 1; i < NV; ++i) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    int win = -1;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const bool hit = id[i] == be;
-      v[i] = hit ? -INFINITY : v[i];
-      id[i] = hit ? INT_MAX : id[i];
+      const unsigned long long b = __ballot(v[i] == m);
+      if (win < 0 && b != 0ull) win = 64 * i + (int)__builtin_ctzll(b);
     }
-    my_v = (lane == j) ? bv : my_v;
-    my_e = (lane == j) ? be : my_e;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = (lane + 64 * i == win) ? -INFINITY : v[i];
+    my_v = (lane == j) ? m : my_v;
+    my_e = (lane == j) ? win : my_e;
   }
-  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
-  const float ex = (lane < k) ? __expf(my_v - m) : 0.f;
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+  const float ex = (lane < k) ? __expf(my_v - m0) : 0.f;
   const float sum = wave_sum(ex);
   if (lane < k) {
     ids_out[lane] = my_e;
@@ -344,6 +344,13 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh) {
   if (f1) a.active[pos + f0] = i1 < E ? i1 : i1 - E;
   if (tid == 0) *a.n_active = n_act;
 
+  if (a.tiles) {  // prefill GEMM tiles of kGemmRows rows, expert by expert
+    const int nt = (tid < E) ? (c + kGemmRows - 1) / kGemmRows : 0;
+    int n_all;
+    const int t0 = block_exscan(nt, sh.scan_tmp, &n_all);
+    for (int i = 0; i < nt; ++i) a.tiles[t0 + i] = make_int2(tid, i * kGemmRows);
+    if (tid == 0) *a.n_tiles = n_all;
+  }
   if (tid < E && c > 0) {
     const bool host = sh.is_host[tid] != 0;
     atomicAdd(&sh.stat[host ? 1 : 0], c);
@@ -373,60 +380,51 @@ struct DecodeShared {
 
 // The same grouping done by one wave, for n = T*k <= kRouteSmallMaxAssign
 // assignments with ids in sh.ids_small and sh.is_host loaded: no block
-// barriers, only wave-level scans. Lane l handles experts [16l, 16l+16) for
-// counts, offsets and the active list.
+// barriers, only wave-level scans and ballots. Experts are taken 64 at a time,
+// expert e = 64b + lane, so every step is one coalesced access per wave.
 __device__ void align_wave(const RouteArgs& a, DecodeShared& sh) {
   const int lane = threadIdx.x & 63;
-  const int n = a.T * a.k, E = a.E;
-  for (int e = lane; e < 1024; e += 64) {
-    sh.cnt[e] = 0;
-    sh.running[e] = 0;
+  const int n = a.T * a.k, E = a.E, NB = (E + 63) >> 6;
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = 0; b < NB; ++b) {
+    const int e = 64 * b + lane;
+    if (e < E) {
+      sh.cnt[e] = 0;
+      sh.running[e] = 0;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   for (int i = lane; i < n; i += 64) atomicAdd(&sh.cnt[sh.ids_small[i]], 1);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-  const int e0 = lane * 16;
-  int c[16], loc = 0, nh = 0, nb = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int e = e0 + j;
-    c[j] = (e < E) ? sh.cnt[e] : 0;
-    loc += c[j];
-    const bool host = (e < E) && sh.is_host[e] != 0;
-    nh += (c[j] > 0 && host) ? 1 : 0;
-    nb += (c[j] > 0 && !host) ? 1 : 0;
-  }
-  const int incl = wave_incl_scan(loc);
-  const int total = __builtin_amdgcn_readlane(incl, 63);
-  int run = incl - loc;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int e = e0 + j;
+  int carry = 0;
+  for (int b = 0; b < NB; ++b) {
+    const int e = 64 * b + lane;
+    const int c = (e < E) ? sh.cnt[e] : 0;
+    const int incl = wave_incl_scan(c);
     if (e < E) {
-      sh.off[e] = run;
-      a.offsets[e] = run;
-      a.counts[e] = c[j];
+      sh.off[e] = carry + incl - c;
+      a.offsets[e] = carry + incl - c;
+      a.counts[e] = c;
     }
-    run += c[j];
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
   if (lane == 0) {
-    sh.off[E] = total;
-    a.offsets[E] = total;
+    sh.off[E] = carry;
+    a.offsets[E] = carry;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // stable positions, 64 assignments per round in ascending order
-  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
     const bool valid = i < n;
     const int e = valid ? sh.ids_small[i] : 0;
     unsigned long long peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 10; ++b) {
-      const unsigned long long bm = __ballot(valid && ((e >> b) & 1));
-      peers &= ((e >> b) & 1) ? bm : ~bm;
+    for (int bit = 0; bit < 10; ++bit) {
+      const unsigned long long bm = __ballot(valid && ((e >> bit) & 1));
+      peers &= ((e >> bit) & 1) ? bm : ~bm;
     }
     const int rank = __popcll(peers & lt_mask);
     if (valid) {
@@ -440,34 +438,37 @@ __device__ void align_wave(const RouteArgs& a, DecodeShared& sh) {
   }
 
   // active experts: host-read ones first, then the HBM ones, ascending id in each
-  const int ih = wave_incl_scan(nh), ib = wave_incl_scan(nb);
-  const int tot_h = __builtin_amdgcn_readlane(ih, 63), tot_b = __builtin_amdgcn_readlane(ib, 63);
-  int ph = ih - nh, pb = tot_h + ib - nb, hits = 0, misses = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int e = e0 + j;
-    if (e < E && c[j] > 0) {
-      if (sh.is_host[e] != 0) {
-        a.active[ph++] = e;
-        misses += c[j];
-      } else {
-        a.active[pb++] = e;
-        hits += c[j];
+  int pos = 0, n_host = 0, hits = 0, misses = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int b = 0; b < NB; ++b) {
+      const int e = 64 * b + lane;
+      const int c = (e < E) ? sh.cnt[e] : 0;
+      const bool host = (e < E) && sh.is_host[e] != 0;
+      const bool flag = c > 0 && (pass == 0 ? host : !host);
+      const unsigned long long m = __ballot(flag);
+      if (flag) {
+        a.active[pos + __popcll(m & lt_mask)] = e;
+        atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)c);
       }
-      atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)c[j]);
+      pos += __popcll(m);
+      if (pass == 0)
+        misses += flag ? c : 0;
+      else
+        hits += flag ? c : 0;
     }
+    if (pass == 0) n_host = pos;
   }
   hits = wave_sum_i(hits);
   misses = wave_sum_i(misses);
   if (lane == 0) {
-    *a.n_active = tot_h + tot_b;
+    *a.n_active = pos;
     unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
     atomicAdd(st + ST_FORWARDS, 1ull);
     atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
     atomicAdd(st + ST_HITS, (unsigned long long)hits);
     atomicAdd(st + ST_MISSES, (unsigned long long)misses);
-    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)tot_b * a.expert_bytes));
-    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)tot_h * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)(pos - n_host) * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)n_host * a.expert_bytes));
   }
 }
 

@@ -51,6 +51,8 @@ struct RouteArgs {
   int64_t* stats;           // [ST_COUNT]
   int64_t expert_bytes;     // canonical bytes per expert (stats)
   int T, E, k;
+  int2* tiles;              // prefill: (expert, first row) of each 64-row tile, or null
+  int32_t* n_tiles;         // [1]
 };
 
 struct GemvArgs {
@@ -67,6 +69,21 @@ struct GemvArgs {
   int chunks, groups;          // K chunks of 32 and quantisation groups per row
   int tiles;                   // tiles per expert
   int H, I, G, k, T;
+};
+
+struct GemmArgs {
+  const uint8_t* const* wptr;  // [E] internal expert blobs
+  const int2* tiles;           // (expert, first row) per 64-row tile
+  const int32_t* n_tiles;      // [1]
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted;       // [T*k]
+  const uint16_t* a_src;       // gate/up: x [T][H]; down: h [T*k][I] by sorted position
+  void* out;                   // gate/up: h [T*k][I] bf16; down: o [T*k][H] fp32
+  int64_t off_codes, off_scales;
+  int chunks, groups;          // per weight row
+  int ntiles_n;                // 64-row weight tiles (gate/up: I/32, down: H/64)
+  int K, out_ld, k, G;
+  int max_tiles;               // launch bound on the number of row tiles
 };
 
 struct CombineArgs {
@@ -87,5 +104,10 @@ void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s);
 void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s);
+void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
+void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
+void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);
+constexpr int kGemmRows = 64;  // token rows per prefill GEMM tile
+
 
 }  // namespace moe

@@ -51,6 +51,17 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Maximum over the wave, broadcast to every lane (rows left out keep their value).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dppf<kDppXor1, 0xF>(v, v));
+  v = fmaxf(v, dppf<kDppXor2, 0xF>(v, v));
+  v = fmaxf(v, dppf<kDppHalfMirror, 0xF>(v, v));
+  v = fmaxf(v, dppf<kDppMirror, 0xF>(v, v));
+  v = fmaxf(v, dppf<kDppBcast15, 0xA>(v, v));
+  v = fmaxf(v, dppf<kDppBcast31, 0xC>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // One step of the arg-max: take (ov, oid) when it comes first in the order
 // (value descending, id ascending).
 __device__ __forceinline__ void better(float& v, int& id, float ov, int oid) {

@@ -13,7 +13,8 @@
  * SplitMix64 output function (Steele, Lea, Flood, "Fast splittable
  * pseudorandom number generators", OOPSLA 2014) applied to key + (i+1)*gamma,
  * gamma = 0x9E3779B97F4A7C15. Normals come in pairs from the Box-Muller
- * transform (Box & Muller 1958) of two 32-bit uniforms taken from one draw.
+ * transform (Box & Muller 1958), in single precision, of two 24-bit uniforms
+ * taken from one draw.
  */
 #include <math.h>
 #include <stdint.h>
@@ -44,12 +45,13 @@ uint64_t synth_u64(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * GAMM
 /* Normal pair number p of stream key: Box-Muller on two 32-bit uniforms in (0,1]. */
 static inline void normal_pair(uint64_t key, uint64_t p, float* z0, float* z1) {
   uint64_t r = synth_u64(key, p);
-  double u1 = ((double)(uint32_t)(r >> 32) + 1.0) * (1.0 / 4294967296.0);
-  double u2 = ((double)(uint32_t)r) * (1.0 / 4294967296.0);
-  double rad = sqrt(-2.0 * log(u1));
-  double th = 6.283185307179586476925286766559 * u2;
-  *z0 = (float)(rad * cos(th));
-  *z1 = (float)(rad * sin(th));
+  /* u1 in (0, 1] from the top 24 bits, u2 in [0, 1) from the low 24 bits */
+  float u1 = ((float)(uint32_t)(r >> 40) + 1.0f) * (1.0f / 16777216.0f);
+  float u2 = ((float)(uint32_t)(r & 0xFFFFFFu)) * (1.0f / 16777216.0f);
+  float rad = sqrtf(-2.0f * logf(u1));
+  float th = 6.28318530717958647692f * u2;
+  *z0 = rad * cosf(th);
+  *z1 = rad * sinf(th);
 }
 
 /* out[j] = mean + std * N_j, j in [0, n), N_j = normal number (first + j) of stream key. */

@@ -93,6 +93,9 @@ SMALL = [
     (384, 96, 12, 3, 32, "f32", 7, 0.5, 12),
     (512, 256, 16, 16, 128, "bf16", 5, 0.0, 13),  # k = E
     (256, 64, 5, 1, 64, "bf16", 9, 0.0, 14),     # k = 1
+    (384, 96, 12, 3, 32, "bf16", 2, 0.5, 15),    # batch 2: per-(tile, token) down + combine
+    (256, 128, 8, 2, 32, "f32", 1, 0.0, 16),     # batch 1, fp32 activations
+    (512, 256, 16, 16, 128, "bf16", 2, 0.0, 17),  # k = E = 16 at batch 2
     (2048, 768, 128, 8, 128, "bf16", 1, 0.8, 1),  # Qwen3-30B-A3B-shaped, decode batch 1
     (2048, 768, 128, 8, 128, "bf16", 4, 0.8, 1),  # and batch 4
 ]
@@ -235,4 +238,41 @@ def test_large_batch_routing_and_sampled_outputs(moe, T):
     y = run(plan, c, logits_in=lg, route=rb)
     check_routing_exact(c, ref, rb)
     check_y(y[toks], ref["y"], "y (%d sampled tokens)" % len(toks))
+    plan.destroy()
+
+
+PREFILL = [
+    # H, I, E, k, G, T, seed: T >= 256 takes the grouped MFMA GEMM path
+    (384, 96, 12, 3, 32, 300, 21),     # G = 32, 3 gate/up n-tiles (one idle wave per workgroup)
+    (512, 256, 16, 4, 128, 600, 22),
+    (2048, 768, 128, 8, 128, 1024, 4),  # Qwen3-30B-A3B-shaped prefill micro-batch
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,G,T,seed", PREFILL)
+def test_prefill_mfma_parity(moe, H, I, E, k, G, T, seed):
+    c = LC.make_case(H, I, E, k, G, "bf16", T, seed, alpha=0.5 if E < 100 else 0.0)
+    lg = LC.oracle_logits(c)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(T, min(T, 64), replace=False))
+    ref = LC.oracle_forward(c, logits_in=lg, tokens=toks)
+    plan = make_plan(moe, c, gemm_min_tokens=256)
+    rb = route_bufs(c)
+    y = run(plan, c, logits_in=lg, route=rb)
+    check_routing_exact(c, ref, rb)
+    check_y(y[toks], ref["y"], "prefill y (%d sampled tokens of %d)" % (len(toks), T))
+    # the MFMA router: logits within fp32 accumulation error, ids where unambiguous
+    rb2 = route_bufs(c)
+    y2 = run(plan, c, route=rb2)
+    glog = rb2["logits"].cpu().numpy().reshape(T, E).astype(np.float64)
+    err = np.abs(glog - lg).max()
+    tol = 1e-5 * max(1.0, np.abs(lg).max())
+    _say("  router logits max err %.3e" % err)
+    assert err <= tol
+    margins = LC.routing_margins(lg, k)
+    clear = margins > 2 * tol
+    ids = rb2["topk_ids"].cpu().numpy().reshape(T, k)
+    np.testing.assert_array_equal(ids[clear], ref["ids"][clear])
+    sel = [i for i, t in enumerate(toks) if clear[t]]
+    check_y(y2[toks[sel]], ref["y"][sel], "prefill y, MFMA router (%d tokens)" % len(sel))
     plan.destroy()
