@@ -14,6 +14,11 @@ Workloads (--workload):
   deepseek  H7168 I2048 E384 k6 G128 bf16, Zipf alpha 1.0, 70% of experts in HBM
             and the coldest 30% read from host memory (--plan mixed | hbm | host).
   prefill   the Qwen3 layer shape with 2048 (or --batch) tokens, bias-free routing.
+  cache     expert-cache decode run: 48 stacked Qwen3-shaped layers (Zipf alpha 0.8,
+            seeded per layer), HBM slots for 70% of each layer's experts, the rest read
+            from host memory; 256 single-token steps, a cache update after every step
+            from a cold start (slots hold experts 0..89), beside the static coldest-on-host
+            plan without updates. value = full-stack tokens/s.
 
 Prints one JSON line. value = layer-tokens/s over exactly --steps timed steps.
 """
@@ -39,9 +44,9 @@ def log(*a):
 
 
 def workload_dims(args):
-    if args.workload in ("decode", "prefill"):
-        return dict(H=2048, I=768, E=128, k=8, G=128, act="bf16", alpha=0.8 if args.workload == "decode" else 0.0,
-                    seed=1 if args.workload == "decode" else 4)
+    if args.workload in ("decode", "prefill", "cache"):
+        return dict(H=2048, I=768, E=128, k=8, G=128, act="bf16", alpha=0.0 if args.workload == "prefill" else 0.8,
+                    seed={"decode": 1, "prefill": 4, "cache": 3}[args.workload])
     if args.workload == "deepseek":
         return dict(H=7168, I=2048, E=384, k=6, G=128, act="bf16", alpha=1.0, seed=2)
     raise SystemExit("unknown workload")
@@ -50,15 +55,16 @@ def workload_dims(args):
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 200, prefill 40, cache 256)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "deepseek", "prefill"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "deepseek", "prefill", "cache"])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--plan", default="mixed", choices=["mixed", "hbm", "host"])
     ap.add_argument("--sweep", default=None,
                     help="comma list of plan:batch runs on the same generated layers, one JSON line each")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--max-promotions", type=int, default=8, help="cache workload: promotions per layer per update")
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
 
@@ -74,6 +80,40 @@ def make_layers(d, L, keep_blobs):
         layers.append(dict(Wr=Wr, b=b, blobs=blobs))
         log("layer %d/%d generated (%.1fs)" % (l + 1, L, time.time() - t0))
     return layers
+
+
+def roofline(per_kernel, bytes_hbm, bytes_host, assignments, H, I):
+    """Roofline of the dominant expert kernel (largest total time over the profiled pass).
+
+    GEMV kernels (decode) move weight bytes: gate/up reads 2/3 of each touched expert's
+    bytes, down 1/3. With every touched expert in HBM the peak is HBM's; with every one on
+    the host it is the host link's; with both, the peak is the rate at which those bytes
+    would move with each link at its own peak (time = hbm bytes / HBM + host bytes / link).
+    GEMM kernels (prefill) are priced in flops against bf16 MFMA: 2*A*H*2I for gate/up,
+    2*A*I*H for down, with A = T*k routed token rows.
+    """
+    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down") if n in per_kernel]
+    dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
+    t = per_kernel[dom]["avg_us"] * 1e-6
+    if dom.startswith("gemm"):
+        flops = 2.0 * assignments * H * I * (2 if dom == "gemm_gateup" else 1)
+        achieved = flops / t / 1e12
+        return dict(bound="mfma", kernel=dom, achieved=round(achieved, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                    alg_flops_per_launch=int(flops), avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
+    share = {"gateup": 2.0 / 3.0, "down": 1.0 / 3.0}[dom]
+    hb, sb = share * bytes_hbm, share * bytes_host
+    if sb == 0:
+        bound, peak = "hbm", HBM_PEAK_GBS
+    elif hb == 0:
+        bound, peak = "host-link", HOST_LINK_PEAK_GBS
+    else:
+        bound = "hbm+host-link"
+        peak = (hb + sb) / (hb / HBM_PEAK_GBS + sb / HOST_LINK_PEAK_GBS)
+    achieved = (hb + sb) / t / 1e9
+    return dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=round(peak, 1), unit="GB/s",
+                frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(hb + sb),
+                alg_bytes_hbm=int(hb), alg_bytes_host=int(sb), avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
 
 
 def run_one(args, d, layers, B, plan_kind, steps, warmup):
@@ -127,16 +167,7 @@ def run_one(args, d, layers, B, plan_kind, steps, warmup):
     fwd = max(st["forwards"], 1)
     bytes_hbm, bytes_host = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
     per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
-    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down") if n in per_kernel]
-    dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
-    frac_bytes = {"gateup": 2.0 / 3.0, "down": 1.0 / 3.0}.get(dom, 0.0)
-    host_only = bytes_hbm == 0 and bytes_host > 0
-    alg = frac_bytes * (bytes_hbm + bytes_host)
-    achieved = alg / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9
-    peak, bound = (HOST_LINK_PEAK_GBS, "host-link") if host_only else (HBM_PEAK_GBS, "hbm")
-    roof = dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=peak, unit="GB/s",
-                frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(alg),
-                avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
+    roof = roofline(per_kernel, bytes_hbm, bytes_host, B * k, H, I)
     name = {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
             "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload]
     return {
@@ -177,8 +208,20 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
     d = workload_dims(args)
-    L = args.layers or {"decode": 24, "deepseek": 3, "prefill": 4}[args.workload]
+    if args.steps is None:
+        args.steps = {"decode": 200, "deepseek": 200, "prefill": 40, "cache": 256}[args.workload]
+    L = args.layers or {"decode": 24, "deepseek": 3, "prefill": 4, "cache": 48}[args.workload]
     layers = make_layers(d, L, keep_blobs=True)
+    if args.workload == "cache":
+        out, xs_bits = run_cache(args, d, layers)
+        if not args.no_cpu:
+            cb = cpu_baseline(args, d, args.batch or 1, L, layers, xs_bits)
+            cb["value"] = round(cb["value"] / L, 6)
+            cb["unit"] = "tokens/s"
+            cb["sample"] += "; value scaled to full %d-layer steps" % L
+            out["cpu_baseline"] = cb
+        print(json.dumps(out), flush=True)
+        return
     default_plan = args.plan if args.workload == "deepseek" else "hbm"
     if args.sweep:
         runs = []
@@ -193,6 +236,110 @@ def main():
         if not args.no_cpu and i == 0:
             out["cpu_baseline"] = cpu_baseline(args, d, B, L, layers, xs_bits)
         print(json.dumps(out), flush=True)
+
+
+def run_cache(args, d, layers):
+    """Expert-cache decode run over the stacked layers: the static plan first (warm-up
+    steps, then the timed steps, no updates), then the cached plan from its cold start
+    with a cache update after every step. One step = one token batch through every layer;
+    each (step, layer) takes its own seeded activations."""
+    import numpy as np
+    import torch
+
+    import expert_offloaded_ffn_moe_amd as moe
+    import synth
+
+    H, I, E, k, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "k", "G", "act", "alpha", "seed"))
+    L, B, steps, warmup = len(layers), args.batch or 1, args.steps, args.warmup
+    S = int(round(0.7 * E))
+    eb = synth.expert_bytes(H, I, G)
+    n_x = (warmup + steps) * L
+    xb = synth.activations(seed, 7000, n_x * B, H, act)
+    xs = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda().view(n_x, B, H)
+    y = torch.empty((B, H), device="cuda")
+    out = {}
+    for mode in ("static", "cache"):
+        cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=S)
+        plan = moe.Plan(cfg)
+        for l, ly in enumerate(layers):
+            res = synth.coldest_host_plan(seed, l, E, S / E) if mode == "static" else None
+            plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], res)
+        torch.cuda.synchronize()
+        first = 0
+        if mode == "static":
+            for i in range(warmup):
+                for l in range(L):
+                    plan.forward(l, xs[i * L + l], y)
+            torch.cuda.synchronize()
+            plan.reset_stats()
+            first = warmup
+        times = []
+        t_all = time.perf_counter()
+        for i in range(first, first + steps):
+            t0 = time.perf_counter()
+            for l in range(L):
+                plan.forward(l, xs[i * L + l], y)
+            if mode == "cache":
+                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions)  # waits for the step first
+            else:
+                torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_all
+        st = plan.stats(-1)
+        log("%s plan: %d steps x %d layers in %.3fs, hit rate %.4f" % (
+            mode, steps, L, elapsed, st["hits"] / max(st["hits"] + st["misses"], 1)))
+        # profiled pass over a further 16 steps (same mode)
+        plan.profile(True)
+        n_prof = min(16, steps)
+        for i in range(first, first + n_prof):
+            for l in range(L):
+                plan.forward(l, xs[i * L + l], y)
+            if mode == "cache":
+                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions)
+        kt = plan.kernel_times()
+        plan.profile(False)
+        plan.destroy()
+        t = np.sort(np.array(times))
+        fwd = max(st["forwards"], 1)
+        per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
+        out[mode] = dict(
+            tokens_per_s=round(B * steps / elapsed, 2),
+            step_ms_median=round(float(np.median(t)) * 1e3, 4),
+            step_ms_p95=round(float(np.percentile(t, 95)) * 1e3, 4),
+            tokens_per_s_median=round(B / float(np.median(t)), 2),
+            tokens_per_s_p5=round(B / float(np.percentile(t, 95)), 2),
+            hit_rate=round(st["hits"] / max(st["hits"] + st["misses"], 1), 5),
+            hits=st["hits"], misses=st["misses"],
+            bytes_hbm_per_layer_step=int(st["bytes_hbm"] / fwd), bytes_host_per_layer_step=int(st["bytes_host"] / fwd),
+            bytes_copied=st["bytes_copied"], promotions=st["promotions"], evictions=st["evictions"],
+            kernels_us={n: round(v["avg_us"], 3) for n, v in per_kernel.items()},
+            roofline=roofline(per_kernel, st["bytes_hbm"] / fwd, st["bytes_host"] / fwd, B * k, H, I))
+    c = out["cache"]
+    res = {
+        "metric": METRIC,
+        "value": c["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 0,
+        "ms_per_step": round(1e3 * B / c["tokens_per_s"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "expert-cache decode run: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d "
+                               "int4 G%d, %d HBM slots per layer (rest host-mapped), batch %d, %d steps, cold start, "
+                               "cache update after every step (max %d promotions per layer)" % (
+                                   L, H, I, E, k, G, S, B, steps, args.max_promotions),
+                   "alpha": alpha, "seed": seed},
+        "roofline": c["roofline"],
+        "cache_run": {n: v for n, v in c.items() if n != "roofline"},
+        "static_plan": out["static"],
+    }
+    xs_bits = [xb[(i * L) * B:(i * L + 1) * B] for i in range(min(8, warmup + steps))]
+    return res, xs_bits
 
 
 def cpu_baseline(args, d, B, L, layers_host, xs_bits):

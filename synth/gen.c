@@ -42,7 +42,7 @@ uint64_t synth_key(uint64_t base, uint64_t kind, uint64_t a, uint64_t b, uint64_
 
 uint64_t synth_u64(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * GAMMA); }
 
-/* Normal pair number p of stream key: Box-Muller on two 32-bit uniforms in (0,1]. */
+/* Normal pair number p of stream key: Box-Muller on two 24-bit uniforms. */
 static inline void normal_pair(uint64_t key, uint64_t p, float* z0, float* z1) {
   uint64_t r = synth_u64(key, p);
   /* u1 in (0, 1] from the top 24 bits, u2 in [0, 1) from the low 24 bits */
