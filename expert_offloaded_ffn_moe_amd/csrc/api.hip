@@ -73,6 +73,7 @@ struct Workspace {
   float* hpart = nullptr;    // [Tmax*k][I/32]
   float* o = nullptr;        // [Tmax*k][H]
   int2* tiles = nullptr;     // [Tmax*k/64 + E] prefill GEMM row tiles
+  WorkDesc* work = nullptr;  // [E] GEMV work descriptors
   int32_t* n_tiles = nullptr;
   unsigned* route_cnt = nullptr;  // [1] arrival counter of the fused decode routing kernel
 };
@@ -294,6 +295,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(alloc_as(p, &w.o, A * H));
   TRY(alloc_as(p, &w.route_cnt, 64));
   TRY(alloc_as(p, &w.tiles, A / kGemmRows + E + 1));
+  TRY(alloc_as(p, &w.work, E));
   TRY(alloc_as(p, &w.n_tiles, 64));
 #undef TRY
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
@@ -408,9 +410,11 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.T = T;
   rt.E = E;
   rt.k = k;
+  rt.wptr = ly.d_wptr;
 
   const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
   const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
+  rt.work = prefill ? nullptr : w.work;
   if (prefill) {
     {
       KernelTimer kt(p, MOE_K_ROUTER);
@@ -489,10 +493,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   if (!prefill) {  // decode / small-batch path: dequant-GEMVs over the active experts
     const int max_act = std::min(E, A);
     GemvArgs ga{};
-    ga.wptr = ly.d_wptr;
-    ga.active = w.active;
-    ga.n_active = w.n_active;
-    ga.offsets = w.offsets;
+    ga.work = w.work;
     ga.sorted = w.sorted;
     ga.in = x;
     ga.insum = w.xsum;

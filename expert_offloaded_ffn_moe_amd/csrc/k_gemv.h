@@ -101,6 +101,10 @@ typedef __attribute__((address_space(1))) const uint16_t gushort;  // loads are 
 
 constexpr int kBatch = 8;   // chunks whose loads are issued together
 constexpr int kMaxW = 16;   // waves per workgroup at most
+// Multi-token variants keep twice the accumulators and activation registers;
+// they run at most 8 waves per workgroup so that 256 VGPRs fit without spills.
+template <int MT>
+constexpr int kMaxThreads = MT == 1 ? 1024 : 512;
 
 // K loop of one wave over groups [g0, g1) (CPG chunks each) for MT token rows.
 // rows[m]: element offset of token m's activation row in `in`; sum_rows[m]: offset
@@ -236,10 +240,7 @@ static __device__ __forceinline__ void stage_rows(const void* __restrict__ src, 
 }
 
 template <int BF16, int MT, int CPG, int XS>
-__global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restrict__ wptr,
-                                                   const int32_t* __restrict__ active,
-                                                   const int32_t* __restrict__ n_active,
-                                                   const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __restrict__ work,
                                                    const int32_t* __restrict__ sorted,
                                                    const void* __restrict__ x, const float* __restrict__ xsum,
                                                    void* __restrict__ h, float* __restrict__ hpart,
@@ -249,10 +250,15 @@ __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restric
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  if (slot >= *n_active) return;
-  const int e = active[slot];
-  const int p0 = offsets[e], M = offsets[e + 1] - p0;
-  const uint8_t* base = wptr[e];
+  // the count and the descriptor are loaded together; a slot past the count has
+  // no rows (no branch between the two loads and their use)
+  // slots past the active count carry M = 0 (written by the grouping step), so
+  // the descriptor is the only dependent load before the weights
+  const WorkDesc* d = work + slot;
+  const uint8_t* base = d->w;
+  int M = d->M;
+  asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
+  const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
   const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
@@ -262,7 +268,8 @@ __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restric
     int64_t rows[MT], sum_rows[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int t = sorted[p0 + m0 + min(m, mc - 1)] / k;
+      const int r = m0 + min(m, mc - 1);
+      const int t = (MT <= kDescTok && m0 == 0) ? d->tok[min(m, mc - 1)] : sorted[p0 + r] / k;
       rows[m] = (int64_t)t * H;
       sum_rows[m] = (int64_t)t * groups;
     }
@@ -314,10 +321,7 @@ __global__ __launch_bounds__(1024) void k_gateup(const uint8_t* const* __restric
 // ----------------------------------------------------------------------------- down projection
 
 template <int BF16, int MT, int CPG, int XS>
-__global__ __launch_bounds__(1024) void k_down(const uint8_t* const* __restrict__ wptr,
-                                                 const int32_t* __restrict__ active,
-                                                 const int32_t* __restrict__ n_active,
-                                                 const int32_t* __restrict__ offsets, const void* __restrict__ h,
+__global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __restrict__ work, const void* __restrict__ h,
                                                  const float* __restrict__ hpart, float* __restrict__ o,
                                                  int64_t off_codes, int64_t off_scales, int chunks, int groups,
                                                  int tiles, int H, int I) {
@@ -325,11 +329,13 @@ __global__ __launch_bounds__(1024) void k_down(const uint8_t* const* __restrict_
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int n_act = *n_active;
-  if (slot >= n_act) return;
-  const int e = active[slot];
-  const int p0 = offsets[e], M = offsets[e + 1] - p0;
-  const uint8_t* base = wptr[e];
+  // slots past the active count carry M = 0 (written by the grouping step), so
+  // the descriptor is the only dependent load before the weights
+  const WorkDesc* d = work + slot;
+  const uint8_t* base = d->w;
+  int M = d->M;
+  asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
+  const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
   const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;

@@ -4,9 +4,10 @@
 namespace moe {
 
 // waves per workgroup: about kBatch chunks of K per wave, at most kMaxW waves
-static int waves_for(const GemvArgs& a) {
+static int waves_for(const GemvArgs& a, int mt) {
   const int chunks = a.groups * (a.G / 32);
-  return std::max(1, std::min(std::min(kMaxW, a.groups), (chunks + kBatch - 1) / kBatch));
+  const int wmax = kMaxThreads<1> / 64 >> (mt > 1 ? 1 : 0);  // within the variant's launch bound
+  return std::max(1, std::min(std::min(wmax, a.groups), (chunks + kBatch - 1) / kBatch));
 }
 
 // Activations from an LDS copy when an expert carries several tokens or K is
@@ -20,11 +21,11 @@ static void down_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStre
   float* o = static_cast<float*>(a.out);
   const size_t lds = (size_t)MT * a.I * 4;
   if (use_lds(lds, MT, a.I))
-    launch_timed(k_down<0, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.wptr, a.active, a.n_active,
-                 a.offsets, a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
+    launch_timed(k_down<0, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.work,
+                 a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
   else
-    launch_timed(k_down<0, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.wptr, a.active, a.n_active,
-                 a.offsets, a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
+    launch_timed(k_down<0, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.work,
+                 a.in, a.insum, o, a.off_codes, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
 }
 
 template <int MT>
@@ -38,7 +39,7 @@ static void down_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hipSt
 }
 
 static void down_mt(const GemvArgs& a, int max_tok, int grid, const Timing& tm, hipStream_t s) {
-  const int W = waves_for(a);
+  const int W = waves_for(a, pick_mt(max_tok));
   switch (pick_mt(max_tok)) {
     case 1: return down_cpg<1>(a, W, grid, tm, s);
     case 2: return down_cpg<2>(a, W, grid, tm, s);

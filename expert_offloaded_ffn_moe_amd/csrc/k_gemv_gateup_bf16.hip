@@ -4,9 +4,10 @@
 namespace moe {
 
 // waves per workgroup: about kBatch chunks of K per wave, at most kMaxW waves
-static int waves_for(const GemvArgs& a) {
+static int waves_for(const GemvArgs& a, int mt) {
   const int chunks = a.groups * (a.G / 32);
-  return std::max(1, std::min(std::min(kMaxW, a.groups), (chunks + kBatch - 1) / kBatch));
+  const int wmax = kMaxThreads<1> / 64 >> (mt > 1 ? 1 : 0);  // within the variant's launch bound
+  return std::max(1, std::min(std::min(wmax, a.groups), (chunks + kBatch - 1) / kBatch));
 }
 
 // Activations from an LDS copy when an expert carries several tokens or K is
@@ -19,12 +20,12 @@ template <int MT, int CPG>
 static void gateup_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
   const size_t lds = (size_t)MT * a.H * 2;
   if (use_lds(lds, MT, a.H))
-    launch_timed(k_gateup<1, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.wptr, a.active, a.n_active,
-                 a.offsets, a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
+    launch_timed(k_gateup<1, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.work,
+                 a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
                  a.groups, a.tiles, a.H, a.I, a.k);
   else
-    launch_timed(k_gateup<1, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.wptr, a.active, a.n_active,
-                 a.offsets, a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
+    launch_timed(k_gateup<1, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.work,
+                 a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
                  a.groups, a.tiles, a.H, a.I, a.k);
 }
 
@@ -39,7 +40,7 @@ static void gateup_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hip
 }
 
 void launch_gateup_bf16(const GemvArgs& a, int max_tok, int grid, const Timing& tm, hipStream_t s) {
-  const int W = waves_for(a);
+  const int W = waves_for(a, pick_mt(max_tok));
   switch (pick_mt(max_tok)) {
     case 1: return gateup_cpg<1>(a, W, grid, tm, s);
     case 2: return gateup_cpg<2>(a, W, grid, tm, s);

@@ -7,7 +7,7 @@
 // time); softmax scores, ties to the lower expert id and renormalisation over
 // the k chosen are the plain reading of it.
 //
-// Decode (T <= 64, T*k <= 1024) runs as one launch: router blocks compute the
+// Decode (T <= 64, T*k <= 256) runs as one launch: router blocks compute the
 // logits, and the last block to finish (an atomic arrival counter, no waiting)
 // does the top-k and the grouping. Larger T uses separate launches.
 #include <hip/hip_runtime.h>
@@ -55,7 +55,7 @@ __device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, float s, 
 // each token the matching x chunks are all loaded before the dot products.
 // fp32 sums in chunk order, then a fixed DPP tree across lanes.
 template <int BF16, int NCH>
-__device__ void router_row(const RouterArgs& a, int e, int lane) {
+__device__ __forceinline__ void router_row(const RouterArgs& a, int e, int lane) {
   const int esz = BF16 ? 2 : 4;
   const int nchunk = a.H * esz / 16;
   gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
@@ -81,7 +81,7 @@ __device__ void router_row(const RouterArgs& a, int e, int lane) {
 
 // Rows longer than 64 * 16 chunks: plain strided loop.
 template <int BF16>
-__device__ void router_row_long(const RouterArgs& a, int e, int lane) {
+__device__ __forceinline__ void router_row_long(const RouterArgs& a, int e, int lane) {
   const int esz = BF16 ? 2 : 4;
   const int nchunk = a.H * esz / 16;
   gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
@@ -99,7 +99,7 @@ __device__ void router_row_long(const RouterArgs& a, int e, int lane) {
 }
 
 template <int BF16>
-__device__ void router_row_any(const RouterArgs& a, int e, int lane) {
+__device__ __forceinline__ void router_row_any(const RouterArgs& a, int e, int lane) {
   const int nch = (a.H * (BF16 ? 2 : 4) / 16 + 63) / 64;
   if (nch <= 1)
     router_row<BF16, 1>(a, e, lane);
@@ -116,7 +116,7 @@ __device__ void router_row_any(const RouterArgs& a, int e, int lane) {
 }
 
 // sum of x[t][g*G .. (g+1)*G) for flat index gid = t * (H/G) + g (bf16 x)
-__device__ void xsum_one(const RouterArgs& a, int gid) {
+__device__ __forceinline__ void xsum_one(const RouterArgs& a, int gid) {
   const int ng = a.H / a.G;
   const int t = gid / ng, g = gid % ng;
   const uint4* src =
@@ -169,7 +169,7 @@ void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStrea
 // left (k <= E). Lane j keeps slot j. Weights: the softmax of the chosen logits,
 // exp(l_j - l_0) / sum over the chosen.
 template <int NV>
-__device__ void topk_wave_nv(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
+__device__ __forceinline__ void topk_wave_nv(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
                              float* __restrict__ w_out, int32_t* lds_ids) {
   float v[NV];
 #pragma unroll
@@ -205,7 +205,7 @@ __device__ void topk_wave_nv(const float* __restrict__ lrow, int E, int k, int l
   }
 }
 
-__device__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane, int32_t* __restrict__ ids_out,
                           float* __restrict__ w_out, int32_t* lds_ids) {
   switch ((E + 63) >> 6) {
     case 1: return topk_wave_nv<1>(lrow, E, k, lane, ids_out, w_out, lds_ids);
@@ -241,7 +241,7 @@ struct AlignShared {
 };
 
 // Exclusive scan of one int per thread over a 1024-thread block; *total = sum.
-__device__ int block_exscan(int v, int* tmp, int* total) {
+__device__ __forceinline__ int block_exscan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
@@ -266,7 +266,7 @@ __device__ __forceinline__ void load_is_host(const RouteArgs& a, AlignShared& sh
 // Counts, offsets, stable permutation, active list and counters for the n = T*k
 // assignments of a.ids.
 // Called by all 1024 threads; sh.is_host must be loaded and visible.
-__device__ void align_block(const RouteArgs& a, AlignShared& sh) {
+__device__ __forceinline__ void align_block(const RouteArgs& a, AlignShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.T * a.k, E = a.E;
   sh.cnt[tid] = 0;
@@ -340,8 +340,23 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh) {
   const int f0 = flag(i0), f1 = flag(i1);
   int n_act;
   const int pos = block_exscan(f0 + f1, sh.scan_tmp, &n_act);
-  if (f0) a.active[pos] = i0 < E ? i0 : i0 - E;
-  if (f1) a.active[pos + f0] = i1 < E ? i1 : i1 - E;
+  // GEMV work descriptors; the block's own sorted[] stores are visible after the
+  // barriers above (one workgroup, one L1)
+  auto put = [&](int ap, int e) {
+    a.active[ap] = e;
+    if (!a.work) return;
+    WorkDesc d;
+    d.w = a.wptr[e];
+    d.p0 = sh.off[e];
+    d.M = sh.cnt[e];
+#pragma unroll
+    for (int j = 0; j < kDescTok; ++j) d.tok[j] = j < d.M ? a.sorted[d.p0 + j] / a.k : 0;
+    a.work[ap] = d;
+  };
+  if (f0) put(pos, i0 < E ? i0 : i0 - E);
+  if (f1) put(pos + f0, i1 < E ? i1 : i1 - E);
+  if (a.work)  // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
+    for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
   if (tid == 0) *a.n_active = n_act;
 
   if (a.tiles) {  // prefill GEMM tiles of kGemmRows rows, expert by expert
@@ -370,104 +385,211 @@ __device__ void align_block(const RouteArgs& a, AlignShared& sh) {
 }
 
 struct DecodeShared {
-  int cnt[1024];
-  int off[1025];
-  int running[1024];
   int is_host[1024];
+  const uint8_t* wptr[1024];
   int ids_small[kRouteSmallMaxAssign];
+  int a_cnt[kRouteSmallMaxAssign], a_off[kRouteSmallMaxAssign];  // per assignment: its expert's count, offset
+  uint64_t m[kRouteSmallMaxAssign / 64][10], vmask[kRouteSmallMaxAssign / 64];
+  uint64_t lead[kRouteSmallMaxAssign / 64], hostm[kRouteSmallMaxAssign / 64];
   int last;
 };
 
-// The same grouping done by one wave, for n = T*k <= kRouteSmallMaxAssign
-// assignments with ids in sh.ids_small and sh.is_host loaded: no block
-// barriers, only wave-level scans and ballots. Experts are taken 64 at a time,
-// expert e = 64b + lane, so every step is one coalesced access per wave.
-__device__ void align_wave(const RouteArgs& a, DecodeShared& sh) {
+// Counting by expert id over one 64-assignment chunk, from the chunk's bit
+// masks m[b] = ballot(bit b of the id) and the set `in` of assignments counted:
+// returns how many of them have an id below v; *eq = which of them have id v.
+// Every thread evaluates its own v with register operations on uniform masks.
+constexpr int kIdBits = 10;  // E <= 1024
+__device__ __forceinline__ int count_below(int v, const uint64_t* m, uint64_t in, int nbits, uint64_t* eq) {
+  uint64_t q = in;
+  int lt = 0;
+#pragma unroll
+  for (int b = kIdBits - 1; b >= 0; --b) {
+    if (b < nbits) {
+      const uint64_t mb = m[b];
+      const bool one = (v >> b) & 1;
+      lt += one ? __popcll(q & ~mb) : 0;
+      q &= one ? mb : ~mb;
+    }
+  }
+  *eq = q;
+  return lt;
+}
+
+// The grouping for n = T*k <= 64 assignments, by one wave with lane i holding
+// assignment i: the id-bit masks stay in scalar registers and every result
+// (positions, expert counts and offsets, active list, descriptors) comes from
+// count_below on them. The shortest code path, for the common decode batches.
+__device__ __forceinline__ void align_one(const RouteArgs& a, DecodeShared& sh) {
   const int lane = threadIdx.x & 63;
   const int n = a.T * a.k, E = a.E, NB = (E + 63) >> 6;
-  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = 0; b < NB; ++b) {
-    const int e = 64 * b + lane;
-    if (e < E) {
-      sh.cnt[e] = 0;
-      sh.running[e] = 0;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int i = lane; i < n; i += 64) atomicAdd(&sh.cnt[sh.ids_small[i]], 1);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-  int carry = 0;
-  for (int b = 0; b < NB; ++b) {
-    const int e = 64 * b + lane;
-    const int c = (e < E) ? sh.cnt[e] : 0;
-    const int incl = wave_incl_scan(c);
-    if (e < E) {
-      sh.off[e] = carry + incl - c;
-      a.offsets[e] = carry + incl - c;
-      a.counts[e] = c;
-    }
-    carry += __builtin_amdgcn_readlane(incl, 63);
-  }
-  if (lane == 0) {
-    sh.off[E] = carry;
-    a.offsets[E] = carry;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-  // stable positions, 64 assignments per round in ascending order
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    const bool valid = i < n;
-    const int e = valid ? sh.ids_small[i] : 0;
-    unsigned long long peers = __ballot(valid);
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const bool valid = lane < n;
+  const int e = valid ? sh.ids_small[lane] : 0;
+  const uint64_t vm = __ballot(valid);
+  uint64_t m[kIdBits];
 #pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const unsigned long long bm = __ballot(valid && ((e >> bit) & 1));
-      peers &= ((e >> bit) & 1) ? bm : ~bm;
-    }
-    const int rank = __popcll(peers & lt_mask);
-    if (valid) {
-      const int pos = sh.off[e] + sh.running[e] + rank;
-      a.sorted[pos] = i;
-      a.inv[i] = pos;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (valid && (peers & lt_mask) == 0) sh.running[e] += __popcll(peers);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int b = 0; b < kIdBits; ++b) m[b] = __ballot(valid && ((e >> b) & 1));
+  uint64_t eq;
+  const int off = count_below(e, m, vm, nbits, &eq);
+  const int rank = __popcll(eq & lt_mask), cnt = __popcll(eq);
+  if (valid) {
+    a.sorted[off + rank] = lane;
+    a.inv[lane] = off + rank;
   }
-
-  // active experts: host-read ones first, then the HBM ones, ascending id in each
-  int pos = 0, n_host = 0, hits = 0, misses = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int b = 0; b < NB; ++b) {
-      const int e = 64 * b + lane;
-      const int c = (e < E) ? sh.cnt[e] : 0;
-      const bool host = (e < E) && sh.is_host[e] != 0;
-      const bool flag = c > 0 && (pass == 0 ? host : !host);
-      const unsigned long long m = __ballot(flag);
-      if (flag) {
-        a.active[pos + __popcll(m & lt_mask)] = e;
-        atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)c);
-      }
-      pos += __popcll(m);
-      if (pass == 0)
-        misses += flag ? c : 0;
-      else
-        hits += flag ? c : 0;
+  const bool host = valid && sh.is_host[e] != 0;
+  const uint64_t lead = __ballot(valid && rank == 0), hm = __ballot(host);
+  const int n_host = __popcll(lead & hm), n_act = __popcll(lead), misses = __popcll(hm);
+  for (int b = 0; b < NB; ++b) {
+    const int ee = 64 * b + lane;
+    uint64_t q;
+    const int lt = count_below(ee, m, vm, nbits, &q);
+    if (ee < E) {
+      a.offsets[ee] = lt;
+      a.counts[ee] = __popcll(q);
     }
-    if (pass == 0) n_host = pos;
   }
-  hits = wave_sum_i(hits);
-  misses = wave_sum_i(misses);
+  if (lane == 0) a.offsets[E] = n;
+  if (valid && rank == 0) {
+    uint64_t q;
+    const int ap = (host ? 0 : n_host) + count_below(e, m, lead & (host ? hm : ~hm), nbits, &q);
+    a.active[ap] = e;
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)cnt);
+    WorkDesc* d = a.work + ap;
+    d->w = sh.wptr[e];
+    d->p0 = off;
+    d->M = cnt;
+    const float inv_k = 1.f / (float)a.k;
+    uint64_t mm = eq;
+    for (int j = 0; mm && j < kDescTok; ++j) {
+      d->tok[j] = (int)(((float)__builtin_ctzll(mm) + 0.5f) * inv_k);  // i / k: margin to the next integer >= 1/(2k)
+      mm &= mm - 1;
+    }
+  }
+  for (int sl = n_act + lane; sl < min(E, n); sl += 64) a.work[sl].M = 0;
   if (lane == 0) {
-    *a.n_active = pos;
+    *a.n_active = n_act;
     unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
     atomicAdd(st + ST_FORWARDS, 1ull);
     atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
-    atomicAdd(st + ST_HITS, (unsigned long long)hits);
+    atomicAdd(st + ST_HITS, (unsigned long long)(n - misses));
     atomicAdd(st + ST_MISSES, (unsigned long long)misses);
-    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)(pos - n_host) * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)(n_act - n_host) * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)n_host * a.expert_bytes));
+  }
+}
+
+// The grouping of n = T*k <= kRouteSmallMaxAssign assignments (ids in
+// sh.ids_small, sh.is_host / sh.wptr loaded) by all threads of the block.
+// Assignment i = 64c + lane sits in chunk c, handled by wave c. Each chunk's
+// wave takes one ballot per id bit; from those masks any thread finds, for an
+// id v, how many assignments have a lower id (v's offset) and which ones have
+// id v (ranks and counts). The work is split over the waves so that the short
+// one-off code paths run side by side: chunk waves place the assignments, then
+// every thread writes expert counts/offsets or, for the first assignment of an
+// expert, its active-list entry (host-read experts first, ascending ids in each
+// part) and GEMV work descriptor.
+__device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.T * a.k, E = a.E, NC = (n + 63) >> 6;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (wave < NC) {
+    const int i = 64 * wave + lane;
+    const bool valid = i < n;
+    const int e = valid ? sh.ids_small[i] : 0;
+    const uint64_t vm = __ballot(valid);
+    uint64_t mb[kIdBits];
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) mb[b] = __ballot(valid && ((e >> b) & 1));
+    if (lane == 0) {
+      sh.vmask[wave] = vm;
+#pragma unroll
+      for (int b = 0; b < kIdBits; ++b) sh.m[wave][b] = mb[b];
+    }
+  }
+  __syncthreads();
+  if (wave < NC) {  // positions in the permutation, leaders, host flags
+    const int i = 64 * wave + lane;
+    const bool valid = i < n;
+    const int e = valid ? sh.ids_small[i] : 0;
+    int lt = 0, rank = 0, cnt = 0;
+    for (int c = 0; c < NC; ++c) {
+      uint64_t eq;
+      lt += count_below(e, sh.m[c], sh.vmask[c], nbits, &eq);
+      cnt += __popcll(eq);
+      rank += c < wave ? __popcll(eq) : (c == wave ? __popcll(eq & lt_mask) : 0);
+    }
+    if (valid) {
+      a.sorted[lt + rank] = i;
+      a.inv[i] = lt + rank;
+      sh.a_cnt[i] = cnt;
+      sh.a_off[i] = lt;
+    }
+    const uint64_t ld = __ballot(valid && rank == 0), hm = __ballot(valid && sh.is_host[e] != 0);
+    if (lane == 0) {
+      sh.lead[wave] = ld;
+      sh.hostm[wave] = hm;
+    }
+  }
+  __syncthreads();
+  int n_host = 0, n_act = 0, misses = 0;
+  for (int c = 0; c < NC; ++c) {
+    n_host += __popcll(sh.lead[c] & sh.hostm[c]);
+    n_act += __popcll(sh.lead[c]);
+    misses += __popcll(sh.hostm[c]);
+  }
+  // counts and offsets of every expert
+  for (int e = tid; e < E; e += blockDim.x) {
+    int lt = 0, cnt = 0;
+    for (int c = 0; c < NC; ++c) {
+      uint64_t eq;
+      lt += count_below(e, sh.m[c], sh.vmask[c], nbits, &eq);
+      cnt += __popcll(eq);
+    }
+    a.offsets[e] = lt;
+    a.counts[e] = cnt;
+  }
+  if (tid == 0) a.offsets[E] = n;
+  // active list and work descriptors, one thread per expert (its first assignment)
+  if (tid < n && ((sh.lead[tid >> 6] >> lane) & 1)) {
+    const int c0 = tid >> 6;
+    const int e = sh.ids_small[tid];
+    const bool host = (sh.hostm[c0] >> lane) & 1;
+    int ap = host ? 0 : n_host;
+    for (int c = 0; c < NC; ++c) {
+      uint64_t eq;
+      ap += count_below(e, sh.m[c], sh.lead[c] & (host ? sh.hostm[c] : ~sh.hostm[c]), nbits, &eq);
+    }
+    const int cnt = sh.a_cnt[tid];
+    a.active[ap] = e;
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + e), (unsigned long long)cnt);
+    WorkDesc* d = a.work + ap;
+    d->w = sh.wptr[e];
+    d->p0 = sh.a_off[tid];
+    d->M = cnt;
+    const float inv_k = 1.f / (float)a.k;
+    int j = 0;
+    for (int c = 0; c < NC && j < kDescTok; ++c) {
+      uint64_t mm;
+      count_below(e, sh.m[c], sh.vmask[c], nbits, &mm);
+      while (mm && j < kDescTok) {
+        const int i = 64 * c + __builtin_ctzll(mm);
+        d->tok[j++] = (int)(((float)i + 0.5f) * inv_k);  // i / k: the margin to the next integer is >= 1/(2k)
+        mm &= mm - 1;
+      }
+    }
+  }
+  // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
+  for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
+  if (tid == 0) {
+    *a.n_active = n_act;
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
+    atomicAdd(st + ST_FORWARDS, 1ull);
+    atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
+    atomicAdd(st + ST_HITS, (unsigned long long)(n - misses));
+    atomicAdd(st + ST_MISSES, (unsigned long long)misses);
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)(n_act - n_host) * a.expert_bytes));
     atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)n_host * a.expert_bytes));
   }
 }
@@ -483,12 +605,18 @@ __global__ __launch_bounds__(1024) void k_align(RouteArgs a) {
 // (one per wave); then xsum blocks; every block then arrives on the counter,
 // and the last one (which sees every other block's logits after the
 // device-scope fences) picks the top-k of every token (one wave per token) and
-// groups the assignments in one wave.
+// groups the assignments with all of its threads.
 template <int BF16>
 __global__ __launch_bounds__(512) void k_route_decode(RouteArgs a, RouterArgs r, unsigned* counter) {
   __shared__ DecodeShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bid = blockIdx.x;
+  // residency and blob tables for the grouping step, loaded while the router
+  // runs (only the last block to arrive uses them)
+  for (int e = threadIdx.x; e < a.E; e += 512) {
+    sh.is_host[e] = a.is_host[e];
+    sh.wptr[e] = a.wptr[e];
+  }
   if (bid < r.router_blocks) {
     const int e = bid * 8 + wave;
     if (e < r.E) router_row_any<BF16>(r, e, lane);
@@ -508,13 +636,16 @@ __global__ __launch_bounds__(512) void k_route_decode(RouteArgs a, RouterArgs r,
   }
   __syncthreads();
   if (!sh.last) return;
-  for (int e = threadIdx.x; e < a.E; e += 512) sh.is_host[e] = a.is_host[e];
   if (threadIdx.x == 0) *counter = 0u;  // ready for the next launch on this stream
   for (int t = wave; t < a.T; t += 8)
     topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, lane, a.ids + (size_t)t * a.k, a.wts + (size_t)t * a.k,
               sh.ids_small + t * a.k);
   __syncthreads();
-  if (threadIdx.x < 64) align_wave(a, sh);
+  if (a.T * a.k <= 64) {
+    if (threadIdx.x < 64) align_one(a, sh);
+  } else {
+    align_small(a, sh);
+  }
 }
 
 void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,

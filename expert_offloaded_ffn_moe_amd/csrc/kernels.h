@@ -36,6 +36,16 @@ struct RouterArgs {
   int router_blocks;     // blocks computing logits (the rest compute xsum)
 };
 
+// One GEMV work item: an active expert of the current forward, written by the
+// grouping step so that the weight kernels reach both the expert's weights and
+// its first tokens' activations after a single dependent load.
+constexpr int kDescTok = 8;
+struct alignas(64) WorkDesc {
+  const uint8_t* w;        // internal blob (HBM slot or host-mapped copy)
+  int32_t p0, M;           // first sorted position of the expert's rows, number of rows
+  int32_t tok[kDescTok];   // token of each of the first min(M, kDescTok) rows
+};
+
 struct RouteArgs {
   const float* logits;      // [T][E]
   int32_t* ids;             // [T*k]
@@ -53,13 +63,12 @@ struct RouteArgs {
   int T, E, k;
   int2* tiles;              // prefill: (expert, first row) of each 64-row tile, or null
   int32_t* n_tiles;         // [1]
+  const uint8_t* const* wptr;  // [E] expert blob table (for the work descriptors)
+  WorkDesc* work;           // [E] one per active expert, in active-list order, or null
 };
 
 struct GemvArgs {
-  const uint8_t* const* wptr;  // [E] internal expert blobs (HBM slot or host-mapped copy)
-  const int32_t* active;       // [E]
-  const int32_t* n_active;     // [1]
-  const int32_t* offsets;      // [E+1]
+  const WorkDesc* work;        // [min(E, T*k)] active experts (blob, rows, first tokens), then M = 0
   const int32_t* sorted;       // [T*k]
   const void* in;              // gate/up: x [T][H]; down: h [T*k][I] (rows by sorted position)
   const float* insum;          // gate/up: xsum [T][H/G]; down: hpart [T*k][I/32] (bf16 path)
