@@ -74,6 +74,7 @@ struct Workspace {
   float* o = nullptr;        // [Tmax*k][H]
   int2* tiles = nullptr;     // [Tmax*k/64 + E] prefill GEMM row tiles
   WorkDesc* work = nullptr;  // [E] GEMV work descriptors
+  const uint8_t** aptr = nullptr;  // [Tmax*k] expert blob per assignment (fused down + combine)
   int32_t* n_tiles = nullptr;
   unsigned* route_cnt = nullptr;  // [1] arrival counter of the fused decode routing kernel
 };
@@ -296,6 +297,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(alloc_as(p, &w.route_cnt, 64));
   TRY(alloc_as(p, &w.tiles, A / kGemmRows + E + 1));
   TRY(alloc_as(p, &w.work, E));
+  TRY(alloc_as(p, &w.aptr, A));
   TRY(alloc_as(p, &w.n_tiles, 64));
 #undef TRY
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
@@ -415,6 +417,12 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
   const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
   rt.work = prefill ? nullptr : w.work;
+  // a few tokens: down projection and combine in one launch (K split over the free
+  // waves), when its (H/64) x T workgroups still keep the CUs streaming; below that
+  // the per-expert down GEMV spreads the same bytes over more workgroups
+  const int down_splits = std::max(1, std::min(16 / k, (int)p->L.dn_groups));
+  const bool fuse_down = bf16 && decode && T <= kDownCombMaxTokens && k <= 16 && (H / 64) * T >= kDownCombMinGroups;
+  rt.aptr = fuse_down ? w.aptr : nullptr;
   if (prefill) {
     {
       KernelTimer kt(p, MOE_K_ROUTER);
@@ -524,7 +532,27 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     da.chunks = (int)p->L.dn_chunks;
     da.groups = (int)p->L.dn_groups;
     da.tiles = (int)p->L.dn_tiles;
-    {
+    if (fuse_down) {
+      DownCombArgs dc{};
+      dc.aptr = w.aptr;
+      dc.inv = w.inv;
+      dc.wts = w.wts;
+      dc.h = w.h;
+      dc.hpart = w.hpart;
+      dc.y = y;
+      dc.off_codes = p->L.off_dn_codes;
+      dc.off_scales = p->L.off_dn_scales;
+      dc.chunks = (int)p->L.dn_chunks;
+      dc.groups = (int)p->L.dn_groups;
+      dc.G = G;
+      dc.H = H;
+      dc.I = I;
+      dc.k = k;
+      dc.T = T;
+      dc.splits = down_splits;
+      KernelTimer kt(p, MOE_K_DOWN);
+      launch_down_combine(dc, kt.tm, s);
+    } else {
       {
         KernelTimer kt(p, MOE_K_DOWN);
         launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);

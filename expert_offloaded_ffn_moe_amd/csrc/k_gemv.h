@@ -258,6 +258,7 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __re
   const uint8_t* base = d->w;
   int M = d->M;
   asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
+  M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
   const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
   const uint8_t* base = d->w;
   int M = d->M;
   asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
+  M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
   const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;

@@ -1,4 +1,5 @@
-// Instantiations of the decode dequant-GEMV kernels: down projection (+ fused combine), bf16 activations.
+// Decode down projection, bf16 activations: instantiations of the grouped
+// dequant-GEMV, and the down projection fused with the combine for small batches.
 #include "k_gemv.h"
 
 namespace moe {
@@ -50,6 +51,62 @@ static void down_mt(const GemvArgs& a, int max_tok, int grid, const Timing& tm, 
 
 void launch_down_bf16(const GemvArgs& a, int max_tok, int grid, const Timing& tm, hipStream_t s) {
   down_mt(a, max_tok, grid, tm, s);
+}
+
+// Down projection fused with the gate-weighted combine, for batches of a few
+// tokens: a workgroup owns (64-row tile of H, token t) and its k * S waves the
+// token's k slots, S waves per slot splitting K. Each wave streams its slot's
+// expert tile once (the same 1 KiB blocks and group scales as k_down) against
+// the slot's h row; the partial sums meet in LDS and one wave forms
+//   y[t][r] = sum over j = 0..k-1, in order, of w_j * (sum over s of part[j][s][r]).
+// No o round trip and no separate combine launch; the order of every sum is fixed.
+template <int CPG>
+__global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __restrict__ aptr,
+                                                    const int32_t* __restrict__ inv, const float* __restrict__ wts,
+                                                    const void* __restrict__ h, const float* __restrict__ hpart,
+                                                    float* __restrict__ y, int64_t off_codes, int64_t off_scales,
+                                                    int chunks, int groups, int H, int I, int k, int splits) {
+  __shared__ float part[kMaxW][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x, t = blockIdx.y;
+  const int j = wave / splits, sp = wave % splits;
+  const int slot = t * k + j;
+  const uint8_t* base = aptr[slot];
+  int p = inv[slot];
+  asm volatile("" : "+v"(p) : "v"(base));  // both loads in flight together
+  p = __builtin_amdgcn_readfirstlane(p);    // and the row stays wave-uniform (scalar loads of h)
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
+  const int g0 = (groups * sp) / splits, g1 = (groups * (sp + 1)) / splits;
+  int64_t rows[1] = {(int64_t)p * I}, sum_rows[1] = {(int64_t)p * (I / 32)};
+  float acc[1] = {0.f};
+  k_loop<1, 1, CPG, true, 0>(codes, scales, h, hpart, rows, sum_rows, 1, g0, g1, acc);
+  part[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave == 0) {
+    float yv = 0.f;
+    for (int jj = 0; jj < k; ++jj) {
+      float o = 0.f;
+      for (int s2 = 0; s2 < splits; ++s2) o += part[jj * splits + s2][lane];
+      yv = fmaf(wts[t * k + jj], o, yv);
+    }
+    y[(size_t)t * H + tile * 64 + lane] = yv;
+  }
+}
+
+void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s) {
+  const dim3 grid(a.H / 64, a.T), block(64 * a.k * a.splits);
+#define DOWN_COMB(C)                                                                                           \
+  launch_timed(k_down_comb<C>, grid, block, 0, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.off_codes,       \
+               a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits)
+  switch (a.G / 32) {
+    case 1: DOWN_COMB(1); break;
+    case 2: DOWN_COMB(2); break;
+    case 4: DOWN_COMB(4); break;
+    default: DOWN_COMB(8); break;
+  }
+#undef DOWN_COMB
 }
 
 }  // namespace moe

@@ -436,6 +436,7 @@ __device__ __forceinline__ void align_one(const RouteArgs& a, DecodeShared& sh) 
   if (valid) {
     a.sorted[off + rank] = lane;
     a.inv[lane] = off + rank;
+    if (a.aptr) a.aptr[lane] = sh.wptr[e];
   }
   const bool host = valid && sh.is_host[e] != 0;
   const uint64_t lead = __ballot(valid && rank == 0), hm = __ballot(host);
@@ -525,6 +526,7 @@ __device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh
       a.inv[i] = lt + rank;
       sh.a_cnt[i] = cnt;
       sh.a_off[i] = lt;
+      if (a.aptr) a.aptr[i] = sh.wptr[e];
     }
     const uint64_t ld = __ballot(valid && rank == 0), hm = __ballot(valid && sh.is_host[e] != 0);
     if (lane == 0) {

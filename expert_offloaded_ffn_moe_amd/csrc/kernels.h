@@ -65,6 +65,7 @@ struct RouteArgs {
   int32_t* n_tiles;         // [1]
   const uint8_t* const* wptr;  // [E] expert blob table (for the work descriptors)
   WorkDesc* work;           // [E] one per active expert, in active-list order, or null
+  const uint8_t** aptr;     // [T*k] blob of each assignment's expert (decode), or null
 };
 
 struct GemvArgs {
@@ -95,6 +96,20 @@ struct GemmArgs {
   int max_tiles;               // launch bound on the number of row tiles
 };
 
+// Down projection fused with the combine, one workgroup per (64-row tile of H,
+// token): y[t] rows = sum over the token's slots j, in order, of w_j * (Wd_e h).
+struct DownCombArgs {
+  const uint8_t* const* aptr;  // [T*k] blob of each assignment's expert
+  const int32_t* inv;          // [T*k] sorted position of each assignment (its h row)
+  const float* wts;            // [T*k]
+  const void* h;               // [T*k][I] bf16 by sorted position
+  const float* hpart;          // [T*k][I/32]
+  float* y;                    // [T][H]
+  int64_t off_codes, off_scales;
+  int chunks, groups, G, H, I, k, T;
+  int splits;                  // waves per slot (K split)
+};
+
 struct CombineArgs {
   const float* o;       // [T*k][H]
   const float* wts;     // [T*k]
@@ -105,6 +120,8 @@ struct CombineArgs {
 
 constexpr int kRouteSmallMaxAssign = 256;   // T*k handled by launch_route_decode
 constexpr int kRouteSmallMaxTokens = 64;
+constexpr int kDownCombMaxTokens = 4;     // decode batches whose down projection and combine fuse
+constexpr int kDownCombMinGroups = 128;   // ... if (H/64) * T workgroups reach this
 
 void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s);
 void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,
@@ -113,6 +130,7 @@ void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s);
 void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s);
+void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s);  // bf16, k * splits <= 16
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);

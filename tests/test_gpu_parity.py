@@ -93,11 +93,13 @@ SMALL = [
     (384, 96, 12, 3, 32, "f32", 7, 0.5, 12),
     (512, 256, 16, 16, 128, "bf16", 5, 0.0, 13),  # k = E
     (256, 64, 5, 1, 64, "bf16", 9, 0.0, 14),     # k = 1
-    (384, 96, 12, 3, 32, "bf16", 2, 0.5, 15),    # batch 2: per-(tile, token) down + combine
+    (384, 96, 12, 3, 32, "bf16", 2, 0.5, 15),    # batch 2
     (256, 128, 8, 2, 32, "f32", 1, 0.0, 16),     # batch 1, fp32 activations
     (512, 256, 16, 16, 128, "bf16", 2, 0.0, 17),  # k = E = 16 at batch 2
     (2048, 768, 128, 8, 128, "bf16", 1, 0.8, 1),  # Qwen3-30B-A3B-shaped, decode batch 1
-    (2048, 768, 128, 8, 128, "bf16", 4, 0.8, 1),  # and batch 4
+    (2048, 768, 128, 8, 128, "bf16", 4, 0.8, 1),  # and batch 4 (down projection fused with the combine)
+    (4096, 256, 24, 6, 128, "bf16", 2, 0.5, 18),  # fused down + combine: 64 tiles x 2 tokens, 12 waves
+    (8192, 128, 16, 2, 64, "bf16", 1, 0.0, 19),   # fused at batch 1: 128 tiles, k * splits = 2 * 2
 ]
 
 
