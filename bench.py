@@ -65,6 +65,9 @@ def parse_args():
                     help="comma list of plan:batch runs on the same generated layers, one JSON line each")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--max-promotions", type=int, default=8, help="cache workload: promotions per layer per update")
+    ap.add_argument("--copy-mb", type=float, default=None,
+                    help="only run 10 device-to-device copies of this many MiB (a plain copy kernel of known "
+                         "size, for scaling the memory counters of a profiler run), then exit")
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
 
@@ -207,6 +210,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_mb:
+        n = int(args.copy_mb * (1 << 20)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 10}), flush=True)
+        return
     d = workload_dims(args)
     if args.steps is None:
         args.steps = {"decode": 200, "deepseek": 200, "prefill": 40, "cache": 256}[args.workload]

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "wave.h"
 
 namespace moe {
 
@@ -26,18 +27,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
 
-__device__ __forceinline__ uint32_t pair0(uint32_t d) { return ((d << 3) & 0x00780078u) | 0x3F803F80u; }
-__device__ __forceinline__ uint32_t pair1(uint32_t d) { return ((d >> 1) & 0x00780078u) | 0x3F803F80u; }
-__device__ __forceinline__ uint32_t pair2(uint32_t d) { return ((d >> 5) & 0x00780078u) | 0x3F803F80u; }
-__device__ __forceinline__ uint32_t pair3(uint32_t d) { return ((d >> 9) & 0x00780078u) | 0x3F803F80u; }
+// (a & m) | c in one instruction. A gfx9 VOP3 instruction reads at most one
+// literal or scalar operand, so the two constants are held in vector registers
+// and passed in; the compiler would otherwise emit a separate AND and OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
 
-// 8 codes of one dword (K offsets 8d .. 8d+7 in order) -> bf16x8 of 1 + n/16
-__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d) {
+// The nibble mask 0x00780078 and the bf16 pair 1.0, 1.0 = 0x3F803F80, in vector registers.
+struct CodeConsts {
+  uint32_t m, c;
+  __device__ __forceinline__ CodeConsts() {
+    asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(m));
+    asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(c));
+  }
+};
+
+// 8 codes of one dword (K offsets 8d .. 8d+7 in order) -> bf16x8 of 1 + n/16:
+// pair j of the dword moved to mantissa bits 3..6 of both halves, then masked
+// and or-ed into 1.0
+__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d, const CodeConsts& k) {
   u32x4 p;
-  p.x = pair0(d);
-  p.y = pair1(d);
-  p.z = pair2(d);
-  p.w = pair3(d);
+  p.x = and_or(d << 3, k.m, k.c);
+  p.y = and_or(d >> 1, k.m, k.c);
+  p.z = and_or(d >> 5, k.m, k.c);
+  p.w = and_or(d >> 9, k.m, k.c);
   return __builtin_bit_cast(bf16x8_t, p);
 }
 
@@ -53,8 +69,17 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8_t& a, const bf16x8_t& b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+// sum over each aligned group of N lanes (N <= 32), in every lane: DPP steps inside a
+// row of 16 (quad xor 1, xor 2, half-row mirror, row mirror), one shuffle across rows
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if (N >= 2) v += dppf<kDppXor1, 0xF>(0.f, v);
+  if (N >= 4) v += dppf<kDppXor2, 0xF>(0.f, v);
+  if (N >= 8) v += dppf<kDppHalfMirror, 0xF>(0.f, v);
+  if (N >= 16) v += dppf<kDppMirror, 0xF>(0.f, v);
+  if (N >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
 
 // ----------------------------------------------------------------------------- router
 
@@ -110,47 +135,83 @@ void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s) {
 constexpr int kBM = 64;          // token rows per tile
 constexpr int kWaves = 4;        // waves per workgroup, one 64-row weight n-tile each
 
-// A tile of one quantisation group in LDS: kBM rows x G bf16, row stride padded by 16 bytes.
+// A tile of one quantisation group in LDS: kBM rows x G bf16, row stride padded
+// by 16 bytes; two of them, so staging group g + 1 overlaps the MFMAs of group g.
 template <int G>
 struct GemmShared {
   static constexpr int kStride = G * 2 + 16;  // bytes
-  uint8_t a[kBM * kStride];
-  float rowsum[kBM];
+  alignas(16) uint8_t a[2][kBM * kStride];
+  float rowsum[2][kBM];
 };
+
+// sum of the 8 bf16 of a 16-byte piece, by dot products with (1, 1)
+__device__ __forceinline__ float piece_sum(const uint4& v) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), one, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z), one, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w), one, s, false);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8), each XCD
+// with its own L2. Logical block ids are laid out so that each XCD runs one
+// contiguous range of them: the workgroups of one row tile (same gathered
+// activation rows) and of neighbouring row tiles (same expert's weights) then
+// share an L2.
+__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
+  constexpr int kXcd = 8;
+  const int per = nb / kXcd, rem = nb % kXcd;
+  const int x = b % kXcd, i = b / kXcd;
+  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
 
 // One workgroup: tile (expert e, rows [m0, m0 + 64) of its tokens) x 4 weight
 // n-tiles of 64 rows. GATEUP: A = gathered x rows (K = H), n-tile = 32 gate + 32
 // up rows, epilogue SwiGLU -> h (bf16, by sorted position). Otherwise: A = h rows
 // (K = I), n-tile = 64 down rows, epilogue -> o (fp32, by sorted position).
+// Per quantisation group: the A rows and the wave's codes and scales of group
+// g + 1 are loaded into registers while group g runs on the MFMAs.
 template <int G, bool GATEUP>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* const* __restrict__ wptr,
-                                              const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-                                              const int32_t* __restrict__ offsets,
-                                              const int32_t* __restrict__ sorted, const uint16_t* __restrict__ a_src,
-                                              void* __restrict__ out, int64_t off_codes, int64_t off_scales,
-                                              int chunks, int groups, int ntiles_n, int K, int out_ld, int k) {
+__global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restrict__ wptr,
+                                                 const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ sorted, const uint16_t* __restrict__ a_src,
+                                                 void* __restrict__ out, int64_t off_codes, int64_t off_scales,
+                                                 int chunks, int groups, int ntiles_n, int K, int out_ld, int k) {
   constexpr int CPG = G / 32;
   __shared__ GemmShared<G> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ngroup_wg = (ntiles_n + kWaves - 1) / kWaves;
-  const int tile_idx = blockIdx.x / ngroup_wg;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int tile_idx = lb / ngroup_wg;
   if (tile_idx >= *n_tiles) return;
-  const int nt = (blockIdx.x % ngroup_wg) * kWaves + wave;
+  const int nt = (lb % ngroup_wg) * kWaves + wave;
   const bool active_wave = nt < ntiles_n;
   const int2 tl = tiles[tile_idx];
   const int e = tl.x, m0 = tl.y;
   const int p0 = offsets[e], M = offsets[e + 1] - p0;
   const int mrows = min(kBM, M - m0);
+  const bool two = mrows > 32;  // second 32-row block has rows
 
-  // staging assignment: 4 threads per row, G/32 16-byte pieces each
-  const int srow = threadIdx.x >> 2, spart = threadIdx.x & 3;
-  const int src_r = min(srow, mrows - 1);
-  const int64_t src_row = GATEUP ? (int64_t)(sorted[p0 + m0 + src_r] / k) : (int64_t)(p0 + m0 + src_r);
-  const uint16_t* src = a_src + src_row * K;
+  // staging assignment: a group's A tile is 64 rows of PPR = G/8 16-byte pieces;
+  // thread t stages pieces t + 256 q (q < CPG): row (t + 256 q) / PPR, piece t % PPR,
+  // so PPR consecutive lanes cover one row's contiguous bytes (no LDS bank conflicts)
+  constexpr int PPR = G / 8;
+  const int spiece = threadIdx.x % PPR;
+  const uint4* src[CPG];
+#pragma unroll
+  for (int q = 0; q < CPG; ++q) {
+    const int r = min((int)(threadIdx.x + 256 * q) / PPR, mrows - 1);
+    const int64_t row = GATEUP ? (int64_t)(sorted[p0 + m0 + r] / k) : (int64_t)(p0 + m0 + r);
+    src[q] = reinterpret_cast<const uint4*>(a_src + row * K) + spiece;
+  }
+  const CodeConsts kc;
 
   const uint8_t* base = wptr[e];
   gu32x4* codes = (gu32x4*)(base + off_codes) + (size_t)(active_wave ? nt : 0) * chunks * 64 + lane;
   gu16* scales = (gu16*)(base + off_scales) + (size_t)(active_wave ? nt : 0) * groups * 64;
+  const int i32 = lane & 31, half = lane >> 5;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -158,64 +219,83 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* const* __restrict__
 #pragma unroll
     for (int o = 0; o < 2; ++o) acc[s][o] = f32x16{};
 
-  const int i32 = lane & 31, half = lane >> 5;
+  // group 0 in registers
+  uint4 av[CPG];
+  u32x4 bv[CPG];
+  uint16_t sc0b, sc1b;
+#pragma unroll
+  for (int q = 0; q < CPG; ++q) av[q] = src[q][0];
+#pragma unroll
+  for (int cc = 0; cc < CPG; ++cc) bv[cc] = codes[(size_t)cc * 64];
+  sc0b = scales[i32];
+  sc1b = scales[32 + i32];
+
   for (int g = 0; g < groups; ++g) {
-    // stage A[64][G] of this group, with per-row sums
-    __syncthreads();
-    {
-      float rs = 0.f;
+    const int buf = g & 1;
+    {  // A rows of group g -> LDS, with their sums (reduced over the PPR lanes of a row)
 #pragma unroll
       for (int q = 0; q < CPG; ++q) {
-        const int piece = spart * CPG + q;  // 16-byte piece (8 values) of the row
-        const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)g * G + piece * 8);
-        *reinterpret_cast<uint4*>(sh.a + srow * GemmShared<G>::kStride + piece * 16) = v;
-        rs += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) + bf16_hi(v.z) +
-              bf16_lo(v.w) + bf16_hi(v.w);
+        const int P = threadIdx.x + 256 * q;
+        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<G>::kStride + spiece * 16) = av[q];
+        const float rs = lane_group_sum<PPR>(piece_sum(av[q]));
+        if (spiece == 0) sh.rowsum[buf][P / PPR] = rs;
       }
-      rs += __shfl_xor(rs, 1, 64);
-      rs += __shfl_xor(rs, 2, 64);
-      if (spart == 0) sh.rowsum[srow] = rs;
     }
-    __syncthreads();
-    if (!active_wave) continue;
-    const float sc0 = half_bits(scales[(size_t)g * 64 + i32]);
-    const float sc1 = half_bits(scales[(size_t)g * 64 + 32 + i32]);
-    f32x16 ag[2][2];
+    // group g + 1 (clamped to the last group) into registers while g computes
+    const int gn = min(g + 1, groups - 1);
+    uint4 avn[CPG];
+    u32x4 bvn[CPG];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int q = 0; q < CPG; ++q) avn[q] = src[q][(size_t)gn * PPR];
 #pragma unroll
-      for (int o = 0; o < 2; ++o) ag[s][o] = f32x16{};
+    for (int cc = 0; cc < CPG; ++cc) bvn[cc] = codes[(size_t)(gn * CPG + cc) * 64];
+    const uint16_t sc0n = scales[(size_t)gn * 64 + i32], sc1n = scales[(size_t)gn * 64 + 32 + i32];
+    __syncthreads();  // buffer `buf` complete; the other one is no longer read
+    if (active_wave) {
+      f32x16 ag[2][2];
 #pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) {
-      const int c = g * CPG + cc;
-      u32x4 wv = codes[(size_t)c * 64];
-      // lanes 0-31 hold n-tile rows 0-31 (gate), lanes 32-63 rows 32-63 (up / second
-      // half), 32 K values each; the swaps give each half's K 0-15 and 16-31 operands
-      const auto s01 = __builtin_amdgcn_permlane32_swap(wv.x, wv.y, false, false);
-      const auto s23 = __builtin_amdgcn_permlane32_swap(wv.z, wv.w, false, false);
-      const bf16x8_t b00 = codes_to_bf16(s01[0]), b10 = codes_to_bf16(s01[1]);  // k-step 0: half 0, half 1
-      const bf16x8_t b01 = codes_to_bf16(s23[0]), b11 = codes_to_bf16(s23[1]);  // k-step 1
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) ag[s][o] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < CPG; ++cc) {
+        // lanes 0-31 hold n-tile rows 0-31 (gate), lanes 32-63 rows 32-63 (up / second
+        // half), 32 K values each; the swaps give each half's K 0-15 and 16-31 operands
+        const auto s01 = __builtin_amdgcn_permlane32_swap(bv[cc].x, bv[cc].y, false, false);
+        const auto s23 = __builtin_amdgcn_permlane32_swap(bv[cc].z, bv[cc].w, false, false);
+        const bf16x8_t b00 = codes_to_bf16(s01[0], kc), b10 = codes_to_bf16(s01[1], kc);  // k-step 0: half 0, half 1
+        const bf16x8_t b01 = codes_to_bf16(s23[0], kc), b11 = codes_to_bf16(s23[1], kc);  // k-step 1
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (s == 1 && !two) break;
+          const uint8_t* arow = sh.a[buf] + (32 * s + i32) * GemmShared<G>::kStride + cc * 64 + half * 16;
+          const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow));
+          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32));
+          ag[s][0] = mfma(a0, b00, ag[s][0]);
+          ag[s][1] = mfma(a0, b10, ag[s][1]);
+          ag[s][0] = mfma(a1, b01, ag[s][0]);
+          ag[s][1] = mfma(a1, b11, ag[s][1]);
+        }
+      }
+      // acc += 16 * s * (sum x v - 1.5 * sum x), per output element
+      const float f0 = 16.f * half_bits(sc0b), f1 = 16.f * half_bits(sc1b);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint8_t* arow = sh.a + (32 * s + i32) * GemmShared<G>::kStride + cc * 64 + half * 16;
-        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow));
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32));
-        ag[s][0] = mfma(a0, b00, ag[s][0]);
-        ag[s][1] = mfma(a0, b10, ag[s][1]);
-        ag[s][0] = mfma(a1, b01, ag[s][0]);
-        ag[s][1] = mfma(a1, b11, ag[s][1]);
+        if (s == 1 && !two) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float r15 = 1.5f * sh.rowsum[buf][32 * s + 8 * (v / 4) + 4 * half + (v % 4)];
+          acc[s][0][v] = fmaf(f0, ag[s][0][v] - r15, acc[s][0][v]);
+          acc[s][1][v] = fmaf(f1, ag[s][1][v] - r15, acc[s][1][v]);
+        }
       }
     }
-    // acc += 16 * s * (sum x v - 1.5 * sum x), per output element
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int q = 0; q < CPG; ++q) av[q] = avn[q];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float r15 = 1.5f * sh.rowsum[32 * s + 8 * (v / 4) + 4 * half + (v % 4)];
-        acc[s][0][v] = fmaf(16.f * sc0, ag[s][0][v] - r15, acc[s][0][v]);
-        acc[s][1][v] = fmaf(16.f * sc1, ag[s][1][v] - r15, acc[s][1][v]);
-      }
-    }
+    for (int cc = 0; cc < CPG; ++cc) bv[cc] = bvn[cc];
+    sc0b = sc0n;
+    sc1b = sc1n;
   }
   if (!active_wave) return;
 #pragma unroll
