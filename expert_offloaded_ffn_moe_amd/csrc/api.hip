@@ -75,8 +75,10 @@ struct Workspace {
   int2* tiles = nullptr;     // [Tmax*k/64 + E] prefill GEMM row tiles
   WorkDesc* work = nullptr;  // [E] GEMV work descriptors
   const uint8_t** aptr = nullptr;  // [Tmax*k] expert blob per assignment (fused down + combine)
+  int32_t* hist = nullptr;   // [ceil(Tmax/16)][E] block counts / bases of the multi-block grouping
+  int32_t* act_pos = nullptr;  // [E]
   int32_t* n_tiles = nullptr;
-  unsigned* route_cnt = nullptr;  // [1] arrival counter of the fused decode routing kernel
+  unsigned* route_cnt = nullptr;  // [64] arrival counters: [0] fused decode routing, [16] multi-block grouping
 };
 
 }  // namespace
@@ -298,6 +300,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(alloc_as(p, &w.tiles, A / kGemmRows + E + 1));
   TRY(alloc_as(p, &w.work, E));
   TRY(alloc_as(p, &w.aptr, A));
+  TRY(alloc_as(p, &w.hist, (size_t)((Tm + kGroupTokens - 1) / kGroupTokens) * E));
+  TRY(alloc_as(p, &w.act_pos, E));
   TRY(alloc_as(p, &w.n_tiles, 64));
 #undef TRY
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
@@ -413,6 +417,8 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.E = E;
   rt.k = k;
   rt.wptr = ly.d_wptr;
+  rt.hist = w.hist;
+  rt.act_pos = w.act_pos;
 
   const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
   const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
@@ -432,7 +438,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     rt.n_tiles = w.n_tiles;
     {
       KernelTimer kt(p, MOE_K_ROUTE);
-      launch_topk_align(rt, kt.tm, s);
+      launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
     }
     GemmArgs gg{};
     gg.wptr = ly.d_wptr;
@@ -495,7 +501,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       launch_router(ra, bf16, kt.tm, s);
     }
     KernelTimer kt(p, MOE_K_ROUTE);
-    launch_topk_align(rt, kt.tm, s);
+    launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
   }
 
   if (!prefill) {  // decode / small-batch path: dequant-GEMVs over the active experts

@@ -83,50 +83,57 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 
 // ----------------------------------------------------------------------------- router
 
-// logits[t][e] = sum_h x[t][h] * Wr[e][h] + b[e]: one wave per 32 x 32 output
-// tile, operands read straight from global memory (x and Wr rows are K-contiguous).
-__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                     const float* __restrict__ b, float* __restrict__ logits, int T,
-                                                     int H, int E) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+// logits[t][e] = sum_h x[t][h] * Wr[e][h] + b[e]: one workgroup per 32 x 32
+// output tile, its 8 waves splitting K (operands straight from global memory,
+// x and Wr rows are K-contiguous); the partial tiles are added in LDS in wave order.
+constexpr int kRouterWaves = 8;
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w,
+                                                                   const float* __restrict__ b,
+                                                                   float* __restrict__ logits, int T, int H, int E) {
+  __shared__ float part[kRouterWaves][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nte = (E + 31) / 32;
-  const int mt = wave / nte, et = wave % nte;
-  if (mt * 32 >= T) return;
+  const int mt = blockIdx.x / nte, et = blockIdx.x % nte;
   const int i = lane & 31, half = lane >> 5;
   const int row = min(mt * 32 + i, T - 1), col = min(et * 32 + i, E - 1);
   gu32x4* xa = (gu32x4*)(x + (size_t)row * H) + half;
   gu32x4* wb = (gu32x4*)(w + (size_t)col * H) + half;
+  const int ks_all = H / 16;  // k-steps of 16
+  const int k0 = (ks_all * wave) / kRouterWaves, k1 = (ks_all * (wave + 1)) / kRouterWaves;
   f32x16 acc = {};
-  int k0 = 0;
-  for (; k0 + 128 <= H; k0 += 128) {  // 8 k-steps: all 16 loads before the MFMAs
+  for (int ks = k0; ks < k1; ks += 8) {  // 8 k-steps: all 16 loads before the MFMAs
     u32x4 av[8], bv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      av[q] = xa[(k0 + 16 * q) / 8];
-      bv[q] = wb[(k0 + 16 * q) / 8];
+      const int kq = min(ks + q, k1 - 1);
+      av[q] = xa[2 * kq];
+      bv[q] = wb[2 * kq];
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc = mfma(__builtin_bit_cast(bf16x8_t, av[q]), __builtin_bit_cast(bf16x8_t, bv[q]), acc);
+    for (int q = 0; q < 8; ++q)
+      if (ks + q < k1) acc = mfma(__builtin_bit_cast(bf16x8_t, av[q]), __builtin_bit_cast(bf16x8_t, bv[q]), acc);
   }
-  for (; k0 < H; k0 += 16) {
-    const u32x4 av = xa[k0 / 8], bv = wb[k0 / 8];
-    acc = mfma(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc);
-  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) part[wave][v][lane] = acc[v];
+  __syncthreads();
+  if (wave != 0) return;
   const int j = et * 32 + i;
-  if (j < E) {
-    const float bias = b ? b[j] : 0.f;
+  if (j >= E) return;
+  const float bias = b ? b[j] : 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = mt * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-      if (r < T) logits[(size_t)r * E + j] = acc[v] + bias;
-    }
+  for (int v = 0; v < 16; ++v) {
+    float sum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kRouterWaves; ++ww) sum += part[ww][v][lane];
+    const int r = mt * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+    if (r < T) logits[(size_t)r * E + j] = sum + bias;
   }
 }
 
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s) {
-  const int waves = ((a.T + 31) / 32) * ((a.E + 31) / 32);
-  launch_timed(k_router_mfma, dim3((waves + 3) / 4), dim3(256), 0, s, tm, static_cast<const uint16_t*>(a.x),
+  const int blocks = ((a.T + 31) / 32) * ((a.E + 31) / 32);
+  launch_timed(k_router_mfma, dim3(blocks), dim3(64 * kRouterWaves), 0, s, tm, static_cast<const uint16_t*>(a.x),
                static_cast<const uint16_t*>(a.w), a.b, a.logits, a.T, a.H, a.E);
 }
 

@@ -9,7 +9,8 @@
 //
 // Decode (T <= 64, T*k <= 256) runs as one launch: router blocks compute the
 // logits, and the last block to finish (an atomic arrival counter, no waiting)
-// does the top-k and the grouping. Larger T uses separate launches.
+// does the top-k and the grouping. Larger T: top-k with per-block counts, then a
+// block-parallel scatter (two launches).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -220,25 +221,9 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E,
   }
 }
 
-__global__ __launch_bounds__(1024) void k_topk(RouteArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 16 + wave;
-  if (t >= a.T) return;
-  topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, lane, a.ids + (size_t)t * a.k, a.wts + (size_t)t * a.k, nullptr);
-}
 
 // ----------------------------------------------------------------------------- align / permute
 
-struct AlignShared {
-  int cnt[1024];
-  int off[1025];
-  int running[1024];
-  int is_host[1024];
-  int wave_cnt[16][1024];
-  int scan_tmp[16];
-  int stat[4];  // hits, misses, unique hbm, unique host
-  int last;
-};
 
 // Exclusive scan of one int per thread over a 1024-thread block; *total = sum.
 __device__ __forceinline__ int block_exscan(int v, int* tmp, int* total) {
@@ -258,132 +243,7 @@ __device__ __forceinline__ int block_exscan(int v, int* tmp, int* total) {
   return base + incl - v;
 }
 
-__device__ __forceinline__ void load_is_host(const RouteArgs& a, AlignShared& sh) {
-  const int tid = threadIdx.x;
-  sh.is_host[tid] = tid < a.E ? a.is_host[tid] : 0;
-}
-
-// Counts, offsets, stable permutation, active list and counters for the n = T*k
-// assignments of a.ids.
-// Called by all 1024 threads; sh.is_host must be loaded and visible.
-__device__ __forceinline__ void align_block(const RouteArgs& a, AlignShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = a.T * a.k, E = a.E;
-  sh.cnt[tid] = 0;
-  sh.running[tid] = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) sh.wave_cnt[w][tid] = 0;
-  if (tid < 4) sh.stat[tid] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += 1024) {
-    const int e = a.ids[i];
-    atomicAdd(&sh.cnt[e], 1);
-  }
-  __syncthreads();
-  int total;
-  const int c = (tid < E) ? sh.cnt[tid] : 0;
-  const int ex = block_exscan(c, sh.scan_tmp, &total);
-  if (tid < E) {
-    sh.off[tid] = ex;
-    a.counts[tid] = c;
-    a.offsets[tid] = ex;
-  }
-  if (tid == 0) {
-    sh.off[E] = total;
-    a.offsets[E] = total;
-  }
-  __syncthreads();
-
-  // stable scatter, 1024 assignments per round in ascending order
-  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + tid;
-    const bool valid = i < n;
-    const int e = valid ? (a.ids[i]) : 0;
-    unsigned long long peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 10; ++b) {
-      const unsigned long long bm = __ballot(valid && ((e >> b) & 1));
-      peers &= ((e >> b) & 1) ? bm : ~bm;
-    }
-    const int rank = __popcll(peers & lt_mask);
-    if (valid && (peers & lt_mask) == 0) sh.wave_cnt[wave][e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int before = 0;
-      for (int w = 0; w < wave; ++w) before += sh.wave_cnt[w][e];
-      const int pos = sh.off[e] + sh.running[e] + before + rank;
-      a.sorted[pos] = i;
-      a.inv[i] = pos;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int s = 0;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        s += sh.wave_cnt[w][tid];
-        sh.wave_cnt[w][tid] = 0;
-      }
-      sh.running[tid] += s;
-    }
-    __syncthreads();
-  }
-
-  // active experts, host-read ones first: scan over 2E flags, two per thread
-  const int i0 = 2 * tid, i1 = 2 * tid + 1;
-  auto flag = [&](int it) -> int {
-    if (it >= 2 * E) return 0;
-    const int e = it < E ? it : it - E;
-    const bool host = sh.is_host[e] != 0;
-    return (sh.cnt[e] > 0 && (it < E ? host : !host)) ? 1 : 0;
-  };
-  const int f0 = flag(i0), f1 = flag(i1);
-  int n_act;
-  const int pos = block_exscan(f0 + f1, sh.scan_tmp, &n_act);
-  // GEMV work descriptors; the block's own sorted[] stores are visible after the
-  // barriers above (one workgroup, one L1)
-  auto put = [&](int ap, int e) {
-    a.active[ap] = e;
-    if (!a.work) return;
-    WorkDesc d;
-    d.w = a.wptr[e];
-    d.p0 = sh.off[e];
-    d.M = sh.cnt[e];
-#pragma unroll
-    for (int j = 0; j < kDescTok; ++j) d.tok[j] = j < d.M ? a.sorted[d.p0 + j] / a.k : 0;
-    a.work[ap] = d;
-  };
-  if (f0) put(pos, i0 < E ? i0 : i0 - E);
-  if (f1) put(pos + f0, i1 < E ? i1 : i1 - E);
-  if (a.work)  // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
-    for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
-  if (tid == 0) *a.n_active = n_act;
-
-  if (a.tiles) {  // prefill GEMM tiles of kGemmRows rows, expert by expert
-    const int nt = (tid < E) ? (c + kGemmRows - 1) / kGemmRows : 0;
-    int n_all;
-    const int t0 = block_exscan(nt, sh.scan_tmp, &n_all);
-    for (int i = 0; i < nt; ++i) a.tiles[t0 + i] = make_int2(tid, i * kGemmRows);
-    if (tid == 0) *a.n_tiles = n_all;
-  }
-  if (tid < E && c > 0) {
-    const bool host = sh.is_host[tid] != 0;
-    atomicAdd(&sh.stat[host ? 1 : 0], c);
-    atomicAdd(&sh.stat[host ? 3 : 2], 1);
-    atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + tid), (unsigned long long)c);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
-    atomicAdd(st + ST_FORWARDS, 1ull);
-    atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
-    atomicAdd(st + ST_HITS, (unsigned long long)sh.stat[0]);
-    atomicAdd(st + ST_MISSES, (unsigned long long)sh.stat[1]);
-    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)sh.stat[2] * a.expert_bytes));
-    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)sh.stat[3] * a.expert_bytes));
-  }
-}
-
+// LDS of the fused decode routing kernel's tail (the last block to arrive).
 struct DecodeShared {
   int is_host[1024];
   const uint8_t* wptr[1024];
@@ -596,12 +456,6 @@ __device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh
   }
 }
 
-__global__ __launch_bounds__(1024) void k_align(RouteArgs a) {
-  __shared__ AlignShared sh;
-  load_is_host(a, sh);
-  __syncthreads();
-  align_block(a, sh);
-}
 
 // Decode routing in one launch. Blocks [0, router_blocks): 8 expert rows each
 // (one per wave); then xsum blocks; every block then arrives on the counter,
@@ -660,12 +514,214 @@ void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, 
     launch_timed(k_route_decode<0>, dim3(grid), dim3(512), 0, s, tm, a, r, counter);
 }
 
-void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s) {
+
+// ----------------------------------------------------------------------------- multi-block grouping
+
+// Top-k and grouping for any number of assignments, over blocks of kGroupTokens
+// tokens. k_topk_count: each block picks its tokens' experts (one wave per
+// token) and counts them per expert; the last block to arrive turns the block
+// counts into expert counts, offsets and per-block bases (expert e's rows from
+// block b start at offsets[e] + the counts of e in blocks before b), and writes
+// the active list (host-read experts first), GEMV descriptors, GEMM row tiles,
+// counters and stats. k_scatter: each block places its assignments at its bases
+// plus their rank among the block's earlier assignments to the same expert, so
+// the permutation is the stable one; it also fills the descriptors' first tokens.
+struct CountShared {
+  int cnt[1024];
+  int off[1024];
+  int is_host[1024];
+  int ids[kGroupTokens * 32];
+  int scan_tmp[16];
+  int stat[4];
+  int last;
+};
+
+__global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* counter) {
+  __shared__ CountShared sh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int E = a.E, k = a.k, nb = gridDim.x;
+  const int t0 = blockIdx.x * kGroupTokens, nt = min(kGroupTokens, a.T - t0);
+  sh.cnt[tid] = 0;
+  sh.is_host[tid] = tid < E ? a.is_host[tid] : 0;
+  if (tid < 4) sh.stat[tid] = 0;
+  if (wave < nt) {
+    const int t = t0 + wave;
+    topk_wave(a.logits + (size_t)t * E, E, k, lane, a.ids + (size_t)t * k, a.wts + (size_t)t * k, sh.ids + wave * k);
+  }
+  __syncthreads();
+  if (tid < nt * k) atomicAdd(&sh.cnt[sh.ids[tid]], 1);
+  __syncthreads();
+  if (tid < E) a.hist[(size_t)blockIdx.x * E + tid] = sh.cnt[tid];
+  // publish, arrive; the last block sees every block's counts
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const unsigned prev = atomicAdd(counter, 1u);
+    sh.last = (prev == (unsigned)nb - 1) ? 1 : 0;
+    if (sh.last) __threadfence();
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  if (tid == 0) *counter = 0u;  // ready for the next launch on this stream
+  const int n = a.T * k;
+  // expert totals, offsets and per-block bases (written over the counts): J threads
+  // per expert, thread (e = tid % E, j = tid / E) summing blocks [j nb / J, (j+1) nb / J)
+  const int J = max(1, (int)blockDim.x / E);
+  const int ej = tid % E, jj = tid / E;
+  const bool sum_thread = jj < J;
+  const int b0 = (nb * jj) / J, b1 = (nb * (jj + 1)) / J;
+  int part = 0;
+  if (sum_thread) {
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {  // four loads in flight
+      const int h0 = a.hist[(size_t)b * E + ej], h1 = a.hist[(size_t)(b + 1) * E + ej];
+      const int h2 = a.hist[(size_t)(b + 2) * E + ej], h3 = a.hist[(size_t)(b + 3) * E + ej];
+      part += (h0 + h1) + (h2 + h3);
+    }
+    for (; b < b1; ++b) part += a.hist[(size_t)b * E + ej];
+  }
+  int* jpart = sh.off;  // [J][E] partial sums (J * E <= 1024)
+  if (sum_thread) jpart[jj * E + ej] = part;
+  __syncthreads();
+  int c = 0;
+  if (tid < E)
+    for (int j = 0; j < J; ++j) c += jpart[j * E + tid];
+  int jbefore = 0;
+  if (sum_thread)
+    for (int j = 0; j < jj; ++j) jbefore += jpart[j * E + ej];
+  int total;
+  const int off = block_exscan(c, sh.scan_tmp, &total);  // (barriers inside: jpart reads are done)
+  if (tid < E) {
+    a.counts[tid] = c;
+    a.offsets[tid] = off;
+    sh.cnt[tid] = off;  // offsets for the base pass
+  }
+  if (tid == 0) a.offsets[E] = n;
+  __syncthreads();
+  if (sum_thread) {
+    int run = sh.cnt[ej] + jbefore;
+    for (int b = b0; b < b1; ++b) {
+      const int hb = a.hist[(size_t)b * E + ej];
+      a.hist[(size_t)b * E + ej] = run;
+      run += hb;
+    }
+  }
+  __syncthreads();
+  // active experts, host-read ones first: scan over 2E flags, two per thread
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  sh.cnt[tid] = c;
+  sh.off[tid] = off;
+  __syncthreads();
+  auto flag = [&](int it) -> int {
+    if (it >= 2 * E) return 0;
+    const int e = it < E ? it : it - E;
+    const bool host = sh.is_host[e] != 0;
+    return (sh.cnt[e] > 0 && (it < E ? host : !host)) ? 1 : 0;
+  };
+  const int f0 = flag(i0), f1 = flag(i1);
+  int n_act;
+  const int pos = block_exscan(f0 + f1, sh.scan_tmp, &n_act);
+  if (f0) {
+    const int e = i0 < E ? i0 : i0 - E;
+    a.active[pos] = e;
+    a.act_pos[e] = pos;
+    if (a.work) {
+      a.work[pos].w = a.wptr[e];
+      a.work[pos].p0 = sh.off[e];
+      a.work[pos].M = sh.cnt[e];
+    }
+  }
+  if (f1) {
+    const int e = i1 < E ? i1 : i1 - E;
+    a.active[pos + f0] = e;
+    a.act_pos[e] = pos + f0;
+    if (a.work) {
+      a.work[pos + f0].w = a.wptr[e];
+      a.work[pos + f0].p0 = sh.off[e];
+      a.work[pos + f0].M = sh.cnt[e];
+    }
+  }
+  if (a.work)  // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
+    for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
+  if (tid == 0) *a.n_active = n_act;
+  if (a.tiles) {  // prefill GEMM tiles of kGemmRows rows, expert by expert
+    const int ntile = (tid < E) ? (c + kGemmRows - 1) / kGemmRows : 0;
+    int n_all;
+    const int q0 = block_exscan(ntile, sh.scan_tmp, &n_all);
+    for (int i = 0; i < ntile; ++i) a.tiles[q0 + i] = make_int2(tid, i * kGemmRows);
+    if (tid == 0) *a.n_tiles = n_all;
+  }
+  if (tid < E && c > 0) {
+    const bool host = sh.is_host[tid] != 0;
+    atomicAdd(&sh.stat[host ? 1 : 0], c);
+    atomicAdd(&sh.stat[host ? 3 : 2], 1);
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.counts_acc + tid), (unsigned long long)c);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
+    atomicAdd(st + ST_FORWARDS, 1ull);
+    atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
+    atomicAdd(st + ST_HITS, (unsigned long long)sh.stat[0]);
+    atomicAdd(st + ST_MISSES, (unsigned long long)sh.stat[1]);
+    atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)sh.stat[2] * a.expert_bytes));
+    atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)sh.stat[3] * a.expert_bytes));
+  }
+}
+
+// One block per kGroupTokens tokens, one thread per assignment (ascending order).
+// A thread's rank among the block's earlier assignments to its expert: within its
+// wave from the ballot of equal ids, over earlier waves from their id-bit masks.
+__global__ __launch_bounds__(kGroupTokens * 32) void k_scatter(RouteArgs a) {
+  constexpr int kW = kGroupTokens * 32 / 64;
+  __shared__ uint64_t masks[kW][kIdBits + 1];  // per wave: id-bit ballots, then the valid mask
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int E = a.E, k = a.k;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const int base = blockIdx.x * kGroupTokens * k;
+  const int n_blk = min(kGroupTokens * k, a.T * k - base);
+  const int i = base + tid;
+  const bool valid = tid < n_blk;
+  const int e = valid ? a.ids[i] : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t m[kIdBits];
+#pragma unroll
+  for (int b = 0; b < kIdBits; ++b) m[b] = __ballot(valid && ((e >> b) & 1));
+  const uint64_t vm = __ballot(valid);
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) masks[wave][b] = m[b];
+    masks[wave][kIdBits] = vm;
+  }
+  __syncthreads();
+  uint64_t eq;
+  count_below(e, m, vm, nbits, &eq);
+  int rank = __popcll(eq & lt_mask);
+  for (int w = 0; w < wave; ++w) {
+    uint64_t q;
+    count_below(e, masks[w], masks[w][kIdBits], nbits, &q);
+    rank += __popcll(q);
+  }
+  if (valid) {
+    const int pos = a.hist[(size_t)blockIdx.x * E + e] + rank;
+    a.sorted[pos] = i;
+    a.inv[i] = pos;
+    if (a.work) {
+      const int j = pos - a.offsets[e];
+      if (j < kDescTok) a.work[a.act_pos[e]].tok[j] = i / k;
+    }
+  }
+}
+
+void launch_topk_group(const RouteArgs& a, unsigned* counter, const Timing& tm, hipStream_t s) {
   Timing t1 = tm, t2 = tm;
   t1.stop = nullptr;
   t2.start = nullptr;
-  launch_timed(k_topk, dim3((a.T + 15) / 16), dim3(1024), 0, s, t1, a);
-  launch_timed(k_align, dim3(1), dim3(1024), 0, s, t2, a);
+  const int nb = (a.T + kGroupTokens - 1) / kGroupTokens;
+  launch_timed(k_topk_count, dim3(nb), dim3(1024), 0, s, t1, a, counter);
+  const int threads = ((kGroupTokens * a.k + 63) / 64) * 64;
+  launch_timed(k_scatter, dim3(nb), dim3(threads), 0, s, t2, a);
 }
 
 // ----------------------------------------------------------------------------- combine

@@ -66,6 +66,8 @@ struct RouteArgs {
   const uint8_t* const* wptr;  // [E] expert blob table (for the work descriptors)
   WorkDesc* work;           // [E] one per active expert, in active-list order, or null
   const uint8_t** aptr;     // [T*k] blob of each assignment's expert (decode), or null
+  int32_t* hist;            // [ceil(T/16)][E] per-block counts, then bases (multi-block grouping)
+  int32_t* act_pos;         // [E] active-list position of each expert (multi-block grouping)
 };
 
 struct GemvArgs {
@@ -126,7 +128,9 @@ constexpr int kDownCombMinGroups = 128;   // ... if (H/64) * T workgroups reach 
 void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s);
 void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,
                          const Timing& tm, hipStream_t s);
-void launch_topk_align(const RouteArgs& a, const Timing& tm, hipStream_t s);
+// top-k and grouping over ceil(T/16) blocks (any T*k), counter: a zeroed device word
+void launch_topk_group(const RouteArgs& a, unsigned* counter, const Timing& tm, hipStream_t s);
+constexpr int kGroupTokens = 16;  // tokens per block of the multi-block grouping
 void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s);
