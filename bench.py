@@ -85,6 +85,31 @@ def make_layers(d, L, keep_blobs):
     return layers
 
 
+def measured_traffic(kernel, workload, plan, batch):
+    """DRAM-side bytes per launch of `kernel` from a committed counter summary
+    (profiles/*_traffic.md, a `traffic:` line), or None when there is none for this
+    workload or the kernel's sources have changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    csrc = os.path.join(ROOT, "expert_offloaded_ffn_moe_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        for line in open(f, encoding="utf-8"):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(t.split("=", 1) for t in line.split()[1:])
+            if (kv.get("kernel"), kv.get("workload"), kv.get("plan"), kv.get("batch")) != (
+                    kernel, workload, plan, str(batch)):
+                continue
+            h = hashlib.sha256()
+            for src in kv["sources"].split(","):
+                with open(os.path.join(csrc, src), "rb") as fh:
+                    h.update(fh.read())
+            if h.hexdigest()[:16] == kv["sha256_16"]:
+                return int(kv["bytes_per_launch"])
+    return None
+
+
 def roofline(per_kernel, bytes_hbm, bytes_host, assignments, H, I):
     """Roofline of the dominant expert kernel (largest total time over the profiled pass).
 
@@ -171,6 +196,7 @@ def run_one(args, d, layers, B, plan_kind, steps, warmup):
     bytes_hbm, bytes_host = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
     per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
     roof = roofline(per_kernel, bytes_hbm, bytes_host, B * k, H, I)
+    roof["traffic"] = measured_traffic(roof["kernel"], args.workload, plan_kind, B)
     name = {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
             "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload]
     return {
