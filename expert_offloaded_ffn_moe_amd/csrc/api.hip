@@ -420,7 +420,9 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.hist = w.hist;
   rt.act_pos = w.act_pos;
 
-  const bool decode = T <= kRouteSmallMaxTokens && A <= kRouteSmallMaxAssign;
+  // one-launch routing for small batches (its router walks the tokens one by one;
+  // past a few bf16 tokens the MFMA router and the multi-block grouping are faster)
+  const bool decode = T <= (bf16 ? kRouteDecodeMaxTokensBf16 : kRouteSmallMaxTokens) && A <= kRouteSmallMaxAssign;
   const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
   rt.work = prefill ? nullptr : w.work;
   // a few tokens: down projection and combine in one launch (K split over the free
@@ -431,8 +433,11 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.aptr = fuse_down ? w.aptr : nullptr;
   if (prefill) {
     {
+      RouterArgs rp = ra;  // logits only: the GEMMs take no group sums
+      rp.router_blocks = 1;
+      rp.xsum = nullptr;
       KernelTimer kt(p, MOE_K_ROUTER);
-      if (!logits_in) launch_router_mfma(ra, kt.tm, s);
+      if (!logits_in) launch_router_mfma(rp, kt.tm, s);
     }
     rt.tiles = w.tiles;
     rt.n_tiles = w.n_tiles;
@@ -495,10 +500,15 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     KernelTimer kt(p, MOE_K_ROUTE);
     launch_route_decode(rt, ra, bf16, w.route_cnt, kt.tm, s);
   } else {
-    ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
     {
       KernelTimer kt(p, MOE_K_ROUTER);
-      launch_router(ra, bf16, kt.tm, s);
+      if (bf16) {  // MFMA logits tiles (unless given) and the group sums, one launch
+        ra.router_blocks = logits_in ? 0 : 1;
+        launch_router_mfma(ra, kt.tm, s);
+      } else {
+        ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
+        launch_router(ra, bf16, kt.tm, s);
+      }
     }
     KernelTimer kt(p, MOE_K_ROUTE);
     launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);

@@ -81,18 +81,46 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
 // ----------------------------------------------------------------------------- router
 
 // logits[t][e] = sum_h x[t][h] * Wr[e][h] + b[e]: one workgroup per 32 x 32
 // output tile, its 8 waves splitting K (operands straight from global memory,
 // x and Wr rows are K-contiguous); the partial tiles are added in LDS in wave order.
+// When xsum is given, workgroups past the logits tiles (all of them when
+// tile_blocks is 0) write xsum[t][g] = sum of x[t][gG .. gG+G) for the GEMVs, in
+// element order.
 constexpr int kRouterWaves = 8;
 __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ w,
                                                                    const float* __restrict__ b,
-                                                                   float* __restrict__ logits, int T, int H, int E) {
+                                                                   float* __restrict__ logits, float* __restrict__ xsum,
+                                                                   int tile_blocks, int T, int H, int E, int G) {
   __shared__ float part[kRouterWaves][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= tile_blocks) {
+    const int ng = H / G;
+    const int gid = (blockIdx.x - tile_blocks) * (64 * kRouterWaves) + threadIdx.x;
+    if (gid >= T * ng) return;
+    const int t = gid / ng, g = gid % ng;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + (size_t)g * G);
+    float sum = 0.f;
+    for (int c = 0; c < G / 8; ++c) {
+      const uint4 v = src[c];
+      sum += bf16_lo(v.x);
+      sum += bf16_hi(v.x);
+      sum += bf16_lo(v.y);
+      sum += bf16_hi(v.y);
+      sum += bf16_lo(v.z);
+      sum += bf16_hi(v.z);
+      sum += bf16_lo(v.w);
+      sum += bf16_hi(v.w);
+    }
+    xsum[gid] = sum;
+    return;
+  }
   const int nte = (E + 31) / 32;
   const int mt = blockIdx.x / nte, et = blockIdx.x % nte;
   const int i = lane & 31, half = lane >> 5;
@@ -132,9 +160,11 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_
 }
 
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s) {
-  const int blocks = ((a.T + 31) / 32) * ((a.E + 31) / 32);
-  launch_timed(k_router_mfma, dim3(blocks), dim3(64 * kRouterWaves), 0, s, tm, static_cast<const uint16_t*>(a.x),
-               static_cast<const uint16_t*>(a.w), a.b, a.logits, a.T, a.H, a.E);
+  const int tiles = a.router_blocks > 0 ? ((a.T + 31) / 32) * ((a.E + 31) / 32) : 0;
+  const int xs = a.xsum ? (a.T * (a.H / a.G) + 64 * kRouterWaves - 1) / (64 * kRouterWaves) : 0;
+  if (tiles + xs == 0) return;
+  launch_timed(k_router_mfma, dim3(tiles + xs), dim3(64 * kRouterWaves), 0, s, tm, static_cast<const uint16_t*>(a.x),
+               static_cast<const uint16_t*>(a.w), a.b, a.logits, a.xsum, tiles, a.T, a.H, a.E, a.G);
 }
 
 // ----------------------------------------------------------------------------- grouped GEMM

@@ -33,7 +33,7 @@ struct RouterArgs {
   float* logits;         // [T][E]
   float* xsum;           // [T][H/G] sums of x over each group (bf16 path), or null
   int T, H, E, G;
-  int router_blocks;     // blocks computing logits (the rest compute xsum)
+  int router_blocks;     // blocks computing logits (the rest compute xsum); MFMA router: > 0 = logits wanted
 };
 
 // One GEMV work item: an active expert of the current forward, written by the
@@ -122,6 +122,7 @@ struct CombineArgs {
 
 constexpr int kRouteSmallMaxAssign = 256;   // T*k handled by launch_route_decode
 constexpr int kRouteSmallMaxTokens = 64;
+constexpr int kRouteDecodeMaxTokensBf16 = 4;  // bf16 batches routed by the one-launch decode routing
 constexpr int kDownCombMaxTokens = 4;     // decode batches whose down projection and combine fuse
 constexpr int kDownCombMinGroups = 128;   // ... if (H/64) * T workgroups reach this
 
