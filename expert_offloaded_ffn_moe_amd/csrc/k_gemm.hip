@@ -16,6 +16,8 @@
 // partial sum, so no rounded q * s ever enters the MFMA.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 #include "wave.h"
 
@@ -67,6 +69,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 32x32x2: lane l gives A[l % 32][l / 32] and B[l / 32][l % 32]; C/D in the
+// same lane layout as the bf16 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 // sum over each aligned group of N lanes (N <= 32), in every lane: DPP steps inside a
@@ -255,85 +263,119 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int o = 0; o < 2; ++o) acc[s][o] = f32x16{};
+  // the previous group's column factors and row sums (rows 32 s + lane % 32), kept
+  // in registers: its LDS buffer is rewritten by waves already on the next group
+  float fp0 = 0.f, fp1 = 0.f, rp[2] = {0.f, 0.f};
 
-  // group 0 in registers
-  uint4 av[CPG];
-  u32x4 bv[CPG];
-  uint16_t sc0b, sc1b;
+  // a group's operands in registers: this thread's staging pieces of the A rows,
+  // the wave's codes (CPG dwords x 4 per lane) and the two column scales
+  struct Regs {
+    uint4 a[CPG];
+    u32x4 b[CPG];
+    uint16_t s0, s1;
+  };
+  auto load = [&](Regs& r, int gl) {
 #pragma unroll
-  for (int q = 0; q < CPG; ++q) av[q] = src[q][0];
+    for (int q = 0; q < CPG; ++q) r.a[q] = src[q][(size_t)gl * PPR];
 #pragma unroll
-  for (int cc = 0; cc < CPG; ++cc) bv[cc] = codes[(size_t)cc * 64];
-  sc0b = scales[i32];
-  sc1b = scales[32 + i32];
+    for (int cc = 0; cc < CPG; ++cc) r.b[cc] = codes[(size_t)(gl * CPG + cc) * 64];
+    r.s0 = scales[(size_t)gl * 64 + i32];
+    r.s1 = scales[(size_t)gl * 64 + 32 + i32];
+  };
 
-  for (int g = 0; g < groups; ++g) {
-    const int buf = g & 1;
-    {  // A rows of group g -> LDS, with their sums (reduced over the PPR lanes of a row)
+  // Group g: its A rows (in `cur`) -> LDS buffer g & 1 with their row sums, group
+  // g + 1 (clamped to the last group) loaded into `nxt` while g runs on the MFMAs.
+  // The two register sets alternate between even and odd groups, so the loads
+  // in flight are only waited for where the next group first uses them.
+  auto step = [&](auto two_c, auto odd_c, int g, Regs& cur, Regs& nxt) {
+    constexpr bool TWO = decltype(two_c)::value;  // second 32-row block has rows
+    constexpr bool ODD = decltype(odd_c)::value;  // g is odd
+    constexpr int buf = ODD ? 1 : 0;
+    {
+      float rs[CPG];
 #pragma unroll
       for (int q = 0; q < CPG; ++q) {
         const int P = threadIdx.x + 256 * q;
-        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<G>::kStride + spiece * 16) = av[q];
-        const float rs = lane_group_sum<PPR>(piece_sum(av[q]));
-        if (spiece == 0) sh.rowsum[buf][P / PPR] = rs;
+        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<G>::kStride + spiece * 16) = cur.a[q];
+        rs[q] = piece_sum(cur.a[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < CPG; ++q) rs[q] = lane_group_sum<PPR>(rs[q]);
+      if (spiece == 0) {
+#pragma unroll
+        for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
       }
     }
-    // group g + 1 (clamped to the last group) into registers while g computes
-    const int gn = min(g + 1, groups - 1);
-    uint4 avn[CPG];
-    u32x4 bvn[CPG];
-#pragma unroll
-    for (int q = 0; q < CPG; ++q) avn[q] = src[q][(size_t)gn * PPR];
-#pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) bvn[cc] = codes[(size_t)(gn * CPG + cc) * 64];
-    const uint16_t sc0n = scales[(size_t)gn * 64 + i32], sc1n = scales[(size_t)gn * 64 + 32 + i32];
+    load(nxt, min(g + 1, groups - 1));
     __syncthreads();  // buffer `buf` complete; the other one is no longer read
-    if (active_wave) {
-      f32x16 ag[2][2];
+    if (!active_wave) return;
+    f32x16 ag[2][2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+    for (int cc = 0; cc < CPG; ++cc) {
+      // lanes 0-31 hold n-tile rows 0-31 (gate), lanes 32-63 rows 32-63 (up / second
+      // half), 32 K values each; the swaps give each half's K 0-15 and 16-31 operands
+      const auto s01 = __builtin_amdgcn_permlane32_swap(cur.b[cc].x, cur.b[cc].y, false, false);
+      const auto s23 = __builtin_amdgcn_permlane32_swap(cur.b[cc].z, cur.b[cc].w, false, false);
+      const bf16x8_t b00 = codes_to_bf16(s01[0], kc), b10 = codes_to_bf16(s01[1], kc);  // k-step 0: half 0, half 1
+      const bf16x8_t b01 = codes_to_bf16(s23[0], kc), b11 = codes_to_bf16(s23[1], kc);  // k-step 1
 #pragma unroll
-        for (int o = 0; o < 2; ++o) ag[s][o] = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < CPG; ++cc) {
-        // lanes 0-31 hold n-tile rows 0-31 (gate), lanes 32-63 rows 32-63 (up / second
-        // half), 32 K values each; the swaps give each half's K 0-15 and 16-31 operands
-        const auto s01 = __builtin_amdgcn_permlane32_swap(bv[cc].x, bv[cc].y, false, false);
-        const auto s23 = __builtin_amdgcn_permlane32_swap(bv[cc].z, bv[cc].w, false, false);
-        const bf16x8_t b00 = codes_to_bf16(s01[0], kc), b10 = codes_to_bf16(s01[1], kc);  // k-step 0: half 0, half 1
-        const bf16x8_t b01 = codes_to_bf16(s23[0], kc), b11 = codes_to_bf16(s23[1], kc);  // k-step 1
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (s == 1 && !two) break;
-          const uint8_t* arow = sh.a[buf] + (32 * s + i32) * GemmShared<G>::kStride + cc * 64 + half * 16;
-          const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow));
-          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32));
-          ag[s][0] = mfma(a0, b00, ag[s][0]);
-          ag[s][1] = mfma(a0, b10, ag[s][1]);
-          ag[s][0] = mfma(a1, b01, ag[s][0]);
-          ag[s][1] = mfma(a1, b11, ag[s][1]);
-        }
-      }
-      // acc += 16 * s * (sum x v - 1.5 * sum x), per output element
-      const float f0 = 16.f * half_bits(sc0b), f1 = 16.f * half_bits(sc1b);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s == 1 && !two) break;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float r15 = 1.5f * sh.rowsum[buf][32 * s + 8 * (v / 4) + 4 * half + (v % 4)];
-          acc[s][0][v] = fmaf(f0, ag[s][0][v] - r15, acc[s][0][v]);
-          acc[s][1][v] = fmaf(f1, ag[s][1][v] - r15, acc[s][1][v]);
-        }
+      for (int s = 0; s < (TWO ? 2 : 1); ++s) {
+        const uint8_t* arow = sh.a[buf] + (32 * s + i32) * GemmShared<G>::kStride + cc * 64 + half * 16;
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow));
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32));
+        ag[s][0] = mfma(a0, b00, cc == 0 ? f32x16{} : ag[s][0]);
+        ag[s][1] = mfma(a0, b10, cc == 0 ? f32x16{} : ag[s][1]);
+        ag[s][0] = mfma(a1, b01, ag[s][0]);
+        ag[s][1] = mfma(a1, b11, ag[s][1]);
       }
     }
+    // acc += 16 s * sum x v per output element; the -16 s * 1.5 * sum x part goes in
+    // below as a rank-2 fp32 MFMA per two groups (rows' sums x columns' factors)
+    const float f0 = 16.f * half_bits(cur.s0), f1 = 16.f * half_bits(cur.s1);
 #pragma unroll
-    for (int q = 0; q < CPG; ++q) av[q] = avn[q];
+    for (int s = 0; s < (TWO ? 2 : 1); ++s) {
 #pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) bv[cc] = bvn[cc];
-    sc0b = sc0n;
-    sc1b = sc1n;
-  }
+      for (int v = 0; v < 16; ++v) {
+        acc[s][0][v] = fmaf(f0, ag[s][0][v], acc[s][0][v]);
+        acc[s][1][v] = fmaf(f1, ag[s][1][v], acc[s][1][v]);
+      }
+    }
+    // groups (g - 1, g) when g is odd, or the last group alone: A = -1.5 * row sums
+    // (k = 0: group g - 1, k = 1: group g), B = the columns' 16 s of those groups
+    float rc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) rc[s] = sh.rowsum[buf][32 * s + i32];
+    if (ODD || g == groups - 1) {
+      const int kg = half;  // this lane's k: 0 -> previous group, 1 -> this one
+      const float fb0 = ODD ? (kg ? f0 : fp0) : (kg ? 0.f : f0);
+      const float fb1 = ODD ? (kg ? f1 : fp1) : (kg ? 0.f : f1);
+#pragma unroll
+      for (int s = 0; s < (TWO ? 2 : 1); ++s) {
+        const float ra = -1.5f * ((ODD && !kg) ? rp[s] : rc[s]);
+        acc[s][0] = mfma_f32(ra, fb0, acc[s][0]);
+        acc[s][1] = mfma_f32(ra, fb1, acc[s][1]);
+      }
+    }
+    if (!ODD) {
+      fp0 = f0;
+      fp1 = f1;
+      rp[0] = rc[0];
+      rp[1] = rc[1];
+    }
+  };
+
+  Regs r0, r1;
+  load(r0, 0);
+  auto run = [&](auto two_c) {
+    for (int g = 0; g < groups; g += 2) {
+      step(two_c, std::false_type{}, g, r0, r1);
+      if (g + 1 < groups) step(two_c, std::true_type{}, g + 1, r1, r0);
+    }
+  };
+  if (two)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
   if (!active_wave) return;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
