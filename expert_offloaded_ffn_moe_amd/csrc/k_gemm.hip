@@ -228,9 +228,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   __shared__ GemmShared<G> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ngroup_wg = (ntiles_n + kWaves - 1) / kWaves;
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  // the grid is sized for the most tiles a batch can have; the order is laid out
+  // over the tiles this batch has, so every XCD gets its share of the real work
+  const int nb = *n_tiles * ngroup_wg;
+  if ((int)blockIdx.x >= nb) return;
+  const int lb = xcd_logical_block(blockIdx.x, nb);
   const int tile_idx = lb / ngroup_wg;
-  if (tile_idx >= *n_tiles) return;
   const int nt = (lb % ngroup_wg) * kWaves + wave;
   const bool active_wave = nt < ntiles_n;
   const int2 tl = tiles[tile_idx];
