@@ -224,8 +224,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
                                                  const int32_t* __restrict__ sorted, const uint16_t* __restrict__ a_src,
                                                  void* __restrict__ out, int64_t off_codes, int64_t off_scales,
                                                  int chunks, int groups, int ntiles_n, int K, int out_ld, int k) {
-  constexpr int CPG = G / 32;
-  __shared__ GemmShared<G> sh;
+  // The loop runs over sub-groups of SG <= 128 K values (G = 256 takes two per
+  // quantisation group, sharing its scale), so that two register sets of a
+  // sub-group's operands fit beside the accumulators at two waves per SIMD.
+  constexpr int SG = G > 128 ? 128 : G, SPG = G / SG;
+  constexpr int CPG = SG / 32;
+  __shared__ GemmShared<SG> sh;
+  const int nsub = groups * SPG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ngroup_wg = (ntiles_n + kWaves - 1) / kWaves;
   // the grid is sized for the most tiles a batch can have; the order is laid out
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   // staging assignment: a group's A tile is 64 rows of PPR = G/8 16-byte pieces;
   // thread t stages pieces t + 256 q (q < CPG): row (t + 256 q) / PPR, piece t % PPR,
   // so PPR consecutive lanes cover one row's contiguous bytes (no LDS bank conflicts)
-  constexpr int PPR = G / 8;
+  constexpr int PPR = SG / 8;
   const int spiece = threadIdx.x % PPR;
   const uint4* src[CPG];
 #pragma unroll
@@ -282,8 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     for (int q = 0; q < CPG; ++q) r.a[q] = src[q][(size_t)gl * PPR];
 #pragma unroll
     for (int cc = 0; cc < CPG; ++cc) r.b[cc] = codes[(size_t)(gl * CPG + cc) * 64];
-    r.s0 = scales[(size_t)gl * 64 + i32];
-    r.s1 = scales[(size_t)gl * 64 + 32 + i32];
+    r.s0 = scales[(size_t)(gl / SPG) * 64 + i32];
+    r.s1 = scales[(size_t)(gl / SPG) * 64 + 32 + i32];
   };
 
   // Group g: its A rows (in `cur`) -> LDS buffer g & 1 with their row sums, group
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
 #pragma unroll
       for (int q = 0; q < CPG; ++q) {
         const int P = threadIdx.x + 256 * q;
-        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<G>::kStride + spiece * 16) = cur.a[q];
+        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<SG>::kStride + spiece * 16) = cur.a[q];
         rs[q] = piece_sum(cur.a[q]);
       }
 #pragma unroll
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
         for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
       }
     }
-    load(nxt, min(g + 1, groups - 1));
+    load(nxt, min(g + 1, nsub - 1));
     __syncthreads();  // buffer `buf` complete; the other one is no longer read
     if (!active_wave) return;
     f32x16 ag[2][2];
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
       const bf16x8_t b01 = codes_to_bf16(s23[0], kc), b11 = codes_to_bf16(s23[1], kc);  // k-step 1
 #pragma unroll
       for (int s = 0; s < (TWO ? 2 : 1); ++s) {
-        const uint8_t* arow = sh.a[buf] + (32 * s + i32) * GemmShared<G>::kStride + cc * 64 + half * 16;
+        const uint8_t* arow = sh.a[buf] + (32 * s + i32) * GemmShared<SG>::kStride + cc * 64 + half * 16;
         const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow));
         const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32));
         ag[s][0] = mfma(a0, b00, cc == 0 ? f32x16{} : ag[s][0]);
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     float rc[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) rc[s] = sh.rowsum[buf][32 * s + i32];
-    if (ODD || g == groups - 1) {
+    if (ODD || g == nsub - 1) {
       const int kg = half;  // this lane's k: 0 -> previous group, 1 -> this one
       const float fb0 = ODD ? (kg ? f0 : fp0) : (kg ? 0.f : f0);
       const float fb1 = ODD ? (kg ? f1 : fp1) : (kg ? 0.f : f1);
@@ -370,9 +375,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   Regs r0, r1;
   load(r0, 0);
   auto run = [&](auto two_c) {
-    for (int g = 0; g < groups; g += 2) {
+    for (int g = 0; g < nsub; g += 2) {
       step(two_c, std::false_type{}, g, r0, r1);
-      if (g + 1 < groups) step(two_c, std::true_type{}, g + 1, r1, r0);
+      if (g + 1 < nsub) step(two_c, std::true_type{}, g + 1, r1, r0);
     }
   };
   if (two)

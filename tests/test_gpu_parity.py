@@ -249,6 +249,8 @@ PREFILL = [
     (384, 96, 12, 3, 32, 300, 21),     # G = 32, 3 gate/up n-tiles (one idle wave per workgroup)
     (512, 256, 16, 4, 128, 600, 22),
     (2048, 768, 128, 8, 128, 1024, 4),  # Qwen3-30B-A3B-shaped prefill micro-batch
+    (1024, 512, 32, 4, 64, 700, 5),     # G = 64; the last tile of most experts has <= 32 rows
+    (2048, 1536, 64, 8, 256, 500, 7),   # G = 256: two 128-wide passes per quantisation group
 ]
 
 
@@ -264,6 +266,11 @@ def test_prefill_mfma_parity(moe, H, I, E, k, G, T, seed):
     y = run(plan, c, logits_in=lg, route=rb)
     check_routing_exact(c, ref, rb)
     check_y(y[toks], ref["y"], "prefill y (%d sampled tokens of %d)" % (len(toks), T))
+    # every token, a second run: the grouped GEMM has no order-dependent reductions,
+    # so y repeats bit for bit (NaN compares equal here, so a NaN fails the checks above)
+    y_again = run(plan, c, logits_in=lg, route=rb)
+    assert np.all(np.isfinite(y))
+    np.testing.assert_array_equal(y_again, y)
     # the MFMA router: logits within fp32 accumulation error, ids where unambiguous
     rb2 = route_bufs(c)
     y2 = run(plan, c, route=rb2)
