@@ -35,7 +35,8 @@ static void down_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hipSt
     case 1: return down_w<MT, 1>(a, W, grid, tm, s);
     case 2: return down_w<MT, 2>(a, W, grid, tm, s);
     case 4: return down_w<MT, 4>(a, W, grid, tm, s);
-    default: return down_w<MT, 8>(a, W, grid, tm, s);
+    // G = 256 with two tokens: the 4-token kernel (the two-token one spills)
+    default: return down_w<MT == 2 ? 4 : MT, 8>(a, W, grid, tm, s);
   }
 }
 

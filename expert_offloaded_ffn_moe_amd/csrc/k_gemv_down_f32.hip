@@ -14,7 +14,9 @@ static int waves_for(const GemvArgs& a, int mt) {
 // long (measured faster there), and the rows fit in 64 KiB; else scalar loads.
 static bool use_lds(size_t bytes, int mt, int K) { return bytes <= 65536 && (mt >= 2 || K >= 4096); }
 
-static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : max_tok <= 4 ? 4 : 8; }
+// No two-token variant for fp32 rows: it needs more than 256 VGPRs and spills, so
+// experts with 2 tokens take the 4-token kernel (rows past the count are skipped).
+static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 4 ? 4 : 8; }
 
 template <int MT, int CPG>
 static void down_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
@@ -42,7 +44,6 @@ static void down_mt(const GemvArgs& a, int max_tok, int grid, const Timing& tm, 
   const int W = waves_for(a, pick_mt(max_tok));
   switch (pick_mt(max_tok)) {
     case 1: return down_cpg<1>(a, W, grid, tm, s);
-    case 2: return down_cpg<2>(a, W, grid, tm, s);
     case 4: return down_cpg<4>(a, W, grid, tm, s);
     default: return down_cpg<8>(a, W, grid, tm, s);
   }

@@ -35,7 +35,8 @@ static void gateup_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hip
     case 1: return gateup_w<MT, 1>(a, W, grid, tm, s);
     case 2: return gateup_w<MT, 2>(a, W, grid, tm, s);
     case 4: return gateup_w<MT, 4>(a, W, grid, tm, s);
-    default: return gateup_w<MT, 8>(a, W, grid, tm, s);
+    // G = 256 with two tokens: the 4-token kernel (the two-token one spills)
+    default: return gateup_w<MT == 2 ? 4 : MT, 8>(a, W, grid, tm, s);
   }
 }
 

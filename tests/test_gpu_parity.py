@@ -101,6 +101,8 @@ SMALL = [
     (4096, 256, 24, 6, 128, "bf16", 2, 0.5, 18),  # fused down + combine: 64 tiles x 2 tokens, 12 waves
     (8192, 128, 16, 2, 64, "bf16", 1, 0.0, 19),   # fused at batch 1: 128 tiles, k * splits = 2 * 2
     (256, 128, 8, 2, 32, "f32", 150, 0.5, 20),    # T*k > 256: multi-block grouping, fp32 GEMVs, ragged last block
+    (2048, 256, 16, 4, 256, "bf16", 2, 0.5, 21),  # G = 256 with experts holding 2 tokens (4-token kernel)
+    (512, 256, 16, 4, 128, "f32", 2, 0.0, 22),    # fp32 rows, experts holding 2 tokens (4-token kernel)
 ]
 
 
