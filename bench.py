@@ -16,7 +16,7 @@ Workloads (--workload):
   prefill   the Qwen3 layer shape with 2048 (or --batch) tokens, bias-free routing.
   cache     expert-cache decode run: 48 stacked Qwen3-shaped layers (Zipf alpha 0.8,
             seeded per layer), HBM slots for 70% of each layer's experts, the rest read
-            from host memory; 256 single-token steps, a cache update after every step
+            from host memory; 256 single-token steps, a pipelined cache update after every step
             from a cold start (slots hold experts 0..89), beside the static coldest-on-host
             plan without updates. value = full-stack tokens/s.
 
@@ -279,7 +279,7 @@ def main():
 def run_cache(args, d, layers):
     """Expert-cache decode run over the stacked layers: the static plan first (warm-up
     steps, then the timed steps, no updates), then the cached plan from its cold start
-    with a cache update after every step. One step = one token batch through every layer;
+    with a pipelined cache update after every step. One step = one token batch through every layer;
     each (step, layer) takes its own seeded activations."""
     import numpy as np
     import torch
@@ -318,7 +318,7 @@ def run_cache(args, d, layers):
             for l in range(L):
                 plan.forward(l, xs[i * L + l], y)
             if mode == "cache":
-                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions)  # waits for the step first
+                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions, overlap=True)  # pipelined
             else:
                 torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
@@ -334,7 +334,7 @@ def run_cache(args, d, layers):
             for l in range(L):
                 plan.forward(l, xs[i * L + l], y)
             if mode == "cache":
-                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions)
+                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions, overlap=True)
         kt = plan.kernel_times()
         plan.profile(False)
         plan.destroy()
@@ -369,7 +369,7 @@ def run_cache(args, d, layers):
         "data": "synthetic",
         "config": {"workload": "expert-cache decode run: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d "
                                "int4 G%d, %d HBM slots per layer (rest host-mapped), batch %d, %d steps, cold start, "
-                               "cache update after every step (max %d promotions per layer)" % (
+                               "pipelined cache update after every step (max %d promotions per layer)" % (
                                    L, H, I, E, k, G, S, B, steps, args.max_promotions),
                    "alpha": alpha, "seed": seed},
         "roofline": c["roofline"],

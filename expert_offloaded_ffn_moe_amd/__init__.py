@@ -45,7 +45,7 @@ class Stats(ctypes.Structure):
 
 
 class CachePolicy(ctypes.Structure):
-    _fields_ = [("decay", ctypes.c_double), ("max_promotions", ctypes.c_int32)]
+    _fields_ = [("decay", ctypes.c_double), ("max_promotions", ctypes.c_int32), ("overlap", ctypes.c_int32)]
 
 
 KERNELS = ["router", "route", "gateup", "down", "combine", "gemm_gateup", "gemm_down"]
@@ -174,8 +174,10 @@ class Plan:
                "moe_layer_forward")
         return y
 
-    def cache_update(self, layer=-1, decay=0.9, max_promotions=8, stream=None):
-        pol = CachePolicy(decay, max_promotions)
+    def cache_update(self, layer=-1, decay=0.9, max_promotions=8, overlap=False, stream=None):
+        """overlap=True: the pipelined update (decisions lag one update; copies on the
+        plan's copy stream, promoted experts switched to HBM by the next update)."""
+        pol = CachePolicy(decay, max_promotions, 1 if overlap else 0)
         _check(self.lib.moe_cache_update(self.handle, layer, ctypes.byref(pol), _stream(stream)),
                "moe_cache_update")
 

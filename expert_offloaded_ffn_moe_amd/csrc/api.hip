@@ -52,8 +52,9 @@ struct Layer {
   uint64_t* h_wptr_stage = nullptr;  // pinned [E] staging of the pointer table
   int32_t* h_ishost_stage = nullptr; // pinned [E]
   int64_t* h_counts_stage = nullptr; // pinned [E]
-  std::vector<int32_t> slot_of;      // host mirror
+  std::vector<int32_t> slot_of;      // host mirror (a pending promotion already holds its slot)
   std::vector<double> score;
+  std::vector<Promotion> pending;    // pipelined update: copies in flight, table still reads host
   bool loaded = false;
   int64_t bytes_copied = 0, promotions = 0, evictions = 0;
 };
@@ -99,6 +100,21 @@ struct moe_plan {
   std::vector<hipEvent_t> spare;   // reusable events
   std::vector<void*> dev_allocs;   // freed with hipFree
   std::vector<void*> host_allocs;  // freed with hipHostFree
+  // Per-layer counters and pointer tables live in [layers][E] arrays, so that a
+  // pipelined cache update moves all layers' counts and tables with one copy each.
+  int64_t* d_counts_all = nullptr;
+  const uint8_t** d_wptr_all = nullptr;
+  int32_t* d_ishost_all = nullptr;
+  // pipelined cache updates: pinned staging used by alternate updates, a copy
+  // stream for the promotions, and the events that order them
+  int64_t* h_counts_all[2] = {nullptr, nullptr};
+  uint64_t* h_wptr_all[2] = {nullptr, nullptr};
+  int32_t* h_ishost_all[2] = {nullptr, nullptr};
+  std::vector<char> counts_staged[2];  // per layer: that staging set holds counts not yet used
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_counts[2] = {nullptr, nullptr}, ev_table[2] = {nullptr, nullptr}, ev_copy = nullptr;
+  bool counts_recorded[2] = {false, false}, table_recorded[2] = {false, false}, copy_pending = false;
+  unsigned update_seq = 0;
 };
 
 namespace {
@@ -139,6 +155,9 @@ void free_plan(moe_plan* p) {
     (void)hipEventDestroy(r.b);
   }
   for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {p->ev_counts[0], p->ev_counts[1], p->ev_table[0], p->ev_table[1], p->ev_copy})
+    if (e) (void)hipEventDestroy(e);
+  if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
   for (void* q : p->dev_allocs) (void)hipFree(q);
   for (void* q : p->host_allocs) (void)hipHostFree(q);
   delete p;
@@ -193,6 +212,97 @@ moe_status push_tables(moe_plan* p, Layer& ly, hipStream_t s) {
   }
   HIP_TRY(hipMemcpyAsync(ly.d_wptr, ly.h_wptr_stage, sizeof(uint64_t) * E, hipMemcpyHostToDevice, s));
   HIP_TRY(hipMemcpyAsync(ly.d_is_host, ly.h_ishost_stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, s));
+  return MOE_OK;
+}
+
+// Wait for the promotion copies of a pipelined update and drop what it staged
+// for layers [l0, l1): afterwards slot_of is exactly what push_tables uploads.
+moe_status settle_pipelined(moe_plan* p, int l0, int l1) {
+  if (p->copy_pending) {
+    HIP_TRY(hipStreamSynchronize(p->copy_stream));
+    p->copy_pending = false;
+  }
+  for (int l = l0; l < l1; ++l) p->layers[l].pending.clear();
+  return MOE_OK;
+}
+
+// Pipelined cache update of layers [l0, l1) (see moe_cache_update): the policy
+// reads the counts the previous update staged, so the host never waits for the
+// step just enqueued; promotions are copied on the plan's copy stream and become
+// visible at the next update.
+moe_status cache_update_pipelined(moe_plan* p, int l0, int l1, double decay, int maxp, hipStream_t s) {
+  const int E = p->cfg.num_experts, S = p->cfg.hbm_slots;
+  const int cur = (int)(p->update_seq & 1u), prev = cur ^ 1;
+  ++p->update_seq;
+  const size_t off = (size_t)l0 * E, n = (size_t)(l1 - l0) * E;
+  // (a) the previous update's promotions: forwards after this table upload read
+  // them from HBM, so the upload waits for their copies (a device-side wait)
+  if (p->copy_pending) {
+    HIP_TRY(hipStreamWaitEvent(s, p->ev_copy, 0));
+    p->copy_pending = false;
+  }
+  // (b) the counts of the forwards enqueued since the last update, for the next update
+  if (p->counts_recorded[cur]) HIP_TRY(hipEventSynchronize(p->ev_counts[cur]));
+  HIP_TRY(hipMemcpyAsync(p->h_counts_all[cur] + off, p->d_counts_all + off, sizeof(int64_t) * n,
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemsetAsync(p->d_counts_all + off, 0, sizeof(int64_t) * n, s));
+  HIP_TRY(hipEventRecord(p->ev_counts[cur], s));
+  p->counts_recorded[cur] = true;
+  // (c) the policy on the counts staged by the previous update (complete by now:
+  // a whole step has been enqueued since)
+  if (p->counts_recorded[prev]) HIP_TRY(hipEventSynchronize(p->ev_counts[prev]));
+  if (p->table_recorded[cur]) HIP_TRY(hipEventSynchronize(p->ev_table[cur]));  // staging set free again
+  std::vector<Promotion> promoted;
+  std::vector<int32_t> evicted;
+  bool copies = false;
+  for (int l = l0; l < l1; ++l) {
+    Layer& ly = p->layers[l];
+    ly.pending.clear();
+    if (p->counts_staged[prev][l]) {
+      cache_policy_step(E, S, decay, maxp, p->h_counts_all[prev] + (size_t)l * E, ly.score.data(),
+                        ly.slot_of.data(), &promoted, &evicted);
+      ly.pending = promoted;
+      ly.promotions += (int64_t)promoted.size();
+      ly.evictions += (int64_t)evicted.size();
+      ly.bytes_copied += (int64_t)promoted.size() * p->L.canonical_bytes;
+      copies |= !promoted.empty();
+    }
+    p->counts_staged[prev][l] = 0;
+    p->counts_staged[cur][l] = 1;
+    // (d) the table: resident experts read HBM, except the promotions whose
+    // copies are only being enqueued now
+    uint64_t* wp = p->h_wptr_all[cur] + (size_t)l * E;
+    int32_t* ih = p->h_ishost_all[cur] + (size_t)l * E;
+    for (int e = 0; e < E; ++e) {
+      const int slot = ly.slot_of[e];
+      const uint8_t* ptr = slot >= 0 ? ly.hbm + (size_t)slot * p->L.bytes : ly.host_pool_dev + (size_t)e * p->L.bytes;
+      wp[e] = reinterpret_cast<uint64_t>(ptr);
+      ih[e] = slot >= 0 ? 0 : 1;
+    }
+    for (const Promotion& pr : ly.pending) {
+      wp[pr.expert] = reinterpret_cast<uint64_t>(ly.host_pool_dev + (size_t)pr.expert * p->L.bytes);
+      ih[pr.expert] = 1;
+    }
+  }
+  HIP_TRY(hipMemcpyAsync(p->d_wptr_all + off, p->h_wptr_all[cur] + off, sizeof(uint64_t) * n,
+                         hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(p->d_ishost_all + off, p->h_ishost_all[cur] + off, sizeof(int32_t) * n,
+                         hipMemcpyHostToDevice, s));
+  HIP_TRY(hipEventRecord(p->ev_table[cur], s));
+  p->table_recorded[cur] = true;
+  // (e) the copies: after the upload above, no forward enqueued later reads the
+  // evicted experts' slots, and the ones enqueued before it have finished
+  if (copies) {
+    HIP_TRY(hipStreamWaitEvent(p->copy_stream, p->ev_table[cur], 0));
+    for (int l = l0; l < l1; ++l) {
+      Layer& ly = p->layers[l];
+      for (const Promotion& pr : ly.pending)
+        HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)pr.slot * p->L.bytes, ly.host_pool + (size_t)pr.expert * p->L.bytes,
+                               p->L.bytes, hipMemcpyHostToDevice, p->copy_stream));
+    }
+    HIP_TRY(hipEventRecord(p->ev_copy, p->copy_stream));
+    p->copy_pending = true;
+  }
   return MOE_OK;
 }
 
@@ -252,7 +362,34 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
     }                   \
   } while (0)
   p->layers.resize(cfg->num_layers);
-  for (auto& ly : p->layers) {
+  const size_t LE = (size_t)cfg->num_layers * E;
+  TRY(alloc_as(p, &p->d_counts_all, LE));
+  {
+    void* v;
+    TRY(dev_alloc(p, &v, sizeof(uint64_t) * LE));
+    p->d_wptr_all = static_cast<const uint8_t**>(v);
+    for (int b = 0; b < 2; ++b) {
+      TRY(host_alloc(p, &v, sizeof(int64_t) * LE, 0));
+      p->h_counts_all[b] = static_cast<int64_t*>(v);
+      TRY(host_alloc(p, &v, sizeof(uint64_t) * LE, 0));
+      p->h_wptr_all[b] = static_cast<uint64_t*>(v);
+      TRY(host_alloc(p, &v, sizeof(int32_t) * LE, 0));
+      p->h_ishost_all[b] = static_cast<int32_t*>(v);
+      p->counts_staged[b].assign(cfg->num_layers, 0);
+    }
+  }
+  TRY(alloc_as(p, &p->d_ishost_all, LE));
+  if (hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+    free_plan(p);
+    return fail(MOE_E_HIP, "creating the copy stream failed");
+  }
+  for (hipEvent_t* e : {&p->ev_counts[0], &p->ev_counts[1], &p->ev_table[0], &p->ev_table[1], &p->ev_copy})
+    if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
+      free_plan(p);
+      return fail(MOE_E_HIP, "creating cache-update events failed");
+    }
+  for (size_t li = 0; li < p->layers.size(); ++li) {
+    Layer& ly = p->layers[li];
     void* v;
     TRY(host_alloc(p, &v, (size_t)E * p->L.bytes, hipHostMallocMapped | hipHostMallocNonCoherent));
     ly.host_pool = static_cast<uint8_t*>(v);
@@ -266,12 +403,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
       TRY(dev_alloc(p, &v, (size_t)cfg->hbm_slots * p->L.bytes));
       ly.hbm = static_cast<uint8_t*>(v);
     }
-    TRY(dev_alloc(p, &v, sizeof(uint64_t) * E));
-    ly.d_wptr = static_cast<const uint8_t**>(v);
-    TRY(alloc_as(p, &ly.d_is_host, E));
+    ly.d_wptr = p->d_wptr_all + li * E;
+    ly.d_is_host = p->d_ishost_all + li * E;
     TRY(dev_alloc(p, &ly.d_router_w, (size_t)E * H * p->act_size));
     TRY(alloc_as(p, &ly.d_router_b, E));
-    TRY(alloc_as(p, &ly.d_counts_acc, E));
+    ly.d_counts_acc = p->d_counts_all + li * E;
     TRY(alloc_as(p, &ly.d_stats, ST_COUNT));
     TRY(host_alloc(p, &v, sizeof(uint64_t) * E, 0));
     ly.h_wptr_stage = static_cast<uint64_t*>(v);
@@ -335,6 +471,11 @@ moe_status moe_plan_load_layer(moe_plan* p, int32_t layer, const moe_layer_weigh
   }
   HIP_TRY(hipSetDevice(p->device));
   HIP_TRY(hipStreamSynchronize(s));  // no queued work may still read this layer
+  {
+    moe_status st = settle_pipelined(p, layer, layer + 1);  // nor copy into it
+    if (st != MOE_OK) return st;
+    p->counts_staged[0][layer] = p->counts_staged[1][layer] = 0;
+  }
 
   // repack every expert into the host pool, threads over experts
   const Layout L = p->L;
@@ -613,19 +754,39 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
   const int E = p->cfg.num_experts;
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(p->device));
+  if (pol && pol->overlap) return cache_update_pipelined(p, l0, l1, decay, maxp, s);
   for (int l = l0; l < l1; ++l) {
     Layer& ly = p->layers[l];
     HIP_TRY(hipMemcpyAsync(ly.h_counts_stage, ly.d_counts_acc, sizeof(int64_t) * E, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
   }
   HIP_TRY(hipStreamSynchronize(s));
+  std::vector<char> settled(p->cfg.num_layers, 0);  // layers whose pipelined promotions become visible now
+  for (int l = l0; l < l1; ++l) settled[l] = !p->layers[l].pending.empty();
+  {  // after pipelined updates: their copies done, their staged counts not lost
+    moe_status st = settle_pipelined(p, l0, l1);
+    if (st != MOE_OK) return st;
+    for (int b = 0; b < 2; ++b)
+      for (int l = l0; l < l1; ++l) {
+        if (!p->counts_staged[b][l]) continue;
+        HIP_TRY(hipEventSynchronize(p->ev_counts[b]));
+        for (int e = 0; e < E; ++e) p->layers[l].h_counts_stage[e] += p->h_counts_all[b][(size_t)l * E + e];
+        p->counts_staged[b][l] = 0;
+      }
+  }
   std::vector<Promotion> promoted;
   std::vector<int32_t> evicted;
   for (int l = l0; l < l1; ++l) {
     Layer& ly = p->layers[l];
     cache_policy_step(E, p->cfg.hbm_slots, decay, maxp, ly.h_counts_stage, ly.score.data(), ly.slot_of.data(),
                       &promoted, &evicted);
-    if (promoted.empty()) continue;
+    if (promoted.empty()) {
+      if (settled[l]) {
+        moe_status st = push_tables(p, ly, s);
+        if (st != MOE_OK) return st;
+      }
+      continue;
+    }
     for (const Promotion& pr : promoted) {
       HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)pr.slot * p->L.bytes, ly.host_pool + (size_t)pr.expert * p->L.bytes,
                              p->L.bytes, hipMemcpyHostToDevice, s));
@@ -678,8 +839,9 @@ moe_status moe_plan_reset_stats(moe_plan* p) {
 moe_status moe_plan_residency(moe_plan* p, int32_t layer, int32_t* slot_of) {
   if (!p || !slot_of) return fail(MOE_E_INVALID, "null argument");
   if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
-  const auto& v = p->layers[layer].slot_of;
-  std::copy(v.begin(), v.end(), slot_of);
+  const Layer& ly = p->layers[layer];
+  std::copy(ly.slot_of.begin(), ly.slot_of.end(), slot_of);
+  for (const Promotion& pr : ly.pending) slot_of[pr.expert] = -1;  // copy in flight: still read from host
   return MOE_OK;
 }
 

@@ -120,6 +120,7 @@ typedef struct {
 typedef struct {
   double decay;           /* score_e <- decay * score_e + count_e; default 0.9 */
   int32_t max_promotions; /* per layer per update; default 8 */
+  int32_t overlap;        /* 0: synchronous update; 1: pipelined update (see moe_cache_update) */
 } moe_cache_policy;
 
 /* Kernel classes timed by the profiling hooks. */
@@ -176,8 +177,20 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
  * switch is enqueued after the copies on `stream`, so forwards enqueued later
  * on the same stream see it and earlier ones finish on the old table; other
  * streams must order themselves with events. Synchronises `stream` first to
- * read the counts. policy NULL = defaults. Errors: MOE_E_INVALID, MOE_E_STATE
- * (hbm_slots == 0), MOE_E_HIP. */
+ * read the counts. policy NULL = defaults.
+ * Pipelined form (policy->overlap = 1), for decode loops that update after every
+ * step: the host does not wait for the step just enqueued. The counts of the
+ * forwards since the last update are staged (one copy for all the layers) and
+ * used by the next update; this update's policy uses the counts the previous
+ * update staged, so decisions lag one update behind. The new pointer tables
+ * (evictions now, promotions not yet) are uploaded on `stream` with one copy;
+ * the promotion copies then run on a copy stream of the plan, after that upload,
+ * overlapping the forwards enqueued next, and the promoted experts are switched
+ * to HBM by the next update's table upload, which waits for the copies on the
+ * device. moe_plan_residency reports the table the kernels read (a promotion in
+ * flight reads as -1). A synchronous update after pipelined ones first waits for
+ * their copies and adds the counts they staged.
+ * Errors: MOE_E_INVALID, MOE_E_STATE (hbm_slots == 0), MOE_E_HIP. */
 moe_status moe_cache_update(moe_plan* plan, int32_t layer, const moe_cache_policy* policy,
                             moe_stream stream);
 

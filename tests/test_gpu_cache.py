@@ -32,8 +32,12 @@ def _say(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_chained_cache_run(moe, T):
+@pytest.mark.parametrize("T,overlap", [(1, False), (3, False), (1, True), (3, True)])
+def test_chained_cache_run(moe, T, overlap):
+    """overlap: the pipelined update. Its policy reads the counts of the step before
+    the one just run, and the experts it promotes are still read from host memory
+    until the next update (their copies run meanwhile). A final synchronous update
+    then adds the last staged counts and makes every promotion visible."""
     import synth
 
     H, I, E, k, G, L, steps, seed = 512, 256, 32, 4, 128, 4, 10, 31
@@ -50,7 +54,9 @@ def test_chained_cache_run(moe, T):
 
     cached, full = plan_with(S), plan_with(E)
     slot_ref = [np.where(np.arange(E) < S, np.arange(E), -1) for _ in range(L)]
+    table_ref = [v.copy() for v in slot_ref]  # what the kernels read
     score_ref = [np.zeros(E) for _ in range(L)]
+    prev_counts, n_prom = None, 0
     for l in range(L):
         assert np.array_equal(cached.residency(l), slot_ref[l])
     acc = dict(hits=0, misses=0, bytes_hbm=0, bytes_host=0)
@@ -71,7 +77,7 @@ def test_chained_cache_run(moe, T):
             assert torch.equal(y, yf), "step %d layer %d: y differs between the cached and all-HBM plans" % (step, l)
             ids = rb["topk_ids"].cpu().numpy().reshape(T, k)
             counts[l] += np.bincount(ids.ravel(), minlength=E)
-            a = O.link_accounting(ids, slot_ref[l] >= 0, eb)
+            a = O.link_accounting(ids, table_ref[l] >= 0, eb)
             for n in acc:
                 acc[n] += a[n]
             if (step * L + l) % 7 == 0:  # oracle on the exact bf16 input and the GPU logits
@@ -86,16 +92,33 @@ def test_chained_cache_run(moe, T):
                 assert LC.max_abs(yv, ref["y"]) <= LC.MAX_ABS_BAR
                 checked += 1
             r = r + y
+        cached.cache_update(-1, decay=0.9, max_promotions=3, overlap=overlap)
+        policy_counts = (prev_counts if overlap else counts)
+        for l in range(L):
+            promoted = []
+            if policy_counts is not None:
+                score_ref[l], slot_ref[l], promoted, _ = O.cache_policy_step(score_ref[l], policy_counts[l],
+                                                                            slot_ref[l], S, 0.9, 3)
+            n_prom += len(promoted)
+            table_ref[l] = slot_ref[l].copy()
+            if overlap:
+                for e, _ in promoted:
+                    table_ref[l][e] = -1
+            assert np.array_equal(cached.residency(l), table_ref[l]), "step %d layer %d: slot table" % (step, l)
+        prev_counts = counts
+    if overlap:  # synchronous update: the counts the last pipelined update staged, then all visible
         cached.cache_update(-1, decay=0.9, max_promotions=3)
         for l in range(L):
-            score_ref[l], slot_ref[l], _, _ = O.cache_policy_step(score_ref[l], counts[l], slot_ref[l], S, 0.9, 3)
-            assert np.array_equal(cached.residency(l), slot_ref[l]), "step %d layer %d: slot table" % (step, l)
+            score_ref[l], slot_ref[l], promoted, _ = O.cache_policy_step(score_ref[l], prev_counts[l], slot_ref[l],
+                                                                        S, 0.9, 3)
+            n_prom += len(promoted)
+            assert np.array_equal(cached.residency(l), slot_ref[l]), "final sync update, layer %d" % l
     st = cached.stats(-1)
     _say("  hits %d misses %d promotions %d evictions %d (oracle checks %d)" % (
         st["hits"], st["misses"], st["promotions"], st["evictions"], checked))
     for n in acc:
         assert st[n] == acc[n], n
     assert st["forwards"] == steps * L and st["tokens"] == steps * L * T
-    assert st["promotions"] > 0 and st["bytes_copied"] == st["promotions"] * eb
+    assert st["promotions"] == n_prom > 0 and st["bytes_copied"] == st["promotions"] * eb
     cached.destroy()
     full.destroy()
