@@ -343,7 +343,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
 
   moe_plan* p = new moe_plan();
   p->cfg = *cfg;
-  if (p->cfg.gemm_min_tokens == 0) p->cfg.gemm_min_tokens = 256;
+  if (p->cfg.gemm_min_tokens == 0) p->cfg.gemm_min_tokens = kGemmMinTokensDefault;
   p->L = make_layout(cfg->hidden, cfg->inter, cfg->group_size);
   p->act_size = cfg->act_dtype == MOE_ACT_BF16 ? 2 : 4;
   if (hipGetDevice(&p->device) != hipSuccess) {

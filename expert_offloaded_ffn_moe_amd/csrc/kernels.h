@@ -140,6 +140,11 @@ void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);
 constexpr int kGemmRows = 64;  // token rows per prefill GEMM tile
+// Default of moe_config.gemm_min_tokens. From batches of about 6 tokens on, the
+// experts that several tokens share make the GEMVs' per-token dot products cost
+// more than the grouped MFMA GEMM's padded 64-row tiles (measured on H2048/E128
+// and H7168/E384 layers: equal at 5-6 tokens, the GEMM 13% ahead at 8, 2x at 32).
+constexpr int kGemmMinTokensDefault = 6;
 
 
 }  // namespace moe

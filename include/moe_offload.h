@@ -84,7 +84,10 @@ typedef struct {
   int32_t max_tokens;      /* largest T of any forward; sizes the workspace */
   int32_t hbm_slots;       /* HBM expert slots per layer, 0..E */
   int32_t gemm_min_tokens; /* forwards with T >= this use the grouped MFMA GEMM path
-                              (bf16 only); 0 = library default, < 0 = never */
+                              (bf16 only; never for T <= 4, which take the one-launch
+                              decode routing and the GEMVs); 0 = library default (6:
+                              from about 6 tokens, experts shared by several tokens
+                              make the GEMM faster than the GEMVs), < 0 = never */
 } moe_config;
 
 typedef struct {

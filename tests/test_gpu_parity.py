@@ -106,13 +106,18 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("H,I,E,k,G,act,T,alpha,seed", SMALL)
-def test_layer_parity_oracle_logits(moe, H, I, E, k, G, act, T, alpha, seed):
-    _say("case", H, I, E, k, G, act, T, alpha, seed)
+# bf16 cases of at least 6 tokens take the grouped MFMA GEMM by default; these run
+# them again with the GEMM switched off, through the GEMVs
+SMALL_GEMV = [(c + ("gemv",)) for c in SMALL if c[5] == "bf16" and c[6] >= 6]
+
+
+@pytest.mark.parametrize("H,I,E,k,G,act,T,alpha,seed,path", [c + ("default",) for c in SMALL] + SMALL_GEMV)
+def test_layer_parity_oracle_logits(moe, H, I, E, k, G, act, T, alpha, seed, path):
+    _say("case", H, I, E, k, G, act, T, alpha, seed, path)
     c = LC.make_case(H, I, E, k, G, act, T, seed, alpha)
     lg = LC.oracle_logits(c)
     ref = LC.oracle_forward(c, logits_in=lg)
-    plan = make_plan(moe, c)
+    plan = make_plan(moe, c, gemm_min_tokens=-1 if path == "gemv" else 0)
     rb = route_bufs(c)
     y = run(plan, c, logits_in=lg, route=rb)
     check_routing_exact(c, ref, rb)
@@ -145,12 +150,14 @@ def test_layer_parity_gpu_router(moe, H, I, E, k, G, act, T, alpha, seed):
     plan.destroy()
 
 
-def test_all_tokens_one_expert_multi_pass(moe):
-    """Every token routed to the same k experts: one expert gets T > 8 tokens (several passes)."""
+@pytest.mark.parametrize("gemm_min", [-1, 0])
+def test_all_tokens_one_expert_multi_pass(moe, gemm_min):
+    """Every token routed to the same k experts: one expert gets T > 8 tokens (several
+    GEMV passes with gemm_min -1; one GEMM tile of 21 rows per expert with the default)."""
     c = LC.make_case(384, 96, 12, 3, 32, "bf16", 21, 21)
     lg = np.tile(np.array([0.0] * 9 + [3.0, 2.0, 1.0], np.float32), (c.T, 1))
     ref = LC.oracle_forward(c, logits_in=lg)
-    plan = make_plan(moe, c)
+    plan = make_plan(moe, c, gemm_min_tokens=gemm_min)
     rb = route_bufs(c)
     y = run(plan, c, logits_in=lg, route=rb)
     check_routing_exact(c, ref, rb)
@@ -229,16 +236,17 @@ def test_token_order_invariance_bitwise(moe):
     plan.destroy()
 
 
-@pytest.mark.parametrize("T", [40, 2048])
-def test_large_batch_routing_and_sampled_outputs(moe, T):
-    """T*k > 256: multi-block top-k and the block grouping path. Routing is compared
-    bit-exactly for every token; y on a seeded sample of tokens (the whole batch for T=40)."""
+@pytest.mark.parametrize("T,gemm_min", [(40, -1), (40, 0), (16, 0), (2048, 0)])
+def test_large_batch_routing_and_sampled_outputs(moe, T, gemm_min):
+    """T*k > 64: multi-block top-k and the block grouping path. Routing is compared
+    bit-exactly for every token; y on a seeded sample of tokens (the whole batch for
+    T <= 64). gemm_min -1: the GEMVs; 0: the default dispatch (the MFMA GEMM here)."""
     c = LC.make_case(2048, 768, 128, 8, 128, "bf16", T, 4)
     lg = LC.oracle_logits(c)
     rng = np.random.default_rng(T)
     toks = np.arange(T) if T <= 64 else np.sort(rng.choice(T, 48, replace=False))
     ref = LC.oracle_forward(c, logits_in=lg, tokens=toks)
-    plan = make_plan(moe, c)
+    plan = make_plan(moe, c, gemm_min_tokens=gemm_min)
     rb = route_bufs(c)
     y = run(plan, c, logits_in=lg, route=rb)
     check_routing_exact(c, ref, rb)
