@@ -570,8 +570,17 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   // waves), when its (H/64) x T workgroups still keep the CUs streaming; below that
   // the per-expert down GEMV spreads the same bytes over more workgroups
   const int down_splits = std::max(1, std::min(16 / k, (int)p->L.dn_groups));
-  const bool fuse_down = bf16 && decode && T <= kDownCombMaxTokens && k <= 16 && (H / 64) * T >= kDownCombMinGroups;
-  rt.aptr = fuse_down ? w.aptr : nullptr;
+  const bool fuse_small = bf16 && decode && T <= kDownCombMaxTokens && k <= 16;
+  const bool fuse_down = fuse_small && (H / 64) * T >= kDownCombMinGroups;
+  // fewer 64-row tiles than that: the same fusion on 16-row tiles of H, with the
+  // K chunks of each wave spread over its four 16-lane quarters
+  // (the token's k rows of h staged in LDS); K split over as many waves per slot
+  // as still keep every workgroup resident in one round
+  const bool fuse_narrow = fuse_small && !fuse_down && down_combine16_lds(k, I) <= kDownComb16MaxLds;
+  int narrow_splits = std::max(1, std::min(16 / k, (int)p->L.dn_chunks / 4));
+  while (narrow_splits > 1 && (int64_t)(H / 16) * T > 256LL * (kDownComb16WavesPerCU / (k * narrow_splits)))
+    --narrow_splits;
+  rt.aptr = (fuse_down || fuse_narrow) ? w.aptr : nullptr;
   if (prefill) {
     {
       RouterArgs rp = ra;  // logits only: the GEMMs take no group sums
@@ -689,7 +698,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     da.chunks = (int)p->L.dn_chunks;
     da.groups = (int)p->L.dn_groups;
     da.tiles = (int)p->L.dn_tiles;
-    if (fuse_down) {
+    if (fuse_down || fuse_narrow) {
       DownCombArgs dc{};
       dc.aptr = w.aptr;
       dc.inv = w.inv;
@@ -706,9 +715,12 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       dc.I = I;
       dc.k = k;
       dc.T = T;
-      dc.splits = down_splits;
+      dc.splits = fuse_down ? down_splits : narrow_splits;
       KernelTimer kt(p, MOE_K_DOWN);
-      launch_down_combine(dc, kt.tm, s);
+      if (fuse_down)
+        launch_down_combine(dc, kt.tm, s);
+      else
+        launch_down_combine16(dc, kt.tm, s);
     } else {
       {
         KernelTimer kt(p, MOE_K_DOWN);

@@ -96,6 +96,137 @@ __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __rest
   }
 }
 
+// The same fusion on 16-row tiles of H, for batches too small to give the
+// 64-row form enough workgroups (a batch-1 layer with H = 2048 has only 32 of
+// those). A workgroup owns (16-row tile of H, token t); lane l of a wave takes
+// row l % 16 of the tile and every fourth K chunk starting at l / 16, so each
+// code load reads a quarter (256 contiguous bytes) of four of the 1 KiB blocks
+// that the wide form reads whole. A lane's h chunk is not wave-uniform, so the
+// token's k rows of h and their chunk sums are staged once per workgroup in LDS
+// (their global loads are issued together with the first code loads). Per chunk:
+//   part += 16 s (sum v h - 1.5 sum h),  v = 1 + n/16,
+// then the four chunk lanes of a row are added (lanes r, r+16, r+32, r+48, in
+// a fixed tree), the S waves of a slot and the k slots meet in LDS, and
+//   y[t][r] = sum over j = 0..k-1, in order, of w_j * (sum over s of part[j][s][r]).
+constexpr int kNarrowIt = 4;     // chunks per lane whose code loads are issued together
+constexpr int kNarrowStage = 8;  // h units (16 bytes) per thread staged from registers
+
+template <int CPG>
+struct NarrowBatch {
+  u32x4 wv[kNarrowIt];
+  uint16_t sc[kNarrowIt];
+  __device__ __forceinline__ void load(guint4* codes, gushort* scales, int cfirst, int c1) {
+#pragma unroll
+    for (int i = 0; i < kNarrowIt; ++i) {
+      const int c = min(cfirst + 4 * i, c1 - 1);
+      wv[i] = codes[(size_t)c * 64];
+      sc[i] = scales[(size_t)(c / CPG) * 64];
+    }
+  }
+};
+
+template <int CPG>
+__global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __restrict__ aptr,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ wts, const void* __restrict__ h,
+                                                      const float* __restrict__ hpart, float* __restrict__ y,
+                                                      int64_t off_codes, int64_t off_scales, int chunks, int groups,
+                                                      int H, int I, int k, int splits) {
+  __shared__ float part[kMaxW][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, cl = lane >> 4;
+  const int tile = blockIdx.x, t = blockIdx.y;
+  const int j = wave / splits, sp = wave % splits;
+  const uint8_t* base = aptr[t * k + j];
+  const int lane_off = (tile & 3) * 16 + r;  // place of row r in its 64-row block
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)(tile >> 2) * chunks * 64 + lane_off;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)(tile >> 2) * groups * 64 + lane_off;
+  const int c0 = (chunks * sp) / splits, c1 = (chunks * (sp + 1)) / splits;
+  const int n_it = (c1 - c0 + 3) >> 2;  // chunk iterations of the wave (lanes past c1 count 0)
+
+  NarrowBatch<CPG> cur;
+  if (n_it > 0) cur.load(codes, scales, c0 + cl, c1);
+
+  // stage h rows [k][I] (bf16, 16-byte units) and chunk sums [k][I/32] of token t
+  const int units = I / 8, n_units = k * units, nsum = I / 32;
+  uint4* hl = moe_dyn_lds;
+  float* hsl = reinterpret_cast<float*>(moe_dyn_lds + n_units);
+  const uint4* h4 = static_cast<const uint4*>(h);
+  const int nthr = blockDim.x;
+  for (int u0 = 0; u0 < n_units; u0 += kNarrowStage * nthr) {
+    uint4 hv[kNarrowStage];
+#pragma unroll
+    for (int i = 0; i < kNarrowStage; ++i) {
+      const int u = min(u0 + (int)threadIdx.x + i * nthr, n_units - 1);
+      hv[i] = h4[(size_t)inv[t * k + u / units] * units + u % units];
+    }
+#pragma unroll
+    for (int i = 0; i < kNarrowStage; ++i) {
+      const int u = u0 + (int)threadIdx.x + i * nthr;
+      if (u < n_units) hl[u] = hv[i];
+    }
+  }
+  for (int i = threadIdx.x; i < k * nsum; i += nthr) hsl[i] = hpart[(size_t)inv[t * k + i / nsum] * nsum + i % nsum];
+  __syncthreads();
+
+  const uint4* hrow = hl + j * units;
+  const float* hs_row = hsl + j * nsum;
+  float acc = 0.f;
+  for (int ib = 0; ib < n_it; ib += kNarrowIt) {
+    NarrowBatch<CPG> nxt;
+    if (ib + kNarrowIt < n_it) nxt.load(codes, scales, c0 + cl + 4 * (ib + kNarrowIt), c1);
+#pragma unroll
+    for (int i = 0; i < kNarrowIt; ++i) {
+      const int c = c0 + cl + 4 * (ib + i);
+      const int cc = min(c, c1 - 1);
+      uint32_t xw[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = hrow[cc * 4 + q];
+        xw[4 * q] = v.x;
+        xw[4 * q + 1] = v.y;
+        xw[4 * q + 2] = v.z;
+        xw[4 * q + 3] = v.w;
+      }
+      const float d = chunk_dot_bf16(cur.wv[i], xw, 0.f);
+      const float sc = (c < c1) ? 16.f * half_bits(cur.sc[i]) : 0.f;
+      acc = fmaf(sc, d - 1.5f * hs_row[cc], acc);
+    }
+    cur = nxt;
+  }
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 16) part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+    float yv = 0.f;
+    for (int jj = 0; jj < k; ++jj) {
+      float o = 0.f;
+      for (int s2 = 0; s2 < splits; ++s2) o += part[jj * splits + s2][lane];
+      yv = fmaf(wts[t * k + jj], o, yv);
+    }
+    y[(size_t)t * H + tile * 16 + lane] = yv;
+  }
+}
+
+size_t down_combine16_lds(int k, int I) { return (size_t)k * I * 2 + (size_t)k * (I / 32) * 4; }
+
+void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t s) {
+  const dim3 grid(a.H / 16, a.T), block(64 * a.k * a.splits);
+  const size_t lds = down_combine16_lds(a.k, a.I);
+#define DOWN_COMB16(C)                                                                                          \
+  launch_timed(k_down_comb16<C>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.off_codes, \
+               a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits)
+  switch (a.G / 32) {
+    case 1: DOWN_COMB16(1); break;
+    case 2: DOWN_COMB16(2); break;
+    case 4: DOWN_COMB16(4); break;
+    default: DOWN_COMB16(8); break;
+  }
+#undef DOWN_COMB16
+}
+
 void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s) {
   const dim3 grid(a.H / 64, a.T), block(64 * a.k * a.splits);
 #define DOWN_COMB(C)                                                                                           \

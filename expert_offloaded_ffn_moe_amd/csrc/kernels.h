@@ -136,6 +136,11 @@ void launch_gateup(const GemvArgs& a, int act_bf16, int max_tok, int grid, const
 void launch_down(const GemvArgs& a, int act_bf16, int max_tok, int grid, const Timing& tm, hipStream_t s);
 void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s);
 void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s);  // bf16, k * splits <= 16
+// the same on 16-row tiles of H (grid H/16 x T), for batches with few 64-row tiles
+void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t s);  // bf16, k * splits <= 16
+size_t down_combine16_lds(int k, int I);  // dynamic LDS bytes of launch_down_combine16
+constexpr size_t kDownComb16MaxLds = 48 * 1024;
+constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);

@@ -44,6 +44,7 @@ __device__ __forceinline__ void topk_wave_nv(const float* __restrict__ lrow, int
       const unsigned long long b = __ballot(v[i] == m);
       if (win < 0 && b != 0ull) win = 64 * i + (int)__builtin_ctzll(b);
     }
+    win = max(win, 0);  // only NaN logits (outside the contract) leave no winner; keep ids in range
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = (lane + 64 * i == win) ? -INFINITY : v[i];
     my_v = (lane == j) ? m : my_v;
