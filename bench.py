@@ -70,6 +70,8 @@ def parse_args():
                          "size, for scaling the memory counters of a profiler run), then exit")
     ap.add_argument("--gemm-min-tokens", type=int, default=0,
                     help="batches of at least this many tokens take the grouped MFMA GEMM (0: the library default)")
+    ap.add_argument("--stage-slots", type=int, default=0,
+                    help="prefill: HBM staging slots for the offloaded experts a batch touches (0 = read in place)")
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
 
@@ -124,11 +126,18 @@ def roofline(per_kernel, bytes_hbm, bytes_host, assignments, H, I):
     closer to (flops for large batches, weight bytes for small ones), the other under
     "other".
     """
-    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down") if n in per_kernel]
+    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down", "stage") if n in per_kernel]
     dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
     t = per_kernel[dom]["avg_us"] * 1e-6
-    share = 2.0 / 3.0 if dom in ("gateup", "gemm_gateup") else 1.0 / 3.0
-    hb, sb = share * bytes_hbm, share * bytes_host
+    staged = "stage" in per_kernel
+    if dom == "stage":  # the staging copy moves the touched offloaded experts over the host link once
+        hb, sb = 0.0, bytes_host
+    elif staged:  # the GEMMs then read every touched expert from HBM
+        share = 2.0 / 3.0 if dom == "gemm_gateup" else 1.0 / 3.0
+        hb, sb = share * (bytes_hbm + bytes_host), 0.0
+    else:
+        share = 2.0 / 3.0 if dom in ("gateup", "gemm_gateup") else 1.0 / 3.0
+        hb, sb = share * bytes_hbm, share * bytes_host
     if sb == 0:
         bound, peak = "hbm", HBM_PEAK_GBS
     elif hb == 0:
@@ -165,7 +174,7 @@ def run_one(args, d, layers, B, plan_kind, steps, warmup):
     eb = synth.expert_bytes(H, I, G)
     slots = {"mixed": int(round(0.7 * E)), "hbm": E, "host": 0}[plan_kind]
     cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=slots,
-                          gemm_min_tokens=args.gemm_min_tokens)
+                          gemm_min_tokens=args.gemm_min_tokens, prefill_stage_slots=args.stage_slots)
     plan = moe.Plan(cfg)
     for l, ly in enumerate(layers):
         res = synth.coldest_host_plan(seed, l, E, slots / E) if plan_kind == "mixed" else None
@@ -222,7 +231,8 @@ def run_one(args, d, layers, B, plan_kind, steps, warmup):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "%s layer H%d I%d E%d k%d int4 G%d, batch %d, %d-layer rotation, plan %s" % (
-            name, H, I, E, k, G, B, L, plan_kind), "hbm_slots": slots, "alpha": alpha, "seed": seed},
+            name, H, I, E, k, G, B, L, plan_kind), "hbm_slots": slots, "prefill_stage_slots": args.stage_slots,
+            "alpha": alpha, "seed": seed},
         "roofline": roof,
         "layer": {"expert_bytes_per_step_hbm": int(bytes_hbm), "expert_bytes_per_step_host": int(bytes_host),
                   "unique_experts_per_step": round((bytes_hbm + bytes_host) / eb, 3),

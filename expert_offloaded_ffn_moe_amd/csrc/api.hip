@@ -80,6 +80,8 @@ struct Workspace {
   int32_t* act_pos = nullptr;  // [E]
   int32_t* n_tiles = nullptr;
   unsigned* route_cnt = nullptr;  // [64] arrival counters: [0] fused decode routing, [16] multi-block grouping
+  uint8_t* stage = nullptr;       // [prefill_stage_slots][blob bytes] prefill staging slots
+  const uint8_t** gptr = nullptr; // [E] blob table of a staged prefill forward
 };
 
 }  // namespace
@@ -439,6 +441,12 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   TRY(alloc_as(p, &w.hist, (size_t)((Tm + kGroupTokens - 1) / kGroupTokens) * E));
   TRY(alloc_as(p, &w.act_pos, E));
   TRY(alloc_as(p, &w.n_tiles, 64));
+  if (cfg->prefill_stage_slots > 0) {
+    void* v = nullptr;
+    TRY(dev_alloc(p, &v, (size_t)cfg->prefill_stage_slots * p->L.bytes));
+    w.stage = static_cast<uint8_t*>(v);
+    TRY(alloc_as(p, &w.gptr, E));
+  }
 #undef TRY
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
     free_plan(p);
@@ -595,8 +603,28 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       KernelTimer kt(p, MOE_K_ROUTE);
       launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
     }
+    // offloaded experts of this batch into the staging slots (when the plan has
+    // them and the layer has offloaded experts); the GEMMs read the table it writes
+    const uint8_t* const* gemm_wptr = ly.d_wptr;
+    if (c.prefill_stage_slots > 0 && c.hbm_slots < E) {
+      StageArgs sa{};
+      sa.wptr = ly.d_wptr;
+      sa.is_host = ly.d_is_host;
+      sa.counts = w.counts;
+      sa.act_pos = w.act_pos;
+      sa.active = w.active;
+      sa.n_active = w.n_active;
+      sa.stage = w.stage;
+      sa.gptr = w.gptr;
+      sa.bytes = p->L.bytes;
+      sa.E = E;
+      sa.n_slots = c.prefill_stage_slots;
+      KernelTimer kt(p, MOE_K_STAGE);
+      launch_stage(sa, kt.tm, s);
+      gemm_wptr = w.gptr;
+    }
     GemmArgs gg{};
-    gg.wptr = ly.d_wptr;
+    gg.wptr = gemm_wptr;
     gg.tiles = w.tiles;
     gg.n_tiles = w.n_tiles;
     gg.offsets = w.offsets;

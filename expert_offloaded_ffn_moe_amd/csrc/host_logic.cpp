@@ -48,6 +48,8 @@ std::string check_config(const moe_config& c) {
   if (c.max_tokens < 1 || c.max_tokens > (1 << 20)) return "max_tokens must be in 1..2^20";
   if ((int64_t)c.max_tokens * c.top_k > (1 << 22)) return "max_tokens * top_k must be <= 2^22";
   if (c.hbm_slots < 0 || c.hbm_slots > c.num_experts) return "hbm_slots must be in 0..num_experts";
+  if (c.prefill_stage_slots < 0 || c.prefill_stage_slots > c.num_experts)
+    return "prefill_stage_slots must be in 0..num_experts";
   if (c.hidden > 65536 || c.inter > 65536) return "hidden and inter must be <= 65536";
   return "";
 }

@@ -112,6 +112,21 @@ struct DownCombArgs {
   int splits;                  // waves per slot (K split)
 };
 
+// Prefill staging of offloaded experts (see k_stage.hip).
+struct StageArgs {
+  const uint8_t* const* wptr;  // [E] layer blob table (HBM slot or host-mapped copy)
+  const int32_t* is_host;      // [E]
+  const int32_t* counts;       // [E] rows per expert of this forward
+  const int32_t* act_pos;      // [E] active-list position (valid where counts > 0)
+  const int32_t* active;       // [E] active experts, host-read ones first
+  const int32_t* n_active;     // [1]
+  uint8_t* stage;              // [n_slots][bytes] staging slots in HBM
+  const uint8_t** gptr;        // [E] out: blob table for the GEMMs
+  int64_t bytes;               // internal blob bytes (multiple of 16)
+  int E, n_slots;
+  int table_blocks, blocks_per_expert;  // set by launch_stage
+};
+
 struct CombineArgs {
   const float* o;       // [T*k][H]
   const float* wts;     // [T*k]
@@ -141,6 +156,7 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
 size_t down_combine16_lds(int k, int I);  // dynamic LDS bytes of launch_down_combine16
 constexpr size_t kDownComb16MaxLds = 48 * 1024;
 constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count
+void launch_stage(StageArgs a, const Timing& tm, hipStream_t s);
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);

@@ -88,6 +88,16 @@ typedef struct {
                               decode routing and the GEMVs); 0 = library default (6:
                               from about 6 tokens, experts shared by several tokens
                               make the GEMM faster than the GEMVs), < 0 = never */
+  int32_t prefill_stage_slots; /* 0..E HBM slots, shared by all layers, into which a
+                              GEMM-path forward first copies the offloaded experts its
+                              routing touches (one read of each over the host link, by
+                              a copy kernel, before the GEMMs; those then re-read HBM
+                              once per 64-row tile). Active offloaded experts beyond
+                              this count are read in place. 0 = none: the GEMMs read
+                              every offloaded expert in place. Page "我在 32GB 单卡上
+                              跑两万四千专家的 MoE", section 二, has the VRAM cache
+                              keep slots for the experts a batch needs; P2's prefill
+                              micro-batches (ub 1024/2048) make the re-reads large */
 } moe_config;
 
 typedef struct {
@@ -135,6 +145,7 @@ typedef enum {
   MOE_K_COMBINE = 4,     /* gate-weighted combine */
   MOE_K_GEMM_GATEUP = 5, /* gate/up grouped MFMA GEMM + SwiGLU (prefill path) */
   MOE_K_GEMM_DOWN = 6,   /* down grouped MFMA GEMM (prefill path) */
+  MOE_K_STAGE = 7,       /* copy of offloaded experts into prefill staging slots */
   MOE_K_COUNT = 8
 } moe_kernel;
 

@@ -42,7 +42,8 @@ def test_expert_bytes_and_validation(lib):
     bad = [moe.make_config(250, 128, 8, 2, 32), moe.make_config(256, 128, 8, 9, 32),
            moe.make_config(256, 128, 8, 2, 48), moe.make_config(256, 128, 2000, 2, 32),
            moe.make_config(256, 100, 8, 2, 32), moe.make_config(256, 128, 8, 2, 32, max_tokens=0),
-           moe.make_config(256, 128, 8, 2, 32, hbm_slots=9)]
+           moe.make_config(256, 128, 8, 2, 32, hbm_slots=9), moe.make_config(256, 128, 8, 2, 32, prefill_stage_slots=9),
+           moe.make_config(256, 128, 8, 2, 32, prefill_stage_slots=-1)]
     for cfg in bad:
         out = ctypes.c_size_t()
         assert lib.moe_expert_bytes(ctypes.byref(cfg), ctypes.byref(out)) == moe.MOE_E_INVALID
