@@ -139,7 +139,7 @@ constexpr int kRouteSmallMaxAssign = 256;   // T*k handled by launch_route_decod
 constexpr int kRouteSmallMaxTokens = 64;
 constexpr int kRouteDecodeMaxTokensBf16 = 4;  // bf16 batches routed by the one-launch decode routing
 constexpr int kDownCombMaxTokens = 4;     // decode batches whose down projection and combine fuse
-constexpr int kDownCombMinGroups = 128;   // ... if (H/64) * T workgroups reach this
+constexpr int kDownCombMinGroups = 256;   // ... if (H/64) * T workgroups reach this (else 16-row tiles)
 
 void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s);
 void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, unsigned* counter,
