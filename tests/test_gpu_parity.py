@@ -105,6 +105,8 @@ SMALL = [
     (256, 128, 8, 2, 32, "f32", 150, 0.5, 20),    # T*k > 256: multi-block grouping, fp32 GEMVs, ragged last block
     (2048, 256, 16, 4, 256, "bf16", 2, 0.5, 21),  # G = 256 with experts holding 2 tokens (4-token kernel)
     (512, 256, 16, 4, 128, "f32", 2, 0.0, 22),    # fp32 rows, experts holding 2 tokens (4-token kernel)
+    (1024, 2048, 16, 4, 128, "bf16", 1, 0.5, 23),  # 16-row fused down + combine with h staged in LDS (I > 1024)
+    (512, 1280, 8, 2, 64, "bf16", 3, 0.0, 24),    # the same, G = 64, 5 chunks per wave (ragged chunk quarters)
 ]
 
 
