@@ -65,6 +65,7 @@ def parse_args():
                     help="comma list of plan:batch runs on the same generated layers, one JSON line each")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--max-promotions", type=int, default=8, help="cache workload: promotions per layer per update")
+    ap.add_argument("--decay", type=float, default=0.9, help="cache workload: score decay per update")
     ap.add_argument("--copy-mb", type=float, default=None,
                     help="only run 10 device-to-device copies of this many MiB (a plain copy kernel of known "
                          "size, for scaling the memory counters of a profiler run), then exit")
@@ -337,7 +338,7 @@ def run_cache(args, d, layers):
             for l in range(L):
                 plan.forward(l, xs[i * L + l], y)
             if mode == "cache":
-                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions, overlap=True)  # pipelined
+                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)  # pipelined
             else:
                 torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
@@ -353,7 +354,7 @@ def run_cache(args, d, layers):
             for l in range(L):
                 plan.forward(l, xs[i * L + l], y)
             if mode == "cache":
-                plan.cache_update(-1, decay=0.9, max_promotions=args.max_promotions, overlap=True)
+                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
         kt = plan.kernel_times()
         plan.profile(False)
         plan.destroy()
@@ -388,8 +389,8 @@ def run_cache(args, d, layers):
         "data": "synthetic",
         "config": {"workload": "expert-cache decode run: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d "
                                "int4 G%d, %d HBM slots per layer (rest host-mapped), batch %d, %d steps, cold start, "
-                               "pipelined cache update after every step (max %d promotions per layer)" % (
-                                   L, H, I, E, k, G, S, B, steps, args.max_promotions),
+                               "pipelined cache update after every step (max %d promotions per layer, score decay %g)" % (
+                                   L, H, I, E, k, G, S, B, steps, args.max_promotions, args.decay),
                    "alpha": alpha, "seed": seed},
         "roofline": c["roofline"],
         "cache_run": {n: v for n, v in c.items() if n != "roofline"},
