@@ -6,11 +6,12 @@ namespace moe {
 // waves per workgroup: about kBatch chunks of K per wave, at most 8 waves. With
 // 16 waves (1024 threads) only one workgroup fits a CU, and a 384-workgroup
 // batch-1 launch of a 7168-wide layer then runs in two rounds: 26.6 us against
-// 23.2 us at 8 waves, where two fit and all are resident at once.
+// 23.2 us at 8 waves, where two fit and all are resident at once. The two-token
+// kernel on rows of 4096+ takes 4 waves (7168-wide layer, batch 2: 43.3 -> 38.1
+// us; at 4 tokens 8 waves stay best, 60.7 against 65.1 us).
 static int waves_for(const GemvArgs& a, int mt) {
-  (void)mt;
   const int chunks = a.groups * (a.G / 32);
-  const int wmax = 8;
+  const int wmax = (mt == 2 && chunks >= 128) ? 4 : 8;
   return std::max(1, std::min(std::min(wmax, a.groups), (chunks + kBatch - 1) / kBatch));
 }
 

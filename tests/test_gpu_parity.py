@@ -323,6 +323,10 @@ def test_prefill_offloaded_experts_staged(moe, T, seed):
         ys[name] = run(plan, c, logits_in=lg)
         ys[name + " again"] = run(plan, c, logits_in=lg)
         st = plan.stats(0)
+        if 0 < slots < 128:  # experts promoted and evicted under a staged plan: still the same y
+            plan.cache_update(0, max_promotions=16)
+            ys[name + " after a cache update"] = run(plan, c, logits_in=lg)
+            assert plan.stats(0)["promotions"] > 0
         in_hbm = np.ones(128, np.int32) if resident is None else resident
         acc = O.link_accounting(O.route(lg, c.k)[0], in_hbm, eb)
         assert st["bytes_host"] == 2 * acc["bytes_host"] and st["bytes_hbm"] == 2 * acc["bytes_hbm"], name
