@@ -338,3 +338,89 @@ def test_prefill_offloaded_experts_staged(moe, T, seed):
     toks = np.sort(rng.choice(T, 48, replace=False))
     ref = LC.oracle_forward(c, logits_in=lg, tokens=toks)
     check_y(ys["staged"][toks], ref["y"], "staged prefill y (%d sampled tokens)" % len(toks))
+
+
+# ----------------------------------------------------------------------------- full-size DeepSeek-style layer
+
+DS_LAYER = dict(H=7168, I=2048, E=384, k=6, G=128, seed=2, alpha=1.0)
+DS_CHECKED = {1: [0], 4: [0, 3], 16: [5, 12]}  # batch -> tokens whose outputs are compared
+
+
+@pytest.fixture(scope="module")
+def deepseek_layer(moe):
+    """The DeepSeek-style layer at its full size (H7168 I2048 E384 k6 G128, Zipf bias alpha
+    1.0), one seeded batch per size. Experts that the checked tokens route to carry their
+    generated weights; every other expert is filled with its own constant code byte and
+    small finite scales, so a read of a wrong expert changes the result."""
+    import concurrent.futures
+    import synth
+    d = DS_LAYER
+    H, I, E, k, G, seed = d["H"], d["I"], d["E"], d["k"], d["G"], d["seed"]
+    Wr_store = synth.router_weight(seed, 0, E, H, "bf16")
+    Wr, b = O.bf16_bits_to_f64(Wr_store), synth.router_bias(seed, 0, E, d["alpha"])
+    cases, need = {}, set()
+    for T, toks in DS_CHECKED.items():
+        c = LC.Case(H, I, E, k, G, "bf16", T, seed, d["alpha"], 0)
+        c.x_bits = synth.activations(seed, 100 + T, T, H, "bf16")
+        c.x, c.Wr_store, c.Wr, c.b = O.bf16_bits_to_f64(c.x_bits), Wr_store, Wr, b
+        c.lg = LC.oracle_logits(c)
+        need |= set(int(e) for e in O.route(c.lg, k)[0][toks].ravel())
+        cases[T] = c
+    eb = synth.expert_bytes(H, I, G)
+    blobs = np.empty((E, eb), np.uint8)
+    a0 = O.expert_layout(H, I, G)[0]["s_gate"][0]
+    for e in range(E):
+        blobs[e, :a0].fill((37 * e + 11) & 0xFF)
+        blobs[e, a0:].view(np.uint16)[:] = 0x2000  # fp16 2^-7
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        for e, blob in zip(sorted(need), ex.map(lambda e: synth.expert_blobs(seed, 0, e, 1, H, I, G)[0],
+                                                sorted(need))):
+            blobs[e] = blob
+    res = synth.coldest_host_plan(seed, 0, E, 0.7)  # 269 experts in HBM, the 115 coldest on the host
+    cfg = moe.make_config(H, I, E, k, G, "bf16", max_tokens=max(DS_CHECKED), hbm_slots=int(res.sum()))
+    plan = moe.Plan(cfg)
+    plan.load_layer(0, Wr_store, b, blobs, res)
+    for c in cases.values():
+        c.blobs = blobs
+    _say("  deepseek-shaped layer: %d generated experts, %d in HBM" % (len(need), int(res.sum())))
+    yield plan, cases, res
+    plan.destroy()
+
+
+@pytest.mark.parametrize("T", sorted(DS_CHECKED))
+def test_deepseek_shaped_full_size(moe, deepseek_layer, T):
+    """Full-size DeepSeek-style layer in the launch configuration the benchmark times
+    (70/30 plan, default dispatch: GEMVs with the 16-row fused down + combine at batches
+    1 and 4, the grouped MFMA GEMM at 16). Routing bit-exact against the oracle for every
+    token; y on the checked tokens, with the oracle's logits and with the library's router;
+    link counters against an exact recount."""
+    import synth
+    plan, cases, res = deepseek_layer
+    c = cases[T]
+    toks = np.array(DS_CHECKED[T])
+    ref = LC.oracle_forward(c, logits_in=c.lg, tokens=toks)
+    rb = route_bufs(c)
+    plan.reset_stats()
+    y = run(plan, c, logits_in=c.lg, route=rb)
+    full = O.route(c.lg, c.k)
+    counts, offsets, srt, inv = O.align_permute(full[0], c.E)
+    np.testing.assert_array_equal(rb["topk_ids"].cpu().numpy().reshape(c.T, c.k), full[0])
+    np.testing.assert_array_equal(rb["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(rb["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(rb["sorted"].cpu().numpy(), srt)
+    np.testing.assert_array_equal(rb["inv"].cpu().numpy(), inv)
+    assert np.all(np.isfinite(y))
+    check_y(y[toks], ref["y"], "deepseek-shaped y, batch %d (tokens %s)" % (T, toks.tolist()))
+    st = plan.stats(0)
+    acc = O.link_accounting(full[0], res, synth.expert_bytes(c.H, c.I, c.G))
+    assert (st["hits"], st["misses"]) == (acc["hits"], acc["misses"])
+    assert (st["bytes_hbm"], st["bytes_host"]) == (acc["bytes_hbm"], acc["bytes_host"])
+    # the library's router: logits within fp32 accumulation error, y where the routing is clear
+    rb2 = route_bufs(c)
+    y2 = run(plan, c, route=rb2)
+    glog = rb2["logits"].cpu().numpy().reshape(c.T, c.E).astype(np.float64)
+    tol = 1e-5 * max(1.0, np.abs(c.lg).max())
+    assert np.abs(glog - c.lg).max() <= tol
+    clear = LC.routing_margins(c.lg, c.k)[toks] > 2 * tol
+    if clear.any():
+        check_y(y2[toks[clear]], ref["y"][clear], "deepseek-shaped y, library router, batch %d" % T)
