@@ -217,18 +217,26 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 // (K = I), n-tile = 64 down rows, epilogue -> o (fp32, by sorted position).
 // Per quantisation group: the A rows and the wave's codes and scales of group
 // g + 1 are loaded into registers while group g runs on the MFMAs.
+// Row sums of a group's A rows: for gate/up with G <= 128 (PRESUM) they are the
+// per-token group sums xsum[t][g] that the router launch writes once per token,
+// loaded with the group's other operands; otherwise (the down projection's h
+// rows, and 128-wide halves of G = 256 groups) each workgroup sums the rows it
+// stages. Every workgroup of a token's row tiles would otherwise redo the same
+// sums (for gate/up, k experts x the n-tile groups of each).
 template <int G, bool GATEUP>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restrict__ wptr,
                                                  const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ sorted, const uint16_t* __restrict__ a_src,
-                                                 void* __restrict__ out, int64_t off_codes, int64_t off_scales,
+                                                 const float* __restrict__ xsum, void* __restrict__ out,
+                                                 int64_t off_codes, int64_t off_scales,
                                                  int chunks, int groups, int ntiles_n, int K, int out_ld, int k) {
   // The loop runs over sub-groups of SG <= 128 K values (G = 256 takes two per
   // quantisation group, sharing its scale), so that two register sets of a
   // sub-group's operands fit beside the accumulators at two waves per SIMD.
   constexpr int SG = G > 128 ? 128 : G, SPG = G / SG;
   constexpr int CPG = SG / 32;
+  constexpr bool PRESUM = GATEUP && SPG == 1;
   __shared__ GemmShared<SG> sh;
   const int nsub = groups * SPG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -265,6 +273,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   gu32x4* codes = (gu32x4*)(base + off_codes) + (size_t)(active_wave ? nt : 0) * chunks * 64 + lane;
   gu16* scales = (gu16*)(base + off_scales) + (size_t)(active_wave ? nt : 0) * groups * 64;
   const int i32 = lane & 31, half = lane >> 5;
+  // PRESUM: group sums of the tokens of rows 32 s + lane % 32 (padding rows repeat the last row)
+  const float* xs_row0 = xsum;
+  const float* xs_row1 = xsum;
+  if (PRESUM) {
+    xs_row0 = xsum + (size_t)(sorted[p0 + m0 + min(i32, mrows - 1)] / k) * groups;
+    xs_row1 = xsum + (size_t)(sorted[p0 + m0 + min(32 + i32, mrows - 1)] / k) * groups;
+  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     u32x4 b[CPG];
     uint16_t s0, s1;
   };
-  auto load = [&](Regs& r, int gl) {
+  auto load = [&](Regs& r, int gl) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < CPG; ++q) r.a[q] = src[q][(size_t)gl * PPR];
 #pragma unroll
@@ -295,23 +310,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   // g + 1 (clamped to the last group) loaded into `nxt` while g runs on the MFMAs.
   // The two register sets alternate between even and odd groups, so the loads
   // in flight are only waited for where the next group first uses them.
-  auto step = [&](auto two_c, auto odd_c, int g, Regs& cur, Regs& nxt) {
+  auto step = [&](auto two_c, auto odd_c, int g, Regs& cur, Regs& nxt) __attribute__((always_inline)) {
     constexpr bool TWO = decltype(two_c)::value;  // second 32-row block has rows
     constexpr bool ODD = decltype(odd_c)::value;  // g is odd
     constexpr int buf = ODD ? 1 : 0;
+    // PRESUM: this group's sums of the lane's two rows, loaded now and used after the MFMAs
+    const float xs0 = PRESUM ? xs_row0[g] : 0.f, xs1 = PRESUM ? xs_row1[g] : 0.f;
     {
-      float rs[CPG];
 #pragma unroll
       for (int q = 0; q < CPG; ++q) {
         const int P = threadIdx.x + 256 * q;
-        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<SG>::kStride + spiece * 16) = cur.a[q];
-        rs[q] = piece_sum(cur.a[q]);
+        uint4 v = cur.a[q];
+        // pins the value to vector registers here: without it the compiler merges the even
+        // and odd copies of this step through a scratch copy of both register sets
+        asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<SG>::kStride + spiece * 16) = v;
       }
+      if constexpr (!PRESUM) {
+        float rs[CPG];
 #pragma unroll
-      for (int q = 0; q < CPG; ++q) rs[q] = lane_group_sum<PPR>(rs[q]);
-      if (spiece == 0) {
+        for (int q = 0; q < CPG; ++q) rs[q] = lane_group_sum<PPR>(piece_sum(cur.a[q]));
+        if (spiece == 0) {
 #pragma unroll
-        for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
+          for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
+        }
       }
     }
     load(nxt, min(g + 1, nsub - 1));
@@ -352,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     // (k = 0: group g - 1, k = 1: group g), B = the columns' 16 s of those groups
     float rc[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) rc[s] = sh.rowsum[buf][32 * s + i32];
+    for (int s = 0; s < 2; ++s) rc[s] = PRESUM ? (s == 0 ? xs0 : xs1) : sh.rowsum[buf][32 * s + i32];
     if (ODD || g == nsub - 1) {
       const int kg = half;  // this lane's k: 0 -> previous group, 1 -> this one
       const float fb0 = ODD ? (kg ? f0 : fp0) : (kg ? 0.f : f0);
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
 
   Regs r0, r1;
   load(r0, 0);
-  auto run = [&](auto two_c) {
+  auto run = [&](auto two_c) __attribute__((always_inline)) {
     for (int g = 0; g < nsub; g += 2) {
       step(two_c, std::false_type{}, g, r0, r1);
       if (g + 1 < nsub) step(two_c, std::true_type{}, g + 1, r1, r0);
@@ -412,7 +434,7 @@ static void gemm_g(const GemmArgs& a, const Timing& tm, hipStream_t s) {
   const dim3 grid(a.max_tiles * ngroup_wg), block(64 * kWaves);
 #define GEMM_LAUNCH(GG)                                                                                          \
   launch_timed(k_gemm<GG, GATEUP>, grid, block, 0, s, tm, a.wptr, a.tiles, a.n_tiles, a.offsets, a.sorted, a.a_src, \
-               a.out, a.off_codes, a.off_scales, a.chunks, a.groups, a.ntiles_n, a.K, a.out_ld, a.k)
+               a.xsum, a.out, a.off_codes, a.off_scales, a.chunks, a.groups, a.ntiles_n, a.K, a.out_ld, a.k)
   switch (a.G) {
     case 32: GEMM_LAUNCH(32); break;
     case 64: GEMM_LAUNCH(64); break;
