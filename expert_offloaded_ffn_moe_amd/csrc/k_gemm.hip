@@ -109,24 +109,21 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_
   __shared__ float part[kRouterWaves][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if ((int)blockIdx.x >= tile_blocks) {
-    const int ng = H / G;
-    const int gid = (blockIdx.x - tile_blocks) * (64 * kRouterWaves) + threadIdx.x;
-    if (gid >= T * ng) return;
-    const int t = gid / ng, g = gid % ng;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + (size_t)g * G);
-    float sum = 0.f;
-    for (int c = 0; c < G / 8; ++c) {
-      const uint4 v = src[c];
-      sum += bf16_lo(v.x);
-      sum += bf16_hi(v.x);
-      sum += bf16_lo(v.y);
-      sum += bf16_hi(v.y);
-      sum += bf16_lo(v.z);
-      sum += bf16_hi(v.z);
-      sum += bf16_lo(v.w);
-      sum += bf16_hi(v.w);
+    // one 16-byte piece of x per thread; the G/8 pieces of a group sit in
+    // consecutive lanes and are added with a fixed DPP tree
+    const int64_t piece = (int64_t)(blockIdx.x - tile_blocks) * (64 * kRouterWaves) + threadIdx.x;
+    const int ppg = G / 8;
+    const bool live = piece < (int64_t)T * (H / 8);
+    const uint4 v = live ? reinterpret_cast<const uint4*>(x)[piece] : make_uint4(0u, 0u, 0u, 0u);
+    float sum = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+    switch (ppg) {
+      case 4: sum = lane_group_sum<4>(sum); break;
+      case 8: sum = lane_group_sum<8>(sum); break;
+      case 16: sum = lane_group_sum<16>(sum); break;
+      default: sum = lane_group_sum<32>(sum); break;
     }
-    xsum[gid] = sum;
+    if (live && piece % ppg == 0) xsum[piece / ppg] = sum;
     return;
   }
   const int nte = (E + 31) / 32;
@@ -169,7 +166,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_
 
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s) {
   const int tiles = a.router_blocks > 0 ? ((a.T + 31) / 32) * ((a.E + 31) / 32) : 0;
-  const int xs = a.xsum ? (a.T * (a.H / a.G) + 64 * kRouterWaves - 1) / (64 * kRouterWaves) : 0;
+  const int xs = a.xsum ? (int)(((int64_t)a.T * (a.H / 8) + 64 * kRouterWaves - 1) / (64 * kRouterWaves)) : 0;
   if (tiles + xs == 0) return;
   launch_timed(k_router_mfma, dim3(tiles + xs), dim3(64 * kRouterWaves), 0, s, tm, static_cast<const uint16_t*>(a.x),
                static_cast<const uint16_t*>(a.w), a.b, a.logits, a.xsum, tiles, a.T, a.H, a.E, a.G);
