@@ -591,13 +591,11 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   rt.aptr = (fuse_down || fuse_narrow) ? w.aptr : nullptr;
   if (prefill) {
     {
-      // MFMA logits tiles (unless given) and the per-token group sums of x that
-      // the gate/up GEMM takes for its int4 offset term, one launch
-      RouterArgs rp = ra;
-      rp.router_blocks = logits_in ? 0 : 1;
-      rp.xsum = w.xsum;
+      RouterArgs rp = ra;  // logits only: the GEMMs take no group sums
+      rp.router_blocks = 1;
+      rp.xsum = nullptr;
       KernelTimer kt(p, MOE_K_ROUTER);
-      launch_router_mfma(rp, kt.tm, s);
+      if (!logits_in) launch_router_mfma(rp, kt.tm, s);
     }
     rt.tiles = w.tiles;
     rt.n_tiles = w.n_tiles;
@@ -632,7 +630,6 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     gg.offsets = w.offsets;
     gg.sorted = w.sorted;
     gg.a_src = static_cast<const uint16_t*>(x);
-    gg.xsum = w.xsum;
     gg.out = w.h;
     gg.off_codes = p->L.off_gu_codes;
     gg.off_scales = p->L.off_gu_scales;
@@ -650,7 +647,6 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     }
     GemmArgs gd = gg;
     gd.a_src = static_cast<const uint16_t*>(w.h);
-    gd.xsum = nullptr;
     gd.out = w.o;
     gd.off_codes = p->L.off_dn_codes;
     gd.off_scales = p->L.off_dn_scales;

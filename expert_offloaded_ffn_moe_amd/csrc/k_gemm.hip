@@ -109,21 +109,24 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_
   __shared__ float part[kRouterWaves][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if ((int)blockIdx.x >= tile_blocks) {
-    // one 16-byte piece of x per thread; the G/8 pieces of a group sit in
-    // consecutive lanes and are added with a fixed DPP tree
-    const int64_t piece = (int64_t)(blockIdx.x - tile_blocks) * (64 * kRouterWaves) + threadIdx.x;
-    const int ppg = G / 8;
-    const bool live = piece < (int64_t)T * (H / 8);
-    const uint4 v = live ? reinterpret_cast<const uint4*>(x)[piece] : make_uint4(0u, 0u, 0u, 0u);
-    float sum = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
-                ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
-    switch (ppg) {
-      case 4: sum = lane_group_sum<4>(sum); break;
-      case 8: sum = lane_group_sum<8>(sum); break;
-      case 16: sum = lane_group_sum<16>(sum); break;
-      default: sum = lane_group_sum<32>(sum); break;
+    const int ng = H / G;
+    const int gid = (blockIdx.x - tile_blocks) * (64 * kRouterWaves) + threadIdx.x;
+    if (gid >= T * ng) return;
+    const int t = gid / ng, g = gid % ng;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + (size_t)g * G);
+    float sum = 0.f;
+    for (int c = 0; c < G / 8; ++c) {
+      const uint4 v = src[c];
+      sum += bf16_lo(v.x);
+      sum += bf16_hi(v.x);
+      sum += bf16_lo(v.y);
+      sum += bf16_hi(v.y);
+      sum += bf16_lo(v.z);
+      sum += bf16_hi(v.z);
+      sum += bf16_lo(v.w);
+      sum += bf16_hi(v.w);
     }
-    if (live && piece % ppg == 0) xsum[piece / ppg] = sum;
+    xsum[gid] = sum;
     return;
   }
   const int nte = (E + 31) / 32;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_
 
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s) {
   const int tiles = a.router_blocks > 0 ? ((a.T + 31) / 32) * ((a.E + 31) / 32) : 0;
-  const int xs = a.xsum ? (int)(((int64_t)a.T * (a.H / 8) + 64 * kRouterWaves - 1) / (64 * kRouterWaves)) : 0;
+  const int xs = a.xsum ? (a.T * (a.H / a.G) + 64 * kRouterWaves - 1) / (64 * kRouterWaves) : 0;
   if (tiles + xs == 0) return;
   launch_timed(k_router_mfma, dim3(tiles + xs), dim3(64 * kRouterWaves), 0, s, tm, static_cast<const uint16_t*>(a.x),
                static_cast<const uint16_t*>(a.w), a.b, a.logits, a.xsum, tiles, a.T, a.H, a.E, a.G);
@@ -214,26 +217,18 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 // (K = I), n-tile = 64 down rows, epilogue -> o (fp32, by sorted position).
 // Per quantisation group: the A rows and the wave's codes and scales of group
 // g + 1 are loaded into registers while group g runs on the MFMAs.
-// Row sums of a group's A rows: for gate/up with G <= 128 (PRESUM) they are the
-// per-token group sums xsum[t][g] that the router launch writes once per token,
-// loaded with the group's other operands; otherwise (the down projection's h
-// rows, and 128-wide halves of G = 256 groups) each workgroup sums the rows it
-// stages. Every workgroup of a token's row tiles would otherwise redo the same
-// sums (for gate/up, k experts x the n-tile groups of each).
 template <int G, bool GATEUP>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restrict__ wptr,
                                                  const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ sorted, const uint16_t* __restrict__ a_src,
-                                                 const float* __restrict__ xsum, void* __restrict__ out,
-                                                 int64_t off_codes, int64_t off_scales,
+                                                 void* __restrict__ out, int64_t off_codes, int64_t off_scales,
                                                  int chunks, int groups, int ntiles_n, int K, int out_ld, int k) {
   // The loop runs over sub-groups of SG <= 128 K values (G = 256 takes two per
   // quantisation group, sharing its scale), so that two register sets of a
   // sub-group's operands fit beside the accumulators at two waves per SIMD.
   constexpr int SG = G > 128 ? 128 : G, SPG = G / SG;
   constexpr int CPG = SG / 32;
-  constexpr bool PRESUM = GATEUP && SPG == 1;
   __shared__ GemmShared<SG> sh;
   const int nsub = groups * SPG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -270,13 +265,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   gu32x4* codes = (gu32x4*)(base + off_codes) + (size_t)(active_wave ? nt : 0) * chunks * 64 + lane;
   gu16* scales = (gu16*)(base + off_scales) + (size_t)(active_wave ? nt : 0) * groups * 64;
   const int i32 = lane & 31, half = lane >> 5;
-  // PRESUM: group sums of the tokens of rows 32 s + lane % 32 (padding rows repeat the last row)
-  const float* xs_row0 = xsum;
-  const float* xs_row1 = xsum;
-  if (PRESUM) {
-    xs_row0 = xsum + (size_t)(sorted[p0 + m0 + min(i32, mrows - 1)] / k) * groups;
-    xs_row1 = xsum + (size_t)(sorted[p0 + m0 + min(32 + i32, mrows - 1)] / k) * groups;
-  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -294,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     u32x4 b[CPG];
     uint16_t s0, s1;
   };
-  auto load = [&](Regs& r, int gl) __attribute__((always_inline)) {
+  auto load = [&](Regs& r, int gl) {
 #pragma unroll
     for (int q = 0; q < CPG; ++q) r.a[q] = src[q][(size_t)gl * PPR];
 #pragma unroll
@@ -307,30 +295,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
   // g + 1 (clamped to the last group) loaded into `nxt` while g runs on the MFMAs.
   // The two register sets alternate between even and odd groups, so the loads
   // in flight are only waited for where the next group first uses them.
-  auto step = [&](auto two_c, auto odd_c, int g, Regs& cur, Regs& nxt) __attribute__((always_inline)) {
+  auto step = [&](auto two_c, auto odd_c, int g, Regs& cur, Regs& nxt) {
     constexpr bool TWO = decltype(two_c)::value;  // second 32-row block has rows
     constexpr bool ODD = decltype(odd_c)::value;  // g is odd
     constexpr int buf = ODD ? 1 : 0;
-    // PRESUM: this group's sums of the lane's two rows, loaded now and used after the MFMAs
-    const float xs0 = PRESUM ? xs_row0[g] : 0.f, xs1 = PRESUM ? xs_row1[g] : 0.f;
     {
+      float rs[CPG];
 #pragma unroll
       for (int q = 0; q < CPG; ++q) {
         const int P = threadIdx.x + 256 * q;
-        uint4 v = cur.a[q];
-        // pins the value to vector registers here: without it the compiler merges the even
-        // and odd copies of this step through a scratch copy of both register sets
-        asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<SG>::kStride + spiece * 16) = v;
+        *reinterpret_cast<uint4*>(sh.a[buf] + (P / PPR) * GemmShared<SG>::kStride + spiece * 16) = cur.a[q];
+        rs[q] = piece_sum(cur.a[q]);
       }
-      if constexpr (!PRESUM) {
-        float rs[CPG];
 #pragma unroll
-        for (int q = 0; q < CPG; ++q) rs[q] = lane_group_sum<PPR>(piece_sum(cur.a[q]));
-        if (spiece == 0) {
+      for (int q = 0; q < CPG; ++q) rs[q] = lane_group_sum<PPR>(rs[q]);
+      if (spiece == 0) {
 #pragma unroll
-          for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
-        }
+        for (int q = 0; q < CPG; ++q) sh.rowsum[buf][(threadIdx.x + 256 * q) / PPR] = rs[q];
       }
     }
     load(nxt, min(g + 1, nsub - 1));
@@ -371,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     // (k = 0: group g - 1, k = 1: group g), B = the columns' 16 s of those groups
     float rc[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) rc[s] = PRESUM ? (s == 0 ? xs0 : xs1) : sh.rowsum[buf][32 * s + i32];
+    for (int s = 0; s < 2; ++s) rc[s] = sh.rowsum[buf][32 * s + i32];
     if (ODD || g == nsub - 1) {
       const int kg = half;  // this lane's k: 0 -> previous group, 1 -> this one
       const float fb0 = ODD ? (kg ? f0 : fp0) : (kg ? 0.f : f0);
@@ -393,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
 
   Regs r0, r1;
   load(r0, 0);
-  auto run = [&](auto two_c) __attribute__((always_inline)) {
+  auto run = [&](auto two_c) {
     for (int g = 0; g < nsub; g += 2) {
       step(two_c, std::false_type{}, g, r0, r1);
       if (g + 1 < nsub) step(two_c, std::true_type{}, g + 1, r1, r0);
@@ -431,7 +412,7 @@ static void gemm_g(const GemmArgs& a, const Timing& tm, hipStream_t s) {
   const dim3 grid(a.max_tiles * ngroup_wg), block(64 * kWaves);
 #define GEMM_LAUNCH(GG)                                                                                          \
   launch_timed(k_gemm<GG, GATEUP>, grid, block, 0, s, tm, a.wptr, a.tiles, a.n_tiles, a.offsets, a.sorted, a.a_src, \
-               a.xsum, a.out, a.off_codes, a.off_scales, a.chunks, a.groups, a.ntiles_n, a.K, a.out_ld, a.k)
+               a.out, a.off_codes, a.off_scales, a.chunks, a.groups, a.ntiles_n, a.K, a.out_ld, a.k)
   switch (a.G) {
     case 32: GEMM_LAUNCH(32); break;
     case 64: GEMM_LAUNCH(64); break;

@@ -90,7 +90,6 @@ struct GemmArgs {
   const int32_t* offsets;      // [E+1]
   const int32_t* sorted;       // [T*k]
   const uint16_t* a_src;       // gate/up: x [T][H]; down: h [T*k][I] by sorted position
-  const float* xsum;           // gate/up: [T][H/G] group sums of x (used when G <= 128); down: null
   void* out;                   // gate/up: h [T*k][I] bf16; down: o [T*k][H] fp32
   int64_t off_codes, off_scales;
   int chunks, groups;          // per weight row
