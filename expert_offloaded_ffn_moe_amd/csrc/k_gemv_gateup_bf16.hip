@@ -6,12 +6,11 @@ namespace moe {
 // waves per workgroup: about kBatch chunks of K per wave, at most 8 waves. With
 // 16 waves (1024 threads) only one workgroup fits a CU, and a 384-workgroup
 // batch-1 launch of a 7168-wide layer then runs in two rounds: 26.6 us against
-// 23.2 us at 8 waves, where two fit and all are resident at once. The two-token
-// kernel on rows of 4096+ takes 4 waves (7168-wide layer, batch 2: 43.3 -> 38.1
-// us; at 4 tokens 8 waves stay best, 60.7 against 65.1 us).
+// 23.2 us at 8 waves, where two fit and all are resident at once.
 static int waves_for(const GemvArgs& a, int mt) {
+  (void)mt;
   const int chunks = a.groups * (a.G / 32);
-  const int wmax = (mt == 2 && chunks >= 128) ? 4 : 8;
+  const int wmax = 8;
   return std::max(1, std::min(std::min(wmax, a.groups), (chunks + kBatch - 1) / kBatch));
 }
 
@@ -19,7 +18,10 @@ static int waves_for(const GemvArgs& a, int mt) {
 // long (measured faster there), and the rows fit in 64 KiB; else scalar loads.
 static bool use_lds(size_t bytes, int mt, int K) { return bytes <= 65536 && (mt >= 2 || K >= 4096); }
 
-static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : max_tok <= 4 ? 4 : 8; }
+// Experts of a two- to four-token batch take the 4-token kernel: the 2-token
+// variant needs 202 VGPRs against 96 and ran slower (2048-wide layer, batch 2:
+// gate/up 12.3 -> 11.0 us; 7168-wide: 38.0 -> 37.7 us).
+static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 4 ? 4 : 8; }
 
 template <int MT, int CPG>
 static void gateup_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
@@ -40,8 +42,7 @@ static void gateup_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hip
     case 1: return gateup_w<MT, 1>(a, W, grid, tm, s);
     case 2: return gateup_w<MT, 2>(a, W, grid, tm, s);
     case 4: return gateup_w<MT, 4>(a, W, grid, tm, s);
-    // G = 256 with two tokens: the 4-token kernel (the two-token one spills)
-    default: return gateup_w<MT == 2 ? 4 : MT, 8>(a, W, grid, tm, s);
+    default: return gateup_w<MT, 8>(a, W, grid, tm, s);
   }
 }
 
@@ -49,7 +50,6 @@ void launch_gateup_bf16(const GemvArgs& a, int max_tok, int grid, const Timing& 
   const int W = waves_for(a, pick_mt(max_tok));
   switch (pick_mt(max_tok)) {
     case 1: return gateup_cpg<1>(a, W, grid, tm, s);
-    case 2: return gateup_cpg<2>(a, W, grid, tm, s);
     case 4: return gateup_cpg<4>(a, W, grid, tm, s);
     default: return gateup_cpg<8>(a, W, grid, tm, s);
   }
