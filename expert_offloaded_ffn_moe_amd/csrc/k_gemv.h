@@ -239,31 +239,16 @@ static __device__ __forceinline__ void stage_rows(const void* __restrict__ src, 
     for (int i = threadIdx.x; i < len16; i += blockDim.x) moe_dyn_lds[m * len16 + i] = s4[src_rows16[m] + i];
 }
 
+// The rows of one active expert and one output tile, MT token rows per pass
+// (red: the workgroup's [W][MT][64] partial sums in LDS).
 template <int BF16, int MT, int CPG, int XS>
-__global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __restrict__ work,
-                                                   const int32_t* __restrict__ sorted,
-                                                   const void* __restrict__ x, const float* __restrict__ xsum,
-                                                   void* __restrict__ h, float* __restrict__ hpart,
-                                                   int64_t off_codes, int64_t off_scales, int chunks, int groups,
-                                                   int tiles, int H, int I, int k) {
-  __shared__ float red[kMaxW][MT][64];
-  const int W = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  // the count and the descriptor are loaded together; a slot past the count has
-  // no rows (no branch between the two loads and their use)
-  // slots past the active count carry M = 0 (written by the grouping step), so
-  // the descriptor is the only dependent load before the weights
-  const WorkDesc* d = work + slot;
-  const uint8_t* base = d->w;
-  int M = d->M;
-  asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
-  M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
-  const int p0 = d->p0;
-  guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
-  gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
+static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, int W, int wave, int lane, int tile,
+                                                     const WorkDesc* d, int M, int p0, guint4* codes,
+                                                     gushort* scales, const int32_t* __restrict__ sorted,
+                                                     const void* __restrict__ x, const float* __restrict__ xsum,
+                                                     void* __restrict__ h, float* __restrict__ hpart, int groups,
+                                                     int H, int I, int k) {
   const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
-
   for (int m0 = 0; m0 < M; m0 += MT) {
     const int mc = min(MT, M - m0);
     int64_t rows[MT], sum_rows[MT];
@@ -292,14 +277,14 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __re
       k_loop<BF16, MT, CPG, false, XS>(codes, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MT; ++m) red[(wave * MT + m) * 64 + lane] = acc[m];
     __syncthreads();
     for (int i = threadIdx.x; i < MT * 32; i += blockDim.x) {  // whole 32-lane groups per m
       const int m = i >> 5, j = i & 31;
       float gs = 0.f, us = 0.f;
       for (int w = 0; w < W; ++w) {
-        gs += red[w][m][j];
-        us += red[w][m][32 + j];
+        gs += red[(w * MT + m) * 64 + j];
+        us += red[(w * MT + m) * 64 + 32 + j];
       }
       const float hv = gs / (1.f + __expf(-gs)) * us;
       const int64_t p = p0 + m0 + m;
@@ -317,6 +302,39 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __re
     }
     __syncthreads();
   }
+}
+
+// A workgroup: (active-expert slot, output tile). Multi-token variants (MT > 1)
+// give an expert that holds a single token the one-token path, whose activation
+// row comes in through scalar loads with no LDS staging or barrier before the
+// weights: in a batch of a few tokens most experts hold one.
+template <int BF16, int MT, int CPG, int XS>
+__global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __restrict__ work,
+                                                   const int32_t* __restrict__ sorted,
+                                                   const void* __restrict__ x, const float* __restrict__ xsum,
+                                                   void* __restrict__ h, float* __restrict__ hpart,
+                                                   int64_t off_codes, int64_t off_scales, int chunks, int groups,
+                                                   int tiles, int H, int I, int k) {
+  __shared__ float red[kMaxW * MT * 64];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  // slots past the active count carry M = 0 (written by the grouping step), so
+  // the descriptor is the only dependent load before the weights
+  const WorkDesc* d = work + slot;
+  const uint8_t* base = d->w;
+  int M = d->M;
+  asm volatile("" : "+v"(M) : "v"(base));  // fetch the blob pointer with the row count, not after it
+  M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
+  const int p0 = d->p0;
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
+  if (MT > 1 && M == 1)
+    gateup_expert<BF16, 1, CPG, 0>(red, W, wave, lane, tile, d, M, p0, codes, scales, sorted, x, xsum, h, hpart,
+                                   groups, H, I, k);
+  else
+    gateup_expert<BF16, MT, CPG, XS>(red, W, wave, lane, tile, d, M, p0, codes, scales, sorted, x, xsum, h, hpart,
+                                     groups, H, I, k);
 }
 
 // ----------------------------------------------------------------------------- down projection
