@@ -535,10 +535,11 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
   int part = 0;
   if (sum_thread) {
     int b = b0;
-    for (; b + 4 <= b1; b += 4) {  // four loads in flight
-      const int h0 = a.hist[(size_t)b * E + ej], h1 = a.hist[(size_t)(b + 1) * E + ej];
-      const int h2 = a.hist[(size_t)(b + 2) * E + ej], h3 = a.hist[(size_t)(b + 3) * E + ej];
-      part += (h0 + h1) + (h2 + h3);
+    for (; b + 8 <= b1; b += 8) {  // eight loads in flight
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = a.hist[(size_t)(b + i) * E + ej];
+      part += ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
     }
     for (; b < b1; ++b) part += a.hist[(size_t)b * E + ej];
   }
@@ -560,12 +561,17 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
   }
   if (tid == 0) a.offsets[E] = n;
   __syncthreads();
-  if (sum_thread) {
+  if (sum_thread) {  // counts of 8 blocks loaded together, then their bases written
     int run = sh.cnt[ej] + jbefore;
-    for (int b = b0; b < b1; ++b) {
-      const int hb = a.hist[(size_t)b * E + ej];
-      a.hist[(size_t)b * E + ej] = run;
-      run += hb;
+    for (int b = b0; b < b1; b += 8) {
+      int hb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hb[i] = (b + i < b1) ? a.hist[(size_t)(b + i) * E + ej] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b + i < b1) a.hist[(size_t)(b + i) * E + ej] = run;
+        run += hb[i];
+      }
     }
   }
   __syncthreads();
