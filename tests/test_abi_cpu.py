@@ -59,3 +59,14 @@ def test_status_strings_and_null_args(lib):
     assert lib.moe_layer_forward(None, 0, 1, None, None, None, None, None) == moe.MOE_E_INVALID
     assert lib.moe_cache_update(None, 0, None, None) == moe.MOE_E_INVALID
     lib.moe_plan_destroy(None)
+
+
+def test_config_struct_matches_header():
+    """The binding's moe_config mirror has the header's fields, in order and as int32."""
+    txt = open(os.path.join(ROOT, "include", "moe_offload.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} moe_config;", txt).group(1)
+    fields = re.findall(r"int32_t\s+(\w+)\s*;", body)
+    assert len(fields) == len(re.findall(r";", body)), "every moe_config field is an int32_t"
+    assert [n for n, _ in moe.Config._fields_] == fields
+    assert all(t is ctypes.c_int32 for _, t in moe.Config._fields_)
