@@ -585,11 +585,8 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   // (the token's k rows of h staged in LDS); K split over as many waves per slot
   // as still keep every workgroup resident in one round
   const bool fuse_narrow = fuse_small && !fuse_down && down_combine16_lds(k, I) <= kDownComb16MaxLds;
-  // Tiles of 8 rows when 16-row tiles would leave CUs idle
-  const int narrow_rows = (int64_t)(H / 16) * T < kDownComb16Min16RowTiles ? 8 : 16;
-  int narrow_splits = std::max(1, std::min(16 / k, (int)p->L.dn_chunks / (64 / narrow_rows)));
-  while (narrow_splits > 1 &&
-         (int64_t)(H / narrow_rows) * T > 256LL * (kDownComb16WavesPerCU / (k * narrow_splits)))
+  int narrow_splits = std::max(1, std::min(16 / k, (int)p->L.dn_chunks / 4));
+  while (narrow_splits > 1 && (int64_t)(H / 16) * T > 256LL * (kDownComb16WavesPerCU / (k * narrow_splits)))
     --narrow_splits;
   rt.aptr = (fuse_down || fuse_narrow) ? w.aptr : nullptr;
   if (prefill) {
@@ -747,7 +744,6 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       dc.k = k;
       dc.T = T;
       dc.splits = fuse_down ? down_splits : narrow_splits;
-      dc.rows = narrow_rows;
       KernelTimer kt(p, MOE_K_DOWN);
       if (fuse_down)
         launch_down_combine(dc, kt.tm, s);

@@ -114,21 +114,21 @@ __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __rest
 constexpr int kNarrowIt = 4;     // chunks per lane whose code loads are issued together
 constexpr int kNarrowStage = 8;  // h units (16 bytes) per thread staged from registers
 
-template <int CPG, int QS>
+template <int CPG>
 struct NarrowBatch {
   u32x4 wv[kNarrowIt];
   uint16_t sc[kNarrowIt];
   __device__ __forceinline__ void load(guint4* codes, gushort* scales, int cfirst, int c1) {
 #pragma unroll
     for (int i = 0; i < kNarrowIt; ++i) {
-      const int c = min(cfirst + QS * i, c1 - 1);
+      const int c = min(cfirst + 4 * i, c1 - 1);
       wv[i] = codes[(size_t)c * 64];
       sc[i] = scales[(size_t)(c / CPG) * 64];
     }
   }
 };
 
-template <int CPG, bool STAGE, int ROWS>
+template <int CPG, bool STAGE>
 __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __restrict__ aptr,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ wts, const void* __restrict__ h,
@@ -138,18 +138,17 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
   __shared__ float part[kMaxW][16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int QS = 64 / ROWS;  // chunk lanes per row: a wave covers ROWS rows x QS chunks
-  const int r = lane % ROWS, cl = lane / ROWS;
+  const int r = lane & 15, cl = lane >> 4;
   const int tile = blockIdx.x, t = blockIdx.y;
   const int j = wave / splits, sp = wave % splits;
   const uint8_t* base = aptr[t * k + j];
-  const int lane_off = (tile % QS) * ROWS + r;  // place of row r in its 64-row block
-  guint4* codes = (guint4*)(base + off_codes) + (size_t)(tile / QS) * chunks * 64 + lane_off;
-  gushort* scales = (gushort*)(base + off_scales) + (size_t)(tile / QS) * groups * 64 + lane_off;
+  const int lane_off = (tile & 3) * 16 + r;  // place of row r in its 64-row block
+  guint4* codes = (guint4*)(base + off_codes) + (size_t)(tile >> 2) * chunks * 64 + lane_off;
+  gushort* scales = (gushort*)(base + off_scales) + (size_t)(tile >> 2) * groups * 64 + lane_off;
   const int c0 = (chunks * sp) / splits, c1 = (chunks * (sp + 1)) / splits;
-  const int n_it = (c1 - c0 + QS - 1) / QS;  // chunk iterations of the wave (lanes past c1 count 0)
+  const int n_it = (c1 - c0 + 3) >> 2;  // chunk iterations of the wave (lanes past c1 count 0)
 
-  NarrowBatch<CPG, QS> cur;
+  NarrowBatch<CPG> cur;
   if (n_it > 0) cur.load(codes, scales, c0 + cl, c1);
 
   const uint4* hrow;
@@ -186,11 +185,11 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
   }
   float acc = 0.f;
   for (int ib = 0; ib < n_it; ib += kNarrowIt) {
-    NarrowBatch<CPG, QS> nxt;
-    if (ib + kNarrowIt < n_it) nxt.load(codes, scales, c0 + cl + QS * (ib + kNarrowIt), c1);
+    NarrowBatch<CPG> nxt;
+    if (ib + kNarrowIt < n_it) nxt.load(codes, scales, c0 + cl + 4 * (ib + kNarrowIt), c1);
 #pragma unroll
     for (int i = 0; i < kNarrowIt; ++i) {
-      const int c = c0 + cl + QS * (ib + i);
+      const int c = c0 + cl + 4 * (ib + i);
       const int cc = min(c, c1 - 1);
       uint32_t xw[16];
 #pragma unroll
@@ -207,40 +206,34 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
     }
     cur = nxt;
   }
-#pragma unroll
-  for (int off = ROWS; off < 64; off *= 2) acc += __shfl_xor(acc, off, 64);
-  if (lane < ROWS) part[wave][lane] = acc;
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 16) part[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0 && lane < ROWS) {
+  if (wave == 0 && lane < 16) {
     float yv = 0.f;
     for (int jj = 0; jj < k; ++jj) {
       float o = 0.f;
       for (int s2 = 0; s2 < splits; ++s2) o += part[jj * splits + s2][lane];
       yv = fmaf(wts[t * k + jj], o, yv);
     }
-    y[(size_t)t * H + tile * ROWS + lane] = yv;
+    y[(size_t)t * H + tile * 16 + lane] = yv;
   }
 }
 
 size_t down_combine16_lds(int k, int I) { return (size_t)k * I * 2 + (size_t)k * (I / 32) * 4; }
 
 void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t s) {
-  const dim3 grid(a.H / a.rows, a.T), block(64 * a.k * a.splits);
+  const dim3 grid(a.H / 16, a.T), block(64 * a.k * a.splits);
   const bool stage = a.I > 1024;
   const size_t lds = stage ? down_combine16_lds(a.k, a.I) : 0;
-#define DOWN_COMB16_R(C, R)                                                                                        \
-  if (stage)                                                                                                       \
-    launch_timed(k_down_comb16<C, true, R>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,     \
-                 a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);                          \
-  else                                                                                                             \
-    launch_timed(k_down_comb16<C, false, R>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,    \
+#define DOWN_COMB16(C)                                                                                               \
+  if (stage)                                                                                                         \
+    launch_timed(k_down_comb16<C, true>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,          \
+                 a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);                            \
+  else                                                                                                               \
+    launch_timed(k_down_comb16<C, false>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,         \
                  a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);
-#define DOWN_COMB16(C)         \
-  if (a.rows == 8) {           \
-    DOWN_COMB16_R(C, 8)        \
-  } else {                     \
-    DOWN_COMB16_R(C, 16)       \
-  }
   switch (a.G / 32) {
     case 1: DOWN_COMB16(1); break;
     case 2: DOWN_COMB16(2); break;
@@ -248,7 +241,6 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
     default: DOWN_COMB16(8); break;
   }
 #undef DOWN_COMB16
-#undef DOWN_COMB16_R
 }
 
 void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s) {

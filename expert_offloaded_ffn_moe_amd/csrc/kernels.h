@@ -110,7 +110,6 @@ struct DownCombArgs {
   int64_t off_codes, off_scales;
   int chunks, groups, G, H, I, k, T;
   int splits;                  // waves per slot (K split)
-  int rows;                    // 16-row form: rows of H per workgroup (8 or 16)
 };
 
 // Prefill staging of offloaded experts (see k_stage.hip).
@@ -157,7 +156,6 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
 size_t down_combine16_lds(int k, int I);  // dynamic LDS bytes of launch_down_combine16
 constexpr size_t kDownComb16MaxLds = 48 * 1024;
 constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count
-constexpr int kDownComb16Min16RowTiles = 256;  // fewer (H/16)*T workgroups: 8-row tiles
 void launch_stage(StageArgs a, const Timing& tm, hipStream_t s);
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
