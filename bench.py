@@ -424,9 +424,25 @@ def cpu_baseline(args, d, B, L, layers_host, xs_bits):
         i += 1
     el = time.perf_counter() - t0
     log("cpu oracle: %d forwards in %.1fs" % (i, el))
-    return {"value": round(tokens / el, 4), "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d forwards of batch %d over %d of the %d layers (float64 NumPy oracle, %.1fs)" % (
-                i, B, n_layers, L, el)}
+    out = {"value": round(tokens / el, 4), "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "%d forwards of batch %d over %d of the %d layers (float64 NumPy oracle, %.1fs)" % (
+               i, B, n_layers, L, el)}
+    # the same oracle pinned to one thread, on a shorter sample
+    try:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(limits=1):
+            tok1, t1, j = 0, time.perf_counter(), 0
+            while time.perf_counter() - t1 < args.cpu_seconds / 3:
+                l = j % n_layers
+                Wr, b, blobs = layers_host[l]["Wr"], layers_host[l]["b"], layers_host[l]["blobs"]
+                x = O.bf16_bits_to_f64(xs_bits[j % len(xs_bits)])
+                O.layer_forward(x, O.bf16_bits_to_f64(Wr), b, blobs, H, I, E, k, G, act)
+                tok1 += B
+                j += 1
+            out["value_one_thread"] = round(tok1 / (time.perf_counter() - t1), 4)
+    except Exception as e:  # the one-thread figure is extra; the baseline above stands without it
+        log("cpu oracle, one thread: skipped (%s)" % e)
+    return out
 
 
 if __name__ == "__main__":
