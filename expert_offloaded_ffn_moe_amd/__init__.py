@@ -26,8 +26,7 @@ class Config(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p), ("experts", ctypes.c_void_p),
-                ("resident", ctypes.c_void_p)]
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
 
 
 class Routing(ctypes.Structure):
@@ -45,7 +44,23 @@ class Stats(ctypes.Structure):
 
 
 class CachePolicy(ctypes.Structure):
-    _fields_ = [("decay", ctypes.c_double), ("max_promotions", ctypes.c_int32), ("overlap", ctypes.c_int32)]
+    _fields_ = [("decay", ctypes.c_double), ("max_promotions", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("want_resident", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_int32), ("gpu_numa_node", ctypes.c_int32), ("host_pool_node", ctypes.c_int32),
+                ("numa_bound", ctypes.c_int32), ("internal_expert_bytes", ctypes.c_int64),
+                ("host_pool_bytes", ctypes.c_int64), ("hbm_slot_bytes", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class LinkCeilings(ctypes.Structure):
+    _fields_ = [("hbm_read_gbps", ctypes.c_double), ("host_read_gbps", ctypes.c_double),
+                ("h2d_copy_gbps", ctypes.c_double)]
 
 
 KERNELS = ["router", "route", "gateup", "down", "combine", "gemm_gateup", "gemm_down", "stage"]
@@ -83,8 +98,12 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib = ctypes.CDLL(path)
     vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
     lib.moe_expert_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
-    lib.moe_plan_create.argtypes = [ctypes.POINTER(Config), vp, ctypes.POINTER(vp)]
-    lib.moe_plan_load_layer.argtypes = [vp, i32, ctypes.POINTER(LayerWeights), vp]
+    lib.moe_plan_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights), vp, vp, ctypes.POINTER(vp)]
+    lib.moe_plan_load_layer.argtypes = [vp, i32, ctypes.POINTER(LayerWeights), vp, vp]
+    lib.moe_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.moe_measure_link_ceilings.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i32, vp, ctypes.POINTER(LinkCeilings)]
+    lib.moe_debug_fail_alloc.argtypes = [i32, i32]
+    lib.moe_debug_live_allocs.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
     lib.moe_cache_update.argtypes = [vp, i32, ctypes.POINTER(CachePolicy), vp]
     lib.moe_plan_stats.argtypes = [vp, i32, ctypes.POINTER(Stats)]
@@ -99,7 +118,8 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_last_error.restype = ctypes.c_char_p
     for fn in ("moe_expert_bytes", "moe_plan_create", "moe_plan_load_layer", "moe_layer_forward",
                "moe_cache_update", "moe_plan_stats", "moe_plan_reset_stats", "moe_plan_residency",
-               "moe_plan_profile", "moe_plan_kernel_times"):
+               "moe_plan_profile", "moe_plan_kernel_times", "moe_plan_get_info", "moe_measure_link_ceilings",
+               "moe_debug_fail_alloc", "moe_debug_live_allocs"):
         getattr(lib, fn).restype = st
     _lib = lib
     return lib
@@ -128,6 +148,30 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def measure_link_ceilings(hbm_bytes=1 << 30, host_bytes=1 << 30, iters=5, stream=None) -> dict:
+    """Streaming-read GB/s over device memory and over pinned device-mapped host memory,
+    and host -> device copy GB/s (moe_measure_link_ceilings)."""
+    lib = load_library()
+    out = LinkCeilings()
+    _check(lib.moe_measure_link_ceilings(hbm_bytes, host_bytes, iters, _stream(stream), ctypes.byref(out)),
+           "moe_measure_link_ceilings")
+    return {n: float(getattr(out, n)) for n, _ in out._fields_}
+
+
+def debug_fail_alloc(kind: int, n: int):
+    """Test hook: the n-th next device (kind 0) or pinned host (kind 1) allocation fails."""
+    lib = load_library()
+    _check(lib.moe_debug_fail_alloc(kind, n), "moe_debug_fail_alloc")
+
+
+def debug_live_allocs():
+    """(device, pinned host) allocations the library currently holds."""
+    lib = load_library()
+    d, h = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.moe_debug_live_allocs(ctypes.byref(d), ctypes.byref(h)), "moe_debug_live_allocs")
+    return int(d.value), int(h.value)
+
+
 def make_config(H, I, E, k, G, act="bf16", num_layers=1, max_tokens=16, hbm_slots=None, gemm_min_tokens=0,
                 prefill_stage_slots=0):
     return Config(H, I, E, k, G, num_layers, ACT_BF16 if act == "bf16" else ACT_F32, max_tokens,
@@ -141,27 +185,47 @@ def expert_bytes(cfg: Config) -> int:
     return int(out.value)
 
 
-class Plan:
-    """A residency plan: pools, pointer tables and workspace of `cfg.num_layers` layers."""
+def _layer_weights(router_w, router_b, experts):
+    """(LayerWeights, the arrays it points into, kept alive by the caller)."""
+    rw = np.ascontiguousarray(router_w)
+    rb = None if router_b is None else np.ascontiguousarray(router_b, dtype=np.float32)
+    ex = np.ascontiguousarray(experts, dtype=np.uint8)
+    return LayerWeights(_ptr(rw), _ptr(rb), _ptr(ex)), (rw, rb, ex)
 
-    def __init__(self, cfg: Config, stream=None):
+
+class Plan:
+    """A residency plan: pools, pointer tables and workspace of `cfg.num_layers` layers.
+
+    layers: optional list of (router_w, router_b, experts) per layer, loaded at create;
+    initial_hbm: optional host [L, E] int (1 = the expert starts in an HBM slot)."""
+
+    def __init__(self, cfg: Config, layers=None, initial_hbm=None, stream=None):
         self.lib = load_library()
         self.cfg = cfg
         h = ctypes.c_void_p()
-        _check(self.lib.moe_plan_create(ctypes.byref(cfg), _stream(stream), ctypes.byref(h)), "moe_plan_create")
+        arr, keep, ih = None, [], None
+        if layers is not None:
+            assert len(layers) == cfg.num_layers
+            arr = (LayerWeights * len(layers))()
+            for i, (rw, rb, ex) in enumerate(layers):
+                arr[i], k = _layer_weights(rw, rb, ex)
+                keep.append(k)
+            if initial_hbm is not None:
+                ih = np.ascontiguousarray(initial_hbm, dtype=np.int32)
+                assert ih.shape == (cfg.num_layers, cfg.num_experts)
+        _check(self.lib.moe_plan_create(ctypes.byref(cfg), arr, _ptr(ih), _stream(stream), ctypes.byref(h)),
+               "moe_plan_create")
         self.handle = h
 
     def load_layer(self, layer, router_w: np.ndarray, router_b, experts: np.ndarray, resident=None, stream=None):
         """router_w: host [E, H] float32 (f32 plans) or uint16 bf16 bits (bf16 plans);
         router_b: host [E] float32 or None; experts: host uint8 [E, expert_bytes];
-        resident: host [E] int (1 = HBM slot) or None."""
-        rw = np.ascontiguousarray(router_w)
-        rb = None if router_b is None else np.ascontiguousarray(router_b, dtype=np.float32)
-        ex = np.ascontiguousarray(experts, dtype=np.uint8)
+        resident: host [E] int (1 = the expert starts in an HBM slot) or None."""
+        w, keep = _layer_weights(router_w, router_b, experts)
         res = None if resident is None else np.ascontiguousarray(resident, dtype=np.int32)
-        w = LayerWeights(_ptr(rw), _ptr(rb), _ptr(ex), _ptr(res))
-        _check(self.lib.moe_plan_load_layer(self.handle, layer, ctypes.byref(w), _stream(stream)),
+        _check(self.lib.moe_plan_load_layer(self.handle, layer, ctypes.byref(w), _ptr(res), _stream(stream)),
                "moe_plan_load_layer")
+        del keep
 
     def forward(self, layer, x, y, logits_in=None, route=None, stream=None):
         """x: cuda tensor [T, H] (float32 or bfloat16); y: cuda float32 [T, H];
@@ -175,12 +239,20 @@ class Plan:
                "moe_layer_forward")
         return y
 
-    def cache_update(self, layer=-1, decay=0.9, max_promotions=8, overlap=False, stream=None):
+    def cache_update(self, layer=-1, decay=0.9, max_promotions=8, overlap=False, want_resident=None, stream=None):
         """overlap=True: the pipelined update (decisions lag one update; copies on the
-        plan's copy stream, promoted experts switched to HBM by the next update)."""
-        pol = CachePolicy(decay, max_promotions, 1 if overlap else 0)
+        plan's copy stream, promoted experts switched to HBM by the next update).
+        want_resident: host [E] (one layer) or [L, E] (layer = -1) ints, the residency
+        set to move to instead of the frequency policy's choice."""
+        want = None if want_resident is None else np.ascontiguousarray(want_resident, dtype=np.int32)
+        pol = CachePolicy(decay, max_promotions, 1 if overlap else 0, _ptr(want))
         _check(self.lib.moe_cache_update(self.handle, layer, ctypes.byref(pol), _stream(stream)),
                "moe_cache_update")
+
+    def info(self) -> dict:
+        out = PlanInfo()
+        _check(self.lib.moe_plan_get_info(self.handle, ctypes.byref(out)), "moe_plan_get_info")
+        return out.as_dict()
 
     def stats(self, layer=-1) -> dict:
         s = Stats()

@@ -10,8 +10,14 @@
 // sections "显存缺口从哪里来" and "同一个思路，vLLM 原生方案反而跑不通").
 #include <hip/hip_runtime.h>
 
+#include <linux/mempolicy.h>
+#include <sys/syscall.h>
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -26,6 +32,18 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_last_error;
+
+// moe_debug_fail_alloc: countdown to the device (0) / pinned host (1) allocation that fails
+std::atomic<int> g_fail_alloc[2] = {{0}, {0}};
+// allocations currently held: device (0), pinned host (1)
+std::atomic<int64_t> g_live[2] = {{0}, {0}};
+
+bool injected_failure(int kind) {
+  int v = g_fail_alloc[kind].load();
+  while (v > 0)
+    if (g_fail_alloc[kind].compare_exchange_weak(v, v - 1)) return v == 1;
+  return false;
+}
 
 moe_status fail(moe_status s, const std::string& msg) {
   g_last_error = msg;
@@ -102,6 +120,9 @@ struct moe_plan {
   std::vector<hipEvent_t> spare;   // reusable events
   std::vector<void*> dev_allocs;   // freed with hipFree
   std::vector<void*> host_allocs;  // freed with hipHostFree
+  int debug_ws = 0;                // MOE_DEBUG_WORKSPACE: 1 = poison the float workspace at create, 2 = and per forward
+  int gpu_node = -1, pool_node = -1, numa_bound = 0;
+  int64_t host_pool_bytes = 0, hbm_slot_bytes = 0, workspace_bytes = 0, dev_bytes = 0;
   // Per-layer counters and pointer tables live in [layers][E] arrays, so that a
   // pipelined cache update moves all layers' counts and tables with one copy each.
   int64_t* d_counts_all = nullptr;
@@ -124,6 +145,7 @@ namespace {
 moe_status dev_alloc(moe_plan* p, void** out, size_t bytes) {
   *out = nullptr;
   if (bytes == 0) bytes = 256;
+  if (injected_failure(0)) return fail(MOE_E_NOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed (injected)");
   hipError_t e = hipMalloc(out, bytes);
   if (e != hipSuccess) {
     *out = nullptr;
@@ -131,12 +153,16 @@ moe_status dev_alloc(moe_plan* p, void** out, size_t bytes) {
     return fail(MOE_E_NOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
   }
   p->dev_allocs.push_back(*out);
+  ++g_live[0];
+  p->dev_bytes += (int64_t)bytes;
   return MOE_OK;
 }
 
 moe_status host_alloc(moe_plan* p, void** out, size_t bytes, unsigned flags) {
   *out = nullptr;
   if (bytes == 0) bytes = 256;
+  if (injected_failure(1))
+    return fail(MOE_E_HOST_NOMEM, "hipHostMalloc of " + std::to_string(bytes) + " bytes failed (injected)");
   hipError_t e = hipHostMalloc(out, bytes, flags);
   if (e != hipSuccess) {
     *out = nullptr;
@@ -145,6 +171,57 @@ moe_status host_alloc(moe_plan* p, void** out, size_t bytes, unsigned flags) {
                 "hipHostMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
   }
   p->host_allocs.push_back(*out);
+  ++g_live[1];
+  return MOE_OK;
+}
+
+// Host NUMA node closest to `device` (-1 if not reported). A failed query leaves
+// no error state behind for the caller's next HIP call.
+int gpu_numa_node(int device) {
+  int node = -1;
+  if (hipDeviceGetAttribute(&node, hipDeviceAttributeHostNumaId, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return node;
+}
+
+// NUMA node of the page at `addr` (-1 if the system does not say).
+int page_node(const void* addr) {
+  int node = -1;
+  if (syscall(SYS_get_mempolicy, &node, nullptr, 0, const_cast<void*>(addr), MPOL_F_NODE | MPOL_F_ADDR) != 0)
+    return -1;
+  return node;
+}
+
+// A host pool on the GPU's NUMA node (page "763B MoE 塞进两张 96GB 显卡：闲置专家丢进
+// 主机内存", section "PCIe 拓扑：容易被忽略的性能变量": host memory on a remote node
+// slowed the host link). When the device reports its closest node, the calling
+// thread's memory policy prefers that node while the pool is allocated and pinned
+// (hipHostMallocNumaUser makes HIP follow the thread's policy), and is restored after.
+moe_status host_alloc_numa(moe_plan* p, void** out, size_t bytes, unsigned flags) {
+  if (p->gpu_node < 0 || p->gpu_node >= 1024) return host_alloc(p, out, bytes, flags);
+  constexpr unsigned long kMaxNode = 1024 + 1;  // bits of the masks below, plus one (the kernel's convention)
+  unsigned long old_mask[16] = {0}, mask[16] = {0};
+  int old_mode = MPOL_DEFAULT;
+  if (syscall(SYS_get_mempolicy, &old_mode, old_mask, kMaxNode, nullptr, 0) != 0)
+    return host_alloc(p, out, bytes, flags);
+  mask[p->gpu_node / 64] = 1ul << (p->gpu_node % 64);
+  if (syscall(SYS_set_mempolicy, MPOL_PREFERRED, mask, kMaxNode) != 0) return host_alloc(p, out, bytes, flags);
+  void* q = nullptr;
+  const bool injected = injected_failure(1);
+  hipError_t e = injected ? hipErrorOutOfMemory : hipHostMalloc(&q, bytes, flags | hipHostMallocNumaUser);
+  (void)syscall(SYS_set_mempolicy, old_mode, old_mode == MPOL_DEFAULT ? nullptr : old_mask, kMaxNode);
+  if (injected)
+    return fail(MOE_E_HOST_NOMEM, "hipHostMalloc of " + std::to_string(bytes) + " bytes failed (injected)");
+  if (e != hipSuccess) {  // this allocation path refused: the plain one decides
+    (void)hipGetLastError();
+    return host_alloc(p, out, bytes, flags);
+  }
+  p->host_allocs.push_back(q);
+  ++g_live[1];
+  *out = q;
+  p->numa_bound = 1;
   return MOE_OK;
 }
 
@@ -162,6 +239,8 @@ void free_plan(moe_plan* p) {
   if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
   for (void* q : p->dev_allocs) (void)hipFree(q);
   for (void* q : p->host_allocs) (void)hipHostFree(q);
+  g_live[0] -= (int64_t)p->dev_allocs.size();
+  g_live[1] -= (int64_t)p->host_allocs.size();
   delete p;
 }
 
@@ -308,6 +387,120 @@ moe_status cache_update_pipelined(moe_plan* p, int l0, int l1, double decay, int
   return MOE_OK;
 }
 
+// Arguments of one layer's weights: router and experts given, initial HBM set within the slots.
+moe_status check_layer_args(const moe_config& c, const moe_layer_weights* w, const int32_t* initial_hbm) {
+  if (!w || !w->router_w || !w->experts) return fail(MOE_E_INVALID, "router_w and experts are required");
+  if (initial_hbm) {
+    int n = 0;
+    for (int e = 0; e < c.num_experts; ++e) n += initial_hbm[e] != 0;
+    if (n > c.hbm_slots) return fail(MOE_E_INVALID, "more initially resident experts than hbm_slots");
+  }
+  return MOE_OK;
+}
+
+// Debug mode: the float workspace buffers (logits, group sums, h, its chunk sums, o)
+// filled with a pattern that is a quiet NaN both as fp32 and as each of its bf16
+// halves, so that a kernel reading values no launch of the current forward wrote
+// turns the output into NaN. The index buffers are never filled.
+void poison_workspace(moe_plan* p, hipStream_t s) {
+  const moe_config& c = p->cfg;
+  const size_t Tm = (size_t)c.max_tokens, A = Tm * c.top_k;
+  const uint32_t nan2 = 0x7FC07FC0u;
+  Workspace& w = p->ws;
+  launch_fill32(w.logits, nan2, Tm * c.num_experts, s);
+  launch_fill32(w.xsum, nan2, Tm * (c.hidden / c.group_size), s);
+  launch_fill32(w.h, nan2, A * c.inter * p->act_size / 4, s);
+  launch_fill32(w.hpart, nan2, A * (c.inter / 32), s);
+  launch_fill32(w.o, nan2, A * c.hidden, s);
+}
+
+moe_status load_layer_impl(moe_plan* p, int layer, const moe_layer_weights* w, const int32_t* initial_hbm,
+                           hipStream_t s) {
+  const int E = p->cfg.num_experts, H = p->cfg.hidden, S = p->cfg.hbm_slots;
+  Layer& ly = p->layers[layer];
+  std::vector<int32_t> slot_of(E, -1);
+  int used = 0;
+  for (int e = 0; e < E; ++e)
+    if (initial_hbm ? (initial_hbm[e] != 0) : (e < S)) slot_of[e] = used++;
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipStreamSynchronize(s));  // no queued work may still read this layer
+  {
+    moe_status st = settle_pipelined(p, layer, layer + 1);  // nor copy into it
+    if (st != MOE_OK) return st;
+    p->counts_staged[0][layer] = p->counts_staged[1][layer] = 0;
+  }
+
+  // repack every expert into the host pool, threads over experts
+  const Layout L = p->L;
+  const size_t cb = (size_t)L.canonical_bytes;
+  unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nth; ++t)
+    th.emplace_back([&, t] {
+      for (int e = (int)t; e < E; e += (int)nth)
+        repack_expert(L, w->experts + (size_t)e * cb, ly.host_pool + (size_t)e * L.bytes);
+    });
+  for (auto& x : th) x.join();
+
+  for (int e = 0; e < E; ++e)
+    if (slot_of[e] >= 0)
+      HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)slot_of[e] * L.bytes, ly.host_pool + (size_t)e * L.bytes, L.bytes,
+                             hipMemcpyHostToDevice, s));
+  ly.slot_of = slot_of;
+  ly.score.assign(E, 0.0);
+  {
+    moe_status st = push_tables(p, ly, s);
+    if (st != MOE_OK) return st;
+  }
+  HIP_TRY(hipMemcpyAsync(ly.d_router_w, w->router_w, (size_t)E * H * p->act_size, hipMemcpyHostToDevice, s));
+  if (w->router_b)
+    HIP_TRY(hipMemcpyAsync(ly.d_router_b, w->router_b, sizeof(float) * E, hipMemcpyHostToDevice, s));
+  else
+    HIP_TRY(hipMemsetAsync(ly.d_router_b, 0, sizeof(float) * E, s));
+  HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
+  HIP_TRY(hipMemsetAsync(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  ly.bytes_copied = ly.promotions = ly.evictions = 0;
+  ly.loaded = true;
+  return MOE_OK;
+}
+
+
+// Workspace buffers of a forward. Every launch of moe_layer_forward names the
+// buffers it reads and writes; a read of a buffer that no earlier launch of the
+// same forward wrote would take whatever an earlier forward (or the allocator's
+// previous owner of the memory) left there, so the dispatch refuses to enqueue it.
+// A launch that writes a buffer and reads it back itself (the routing kernels'
+// last blocks reading the logits their router blocks wrote) lists it as written.
+// Partial writes are documented at the kernels: a writer covers the range its
+// readers use (the GEMV work slots up to min(E, T*k), act_pos where counts > 0).
+enum : uint32_t {
+  WB_LOGITS = 1u << 0, WB_XSUM = 1u << 1, WB_IDS = 1u << 2, WB_WTS = 1u << 3, WB_COUNTS = 1u << 4,
+  WB_OFFSETS = 1u << 5, WB_SORTED = 1u << 6, WB_INV = 1u << 7, WB_ACTIVE = 1u << 8, WB_NACTIVE = 1u << 9,
+  WB_H = 1u << 10, WB_HPART = 1u << 11, WB_O = 1u << 12, WB_TILES = 1u << 13, WB_NTILES = 1u << 14,
+  WB_WORK = 1u << 15, WB_APTR = 1u << 16, WB_HIST = 1u << 17, WB_ACTPOS = 1u << 18, WB_STAGE = 1u << 19,
+  WB_GPTR = 1u << 20, WB_COUNT_ = 21
+};
+
+const char* const kWbNames[WB_COUNT_] = {"logits", "xsum",   "ids",   "wts",     "counts", "offsets", "sorted",
+                                         "inv",    "active", "n_active", "h",     "hpart",  "o",       "tiles",
+                                         "n_tiles", "work",  "aptr",  "hist",    "act_pos", "stage",  "gptr"};
+
+struct WsTrack {
+  uint32_t written = 0;
+  std::string err;
+  bool launch(const char* kernel, uint32_t reads, uint32_t writes) {
+    const uint32_t missing = reads & ~written;
+    written |= writes;
+    if (!missing) return true;
+    err = std::string(kernel) + " reads";
+    for (int b = 0; b < WB_COUNT_; ++b)
+      if (missing & (1u << b)) err += std::string(" ") + kWbNames[b];
+    err += " before this forward writes it";
+    return false;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -335,13 +528,20 @@ moe_status moe_expert_bytes(const moe_config* cfg, size_t* out) {
   return MOE_OK;
 }
 
-moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** out) {
+moe_status moe_plan_create(const moe_config* cfg, const moe_layer_weights* layers, const int32_t* initial_hbm,
+                           moe_stream stream, moe_plan** out) {
   if (!out) return fail(MOE_E_INVALID, "out is null");
   *out = nullptr;
   if (!cfg) return fail(MOE_E_INVALID, "cfg is null");
   const std::string why = check_config(*cfg);
   if (!why.empty()) return fail(MOE_E_INVALID, why);
-  (void)stream;
+  if (layers) {
+    for (int l = 0; l < cfg->num_layers; ++l) {
+      moe_status st = check_layer_args(*cfg, &layers[l], initial_hbm ? initial_hbm + (size_t)l * cfg->num_experts
+                                                                     : nullptr);
+      if (st != MOE_OK) return st;
+    }
+  }
 
   moe_plan* p = new moe_plan();
   p->cfg = *cfg;
@@ -351,6 +551,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   if (hipGetDevice(&p->device) != hipSuccess) {
     delete p;
     return fail(MOE_E_HIP, "hipGetDevice failed");
+  }
+  p->gpu_node = gpu_numa_node(p->device);
+  {
+    const char* dbg = std::getenv("MOE_DEBUG_WORKSPACE");
+    p->debug_ws = dbg ? std::atoi(dbg) : 0;
   }
   const int E = cfg->num_experts, H = cfg->hidden, I = cfg->inter, k = cfg->top_k, G = cfg->group_size;
   const size_t Tm = (size_t)cfg->max_tokens, A = Tm * k;
@@ -393,8 +598,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
   for (size_t li = 0; li < p->layers.size(); ++li) {
     Layer& ly = p->layers[li];
     void* v;
-    TRY(host_alloc(p, &v, (size_t)E * p->L.bytes, hipHostMallocMapped | hipHostMallocNonCoherent));
+    TRY(host_alloc_numa(p, &v, (size_t)E * p->L.bytes, hipHostMallocMapped | hipHostMallocNonCoherent));
     ly.host_pool = static_cast<uint8_t*>(v);
+    p->host_pool_bytes += (int64_t)E * p->L.bytes;
     void* dv = nullptr;
     if (hipHostGetDevicePointer(&dv, ly.host_pool, 0) != hipSuccess) {
       free_plan(p);
@@ -404,6 +610,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
     if (cfg->hbm_slots > 0) {
       TRY(dev_alloc(p, &v, (size_t)cfg->hbm_slots * p->L.bytes));
       ly.hbm = static_cast<uint8_t*>(v);
+      p->hbm_slot_bytes += (int64_t)cfg->hbm_slots * p->L.bytes;
     }
     ly.d_wptr = p->d_wptr_all + li * E;
     ly.d_is_host = p->d_ishost_all + li * E;
@@ -421,6 +628,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
     ly.score.assign(E, 0.0);
   }
   Workspace& w = p->ws;
+  const int64_t dev_before_ws = p->dev_bytes;
   TRY(alloc_as(p, &w.logits, Tm * E));
   TRY(alloc_as(p, &w.xsum, Tm * (H / G)));
   TRY(alloc_as(p, &w.ids, A));
@@ -447,77 +655,48 @@ moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** 
     w.stage = static_cast<uint8_t*>(v);
     TRY(alloc_as(p, &w.gptr, E));
   }
-#undef TRY
+  p->workspace_bytes = p->dev_bytes - dev_before_ws;
   if (hipMemset(w.route_cnt, 0, 64 * sizeof(unsigned)) != hipSuccess) {
     free_plan(p);
     return fail(MOE_E_HIP, "clearing arrival counters failed");
   }
+  if (p->debug_ws > 0) poison_workspace(p, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     free_plan(p);
     return fail(MOE_E_HIP, "device synchronize after allocation failed");
   }
+  p->pool_node = page_node(p->layers[0].host_pool);
+  if (layers)
+    for (int l = 0; l < cfg->num_layers; ++l)
+      TRY(load_layer_impl(p, l, &layers[l], initial_hbm ? initial_hbm + (size_t)l * E : nullptr,
+                          static_cast<hipStream_t>(stream)));
+#undef TRY
   *out = p;
   return MOE_OK;
 }
 
-moe_status moe_plan_load_layer(moe_plan* p, int32_t layer, const moe_layer_weights* w, moe_stream stream) {
+moe_status moe_plan_load_layer(moe_plan* p, int32_t layer, const moe_layer_weights* w, const int32_t* initial_hbm,
+                               moe_stream stream) {
   if (!p || !w) return fail(MOE_E_INVALID, "null argument");
   if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
-  if (!w->router_w || !w->experts) return fail(MOE_E_INVALID, "router_w and experts are required");
-  const int E = p->cfg.num_experts, H = p->cfg.hidden, S = p->cfg.hbm_slots;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Layer& ly = p->layers[layer];
-
-  std::vector<int32_t> slot_of(E, -1);
-  int used = 0;
-  for (int e = 0; e < E; ++e) {
-    const bool res = w->resident ? (w->resident[e] != 0) : (e < S);
-    if (res) {
-      if (used >= S) return fail(MOE_E_INVALID, "more resident experts than hbm_slots");
-      slot_of[e] = used++;
-    }
-  }
-  HIP_TRY(hipSetDevice(p->device));
-  HIP_TRY(hipStreamSynchronize(s));  // no queued work may still read this layer
-  {
-    moe_status st = settle_pipelined(p, layer, layer + 1);  // nor copy into it
-    if (st != MOE_OK) return st;
-    p->counts_staged[0][layer] = p->counts_staged[1][layer] = 0;
-  }
-
-  // repack every expert into the host pool, threads over experts
-  const Layout L = p->L;
-  const size_t cb = (size_t)L.canonical_bytes;
-  unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-  std::vector<std::thread> th;
-  for (unsigned t = 0; t < nth; ++t)
-    th.emplace_back([&, t] {
-      for (int e = (int)t; e < E; e += (int)nth)
-        repack_expert(L, w->experts + (size_t)e * cb, ly.host_pool + (size_t)e * L.bytes);
-    });
-  for (auto& x : th) x.join();
-
-  for (int e = 0; e < E; ++e)
-    if (slot_of[e] >= 0)
-      HIP_TRY(hipMemcpyAsync(ly.hbm + (size_t)slot_of[e] * L.bytes, ly.host_pool + (size_t)e * L.bytes, L.bytes,
-                             hipMemcpyHostToDevice, s));
-  ly.slot_of = slot_of;
-  ly.score.assign(E, 0.0);
-  moe_status st = push_tables(p, ly, s);
+  moe_status st = check_layer_args(p->cfg, w, initial_hbm);
   if (st != MOE_OK) return st;
-  HIP_TRY(hipMemcpyAsync(ly.d_router_w, w->router_w, (size_t)E * H * p->act_size, hipMemcpyHostToDevice, s));
-  if (w->router_b)
-    HIP_TRY(hipMemcpyAsync(ly.d_router_b, w->router_b, sizeof(float) * E, hipMemcpyHostToDevice, s));
-  else
-    HIP_TRY(hipMemsetAsync(ly.d_router_b, 0, sizeof(float) * E, s));
-  HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
-  HIP_TRY(hipMemsetAsync(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT, s));
-  HIP_TRY(hipStreamSynchronize(s));
-  ly.bytes_copied = ly.promotions = ly.evictions = 0;
-  ly.loaded = true;
-  return MOE_OK;
+  return load_layer_impl(p, layer, w, initial_hbm, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_plan_get_info(moe_plan* p, moe_plan_info* out) {
+  if (!p || !out) return fail(MOE_E_INVALID, "null argument");
+  std::memset(out, 0, sizeof(*out));
+  out->device = p->device;
+  out->gpu_numa_node = p->gpu_node;
+  out->host_pool_node = p->pool_node;
+  out->numa_bound = p->numa_bound;
+  out->internal_expert_bytes = p->L.bytes;
+  out->host_pool_bytes = p->host_pool_bytes;
+  out->hbm_slot_bytes = p->hbm_slot_bytes;
+  out->workspace_bytes = p->workspace_bytes;
+  return MOE_OK;
+}
 moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
                              const moe_routing* ro, moe_stream stream) {
   if (!p) return fail(MOE_E_INVALID, "plan is null");
@@ -535,6 +714,10 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace& w = p->ws;
   const int A = T * k;
+  if (p->debug_ws >= 2) poison_workspace(p, s);
+  WsTrack trk;
+#define LAUNCH_USES(kernel, reads, writes) \
+  if (!trk.launch(kernel, reads, writes)) return fail(MOE_E_STATE, "internal dispatch error: " + trk.err)
 
   RouterArgs ra{};
   ra.x = x;
@@ -594,12 +777,18 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       RouterArgs rp = ra;  // logits only: the GEMMs take no group sums
       rp.router_blocks = 1;
       rp.xsum = nullptr;
-      KernelTimer kt(p, MOE_K_ROUTER);
-      if (!logits_in) launch_router_mfma(rp, kt.tm, s);
+      if (!logits_in) {
+        LAUNCH_USES("k_router_mfma", 0, WB_LOGITS);
+        KernelTimer kt(p, MOE_K_ROUTER);
+        launch_router_mfma(rp, kt.tm, s);
+      }
     }
     rt.tiles = w.tiles;
     rt.n_tiles = w.n_tiles;
     {
+      LAUNCH_USES("k_topk_count + k_scatter", logits_in ? 0 : WB_LOGITS,
+                  WB_IDS | WB_WTS | WB_COUNTS | WB_OFFSETS | WB_SORTED | WB_INV | WB_ACTIVE | WB_NACTIVE | WB_HIST |
+                      WB_ACTPOS | WB_TILES | WB_NTILES);
       KernelTimer kt(p, MOE_K_ROUTE);
       launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
     }
@@ -619,6 +808,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       sa.bytes = p->L.bytes;
       sa.E = E;
       sa.n_slots = c.prefill_stage_slots;
+      LAUNCH_USES("k_stage", WB_COUNTS | WB_ACTPOS | WB_ACTIVE | WB_NACTIVE, WB_STAGE | WB_GPTR);
       KernelTimer kt(p, MOE_K_STAGE);
       launch_stage(sa, kt.tm, s);
       gemm_wptr = w.gptr;
@@ -641,7 +831,9 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     gg.k = k;
     gg.G = G;
     gg.max_tiles = A / kGemmRows + std::min(E, A);
+    const uint32_t staged = gemm_wptr == w.gptr ? WB_GPTR | WB_STAGE : 0;
     {
+      LAUNCH_USES("k_gemm gate/up", staged | WB_TILES | WB_NTILES | WB_OFFSETS | WB_SORTED, WB_H);
       KernelTimer kt(p, MOE_K_GEMM_GATEUP);
       launch_gemm_gateup(gg, kt.tm, s);
     }
@@ -656,6 +848,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     gd.K = I;
     gd.out_ld = H;
     {
+      LAUNCH_USES("k_gemm down", staged | WB_TILES | WB_NTILES | WB_OFFSETS | WB_H, WB_O);
       KernelTimer kt(p, MOE_K_GEMM_DOWN);
       launch_gemm_down(gd, kt.tm, s);
     }
@@ -668,6 +861,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     ca.H = H;
     ca.k = k;
     {
+      LAUNCH_USES("k_combine", WB_O | WB_WTS | WB_INV, 0);
       KernelTimer kt(p, MOE_K_COMBINE);
       launch_combine(ca, kt.tm, s);
     }
@@ -675,10 +869,14 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
   } else if (decode) {
     // router + group sums + top-k + grouping in one launch (8 expert rows per block)
     ra.router_blocks = logits_in ? 0 : (E + 7) / 8;
+    LAUNCH_USES("k_route_decode", 0,
+                (logits_in ? 0 : WB_LOGITS) | (bf16 ? WB_XSUM : 0) | WB_IDS | WB_WTS | WB_COUNTS | WB_OFFSETS |
+                    WB_SORTED | WB_INV | WB_ACTIVE | WB_NACTIVE | WB_WORK | (rt.aptr ? WB_APTR : 0));
     KernelTimer kt(p, MOE_K_ROUTE);
     launch_route_decode(rt, ra, bf16, w.route_cnt, kt.tm, s);
   } else {
     {
+      LAUNCH_USES(bf16 ? "k_router_mfma" : "k_router", 0, (logits_in ? 0 : WB_LOGITS) | (bf16 ? WB_XSUM : 0));
       KernelTimer kt(p, MOE_K_ROUTER);
       if (bf16) {  // MFMA logits tiles (unless given) and the group sums, one launch
         ra.router_blocks = logits_in ? 0 : 1;
@@ -688,6 +886,9 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
         launch_router(ra, bf16, kt.tm, s);
       }
     }
+    LAUNCH_USES("k_topk_count + k_scatter", logits_in ? 0 : WB_LOGITS,
+                WB_IDS | WB_WTS | WB_COUNTS | WB_OFFSETS | WB_SORTED | WB_INV | WB_ACTIVE | WB_NACTIVE | WB_HIST |
+                    WB_ACTPOS | WB_WORK);
     KernelTimer kt(p, MOE_K_ROUTE);
     launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
   }
@@ -712,6 +913,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     ga.k = k;
     ga.T = T;
     {
+      LAUNCH_USES("k_gateup", WB_WORK | WB_SORTED | (bf16 ? WB_XSUM : 0), WB_H | (bf16 ? WB_HPART : 0));
       KernelTimer kt(p, MOE_K_GATEUP);
       launch_gateup(ga, bf16, std::min(T, 8), max_act * ga.tiles, kt.tm, s);
     }
@@ -744,6 +946,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       dc.k = k;
       dc.T = T;
       dc.splits = fuse_down ? down_splits : narrow_splits;
+      LAUNCH_USES(fuse_down ? "k_down_comb" : "k_down_comb16", WB_APTR | WB_INV | WB_WTS | WB_H | WB_HPART, 0);
       KernelTimer kt(p, MOE_K_DOWN);
       if (fuse_down)
         launch_down_combine(dc, kt.tm, s);
@@ -751,6 +954,7 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
         launch_down_combine16(dc, kt.tm, s);
     } else {
       {
+        LAUNCH_USES("k_down", WB_WORK | WB_H | (bf16 ? WB_HPART : 0), WB_O);
         KernelTimer kt(p, MOE_K_DOWN);
         launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);
       }
@@ -762,11 +966,13 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
       ca.T = T;
       ca.H = H;
       ca.k = k;
+      LAUNCH_USES("k_combine", WB_O | WB_WTS | WB_INV, 0);
       KernelTimer kt(p, MOE_K_COMBINE);
       launch_combine(ca, kt.tm, s);
     }
     HIP_TRY(hipGetLastError());
   }
+#undef LAUNCH_USES
 
   if (ro) {
     if (ro->logits) HIP_TRY(hipMemcpyAsync(ro->logits, logits, sizeof(float) * T * E, hipMemcpyDeviceToDevice, s));
@@ -792,9 +998,16 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
   for (int l = l0; l < l1; ++l)
     if (!p->layers[l].loaded) return fail(MOE_E_INVALID, "layer not loaded");
   const int E = p->cfg.num_experts;
+  const int32_t* want = pol ? pol->want_resident : nullptr;
+  if (want)
+    for (int l = l0; l < l1; ++l) {
+      int n = 0;
+      for (int e = 0; e < E; ++e) n += want[(size_t)(l - l0) * E + e] != 0;
+      if (n > p->cfg.hbm_slots) return fail(MOE_E_INVALID, "want_resident names more experts than hbm_slots");
+    }
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(p->device));
-  if (pol && pol->overlap) return cache_update_pipelined(p, l0, l1, decay, maxp, s);
+  if (pol && pol->overlap && !want) return cache_update_pipelined(p, l0, l1, decay, maxp, s);
   for (int l = l0; l < l1; ++l) {
     Layer& ly = p->layers[l];
     HIP_TRY(hipMemcpyAsync(ly.h_counts_stage, ly.d_counts_acc, sizeof(int64_t) * E, hipMemcpyDeviceToHost, s));
@@ -818,8 +1031,18 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
   std::vector<int32_t> evicted;
   for (int l = l0; l < l1; ++l) {
     Layer& ly = p->layers[l];
-    cache_policy_step(E, p->cfg.hbm_slots, decay, maxp, ly.h_counts_stage, ly.score.data(), ly.slot_of.data(),
-                      &promoted, &evicted);
+    if (want)
+      cache_set_resident(E, p->cfg.hbm_slots, decay, ly.h_counts_stage, want + (size_t)(l - l0) * E, ly.score.data(),
+                         ly.slot_of.data(), &promoted, &evicted);
+    else
+      cache_policy_step(E, p->cfg.hbm_slots, decay, maxp, ly.h_counts_stage, ly.score.data(), ly.slot_of.data(),
+                        &promoted, &evicted);
+    if (promoted.empty() && !evicted.empty()) {  // evictions only: the table still changes
+      ly.evictions += (int64_t)evicted.size();
+      moe_status st = push_tables(p, ly, s);
+      if (st != MOE_OK) return st;
+      continue;
+    }
     if (promoted.empty()) {
       if (settled[l]) {
         moe_status st = push_tables(p, ly, s);
@@ -912,6 +1135,80 @@ moe_status moe_plan_kernel_times(moe_plan* p, moe_kernel_times* out) {
       out->total_ms[r.kind] += ms;
     }
   }
+  return MOE_OK;
+}
+
+moe_status moe_measure_link_ceilings(size_t hbm_bytes, size_t host_bytes, int32_t iters, moe_stream stream,
+                                     moe_link_ceilings* out) {
+  if (!out) return fail(MOE_E_INVALID, "out is null");
+  std::memset(out, 0, sizeof(*out));
+  if (hbm_bytes < (1u << 20) || host_bytes < (1u << 20) || hbm_bytes % 4096 || host_bytes % 4096 || iters < 1)
+    return fail(MOE_E_INVALID, "sizes must be >= 1 MiB and multiples of 4 KiB, iters >= 1");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // a plan-less holder for the buffers, freed on every exit
+  moe_plan tmp;
+  if (hipGetDevice(&tmp.device) != hipSuccess) return fail(MOE_E_HIP, "hipGetDevice failed");
+  tmp.gpu_node = gpu_numa_node(tmp.device);
+  struct Release {
+    moe_plan* p;
+    ~Release() {
+      (void)hipDeviceSynchronize();
+      for (void* q : p->dev_allocs) (void)hipFree(q);
+      for (void* q : p->host_allocs) (void)hipHostFree(q);
+      g_live[0] -= (int64_t)p->dev_allocs.size();
+      g_live[1] -= (int64_t)p->host_allocs.size();
+    }
+  } release{&tmp};
+  void *dbuf = nullptr, *hbuf = nullptr, *hdst = nullptr, *sink = nullptr, *hdev = nullptr;
+  moe_status st = dev_alloc(&tmp, &dbuf, hbm_bytes);
+  if (st == MOE_OK) st = dev_alloc(&tmp, &hdst, host_bytes);
+  if (st == MOE_OK) st = dev_alloc(&tmp, &sink, sizeof(uint32_t) * stream_read_blocks());
+  if (st == MOE_OK) st = host_alloc_numa(&tmp, &hbuf, host_bytes, hipHostMallocMapped | hipHostMallocNonCoherent);
+  if (st != MOE_OK) return st;
+  HIP_TRY(hipHostGetDevicePointer(&hdev, hbuf, 0));
+  std::memset(hbuf, 0, host_bytes);
+  HIP_TRY(hipMemsetAsync(dbuf, 0, hbm_bytes, s));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  auto best_gbps = [&](auto&& run, size_t bytes, double* outv) -> moe_status {
+    double best = 0.0;
+    for (int i = 0; i <= iters; ++i) {  // run 0 is untimed
+      HIP_TRY(hipEventRecord(e0, s));
+      run();
+      HIP_TRY(hipEventRecord(e1, s));
+      HIP_TRY(hipEventSynchronize(e1));
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+      if (i > 0 && ms > 0.f) best = std::max(best, (double)bytes / (ms * 1e-3) / 1e9);
+    }
+    *outv = best;
+    return MOE_OK;
+  };
+  uint32_t* sk = static_cast<uint32_t*>(sink);
+  st = best_gbps([&] { launch_stream_read(dbuf, hbm_bytes, sk, s); }, hbm_bytes, &out->hbm_read_gbps);
+  if (st == MOE_OK)
+    st = best_gbps([&] { launch_stream_read(hdev, host_bytes, sk, s); }, host_bytes, &out->host_read_gbps);
+  if (st == MOE_OK)
+    st = best_gbps([&] { (void)hipMemcpyAsync(hdst, hbuf, host_bytes, hipMemcpyHostToDevice, s); }, host_bytes,
+                   &out->h2d_copy_gbps);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != MOE_OK) return st;
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status moe_debug_fail_alloc(int32_t kind, int32_t n) {
+  if (kind < 0 || kind > 1 || n < 0) return fail(MOE_E_INVALID, "kind must be 0 or 1 and n >= 0");
+  g_fail_alloc[kind].store(n);
+  return MOE_OK;
+}
+
+moe_status moe_debug_live_allocs(int64_t* device, int64_t* host) {
+  if (!device || !host) return fail(MOE_E_INVALID, "null argument");
+  *device = g_live[0].load();
+  *host = g_live[1].load();
   return MOE_OK;
 }
 

@@ -177,4 +177,34 @@ void cache_policy_step(int32_t E, int32_t n_slots, double decay, int32_t max_pro
   }
 }
 
+bool cache_set_resident(int32_t E, int32_t n_slots, double decay, const int64_t* counts, const int32_t* want,
+                        double* score, int32_t* slot_of, std::vector<Promotion>* promoted,
+                        std::vector<int32_t>* evicted) {
+  promoted->clear();
+  evicted->clear();
+  int32_t n_want = 0;
+  for (int32_t e = 0; e < E; ++e) n_want += want[e] != 0;
+  if (n_want > n_slots) return false;
+  for (int32_t e = 0; e < E; ++e) score[e] = decay * score[e] + (double)counts[e];
+  std::vector<char> used(n_slots > 0 ? n_slots : 0, 0);
+  for (int32_t e = 0; e < E; ++e) {
+    if (slot_of[e] < 0) continue;
+    if (want[e]) {
+      used[slot_of[e]] = 1;
+    } else {
+      slot_of[e] = -1;
+      evicted->push_back(e);
+    }
+  }
+  int32_t next_free = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    if (!want[e] || slot_of[e] >= 0) continue;
+    while (used[next_free]) ++next_free;  // a free slot exists: n_want <= n_slots
+    used[next_free] = 1;
+    slot_of[e] = next_free;
+    promoted->push_back({e, next_free});
+  }
+  return true;
+}
+
 }  // namespace moe

@@ -57,4 +57,13 @@ void cache_policy_step(int32_t E, int32_t n_slots, double decay, int32_t max_pro
                        const int64_t* counts, double* score, int32_t* slot_of,
                        std::vector<Promotion>* promoted, std::vector<int32_t>* evicted);
 
+// An update to a residency set the caller chose (want[e] != 0: read from HBM).
+//   score[e] <- decay * score[e] + counts[e] (as in cache_policy_step)
+//   evictions: residents not wanted, ascending id; their slots become free
+//   promotions: wanted non-residents, ascending id, each into the lowest free slot
+// Returns false (nothing changed) when more than n_slots experts are wanted.
+bool cache_set_resident(int32_t E, int32_t n_slots, double decay, const int64_t* counts, const int32_t* want,
+                        double* score, int32_t* slot_of, std::vector<Promotion>* promoted,
+                        std::vector<int32_t>* evicted);
+
 }  // namespace moe

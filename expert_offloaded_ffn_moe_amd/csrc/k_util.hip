@@ -1,0 +1,49 @@
+// Small utility kernels: a 32-bit fill (the workspace poison of the debug mode)
+// and the streaming-read probe behind moe_measure_link_ceilings.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_fill32(uint32_t* __restrict__ p, uint32_t v, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+void launch_fill32(void* p, uint32_t v, size_t n_words, hipStream_t s) {
+  if (n_words == 0) return;
+  const size_t blocks = std::min<size_t>((n_words + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_fill32, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), v, n_words);
+}
+
+// Reads n16 16-byte units once each: a thread takes units i, i + S, i + 2S, ...
+// (S = all threads of the grid), four loads in flight, and folds them with XOR so
+// that none is dead; a thread stores its fold only if it is all ones (never for
+// the zero-filled probe buffers), which keeps the loads live at no store cost.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, size_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  gu32x4* p = (gu32x4*)src;
+  const size_t S = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * S < n16; i += 4 * S) {
+    const u32x4 a = p[i], b = p[i + S], c = p[i + 2 * S], d = p[i + 3 * S];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += S) acc ^= p[i];
+  const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (v == 0xFFFFFFFFu) sink[blockIdx.x] = v;
+}
+
+int stream_read_blocks() { return 2048; }
+
+void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_read, dim3(stream_read_blocks()), dim3(256), 0, s, static_cast<const u32x4*>(src),
+                     bytes / 16, sink);
+}
+
+}  // namespace moe

@@ -167,5 +167,10 @@ constexpr int kGemmRows = 64;  // token rows per prefill GEMM tile
 // and H7168/E384 layers: equal at 5-6 tokens, the GEMM 13% ahead at 8, 2x at 32).
 constexpr int kGemmMinTokensDefault = 6;
 
+// k_util.hip
+void launch_fill32(void* p, uint32_t v, size_t n_words, hipStream_t s);
+int stream_read_blocks();  // workgroups of launch_stream_read (one sink word each)
+void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);  // bytes % 16 == 0
+
 
 }  // namespace moe

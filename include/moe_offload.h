@@ -11,25 +11,18 @@
  * with W = q * s (int4 code times fp16 group scale) and rho rounding the
  * intermediate to the activation dtype; y is fp32.
  *
- * Sources (the pages describe the problem; the numerics above are the plain
- * reading of it):
- *  - "763B MoE 塞进两张 96GB 显卡：闲置专家丢进主机内存", section "显存缺口从哪里来":
- *    a few routed experts per token per layer (6 of 384); idle experts moved
- *    to host memory and read by GPU kernels in place over PCIe through
- *    unified addressing, without explicit copies.
- *  - same page, section "同一个思路，vLLM 原生方案反而跑不通": a per-expert plan,
- *    residency and read path decided for each expert individually.
- *  - same page, section "PCIe 拓扑：容易被忽略的性能变量": keep host-resident
- *    experts on the GPU's NUMA node.
- *  - "我在 32GB 单卡上跑两万四千专家的 MoE:分层放置实测与三个坑", section
- *    "二、跑起来靠的是分层,不是激活": all experts pinned in host RAM, free VRAM
- *    turned into an expert cache of the most used experts that adapts with use.
+ * The pages describe the problem; the numerics above are the plain reading of
+ * them. Page titles are abbreviated below as
+ *   [763B]  "763B MoE 塞进两张 96GB 显卡：闲置专家丢进主机内存"
+ *   [125B]  "125B 稀疏模型塞进一张 32GB 消费卡"
+ *   [24K]   "我在 32GB 单卡上跑两万四千专家的 MoE:分层放置实测与三个坑"
+ * and each call below names the section that defines what it does.
  *
  * Residency. Every expert of every layer has a copy in pinned, device-mapped
- * host memory (hipHostMalloc). A layer has `hbm_slots` HBM slots; an expert in
- * a slot is read from HBM, every other expert is read by the kernels directly
- * from its host copy over the host link. moe_cache_update moves experts
- * between the two.
+ * host memory (hipHostMalloc, on the host NUMA node closest to the GPU when the
+ * system reports one). A layer has `hbm_slots` HBM slots; an expert in a slot
+ * is read from HBM, every other expert is read by the kernels directly from its
+ * host copy over the host link. moe_cache_update moves experts between the two.
  *
  * Canonical expert blob (the weight format of this ABI), per expert:
  *   q_gate[I][H/2] | q_up[I][H/2] | q_down[H][I/2] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G]
@@ -78,7 +71,7 @@ typedef struct {
   int32_t inter;           /* I; multiple of 32 and of group_size */
   int32_t num_experts;     /* E; 1..1024 */
   int32_t top_k;           /* k; 1..min(E, 32) */
-  int32_t group_size;      /* G; multiple of 32 */
+  int32_t group_size;      /* G; 32, 64, 128 or 256 */
   int32_t num_layers;      /* L >= 1 */
   int32_t act_dtype;       /* moe_act_dtype of x, router weights and the intermediate h */
   int32_t max_tokens;      /* largest T of any forward; sizes the workspace */
@@ -94,18 +87,16 @@ typedef struct {
                               a copy kernel, before the GEMMs; those then re-read HBM
                               once per 64-row tile). Active offloaded experts beyond
                               this count are read in place. 0 = none: the GEMMs read
-                              every offloaded expert in place. Page "我在 32GB 单卡上
-                              跑两万四千专家的 MoE", section 二, has the VRAM cache
-                              keep slots for the experts a batch needs; P2's prefill
-                              micro-batches (ub 1024/2048) make the re-reads large */
+                              every offloaded expert in place. [24K] section 二 keeps
+                              the experts in use in VRAM slots; [125B] section
+                              "真正卡死容量的是一块计算缓冲" sizes prefill micro-batches
+                              at 1024/2048 tokens, which makes in-place re-reads large */
 } moe_config;
 
 typedef struct {
   const void* router_w;    /* host [E][H], act dtype (fp32 or bf16 bits) */
   const float* router_b;   /* host [E] fp32, or NULL for zeros */
   const uint8_t* experts;  /* host [E][expert_bytes] canonical blobs */
-  const int32_t* resident; /* host [E], 1 = start in an HBM slot; at most hbm_slots ones.
-                              NULL = experts 0..hbm_slots-1 */
 } moe_layer_weights;
 
 typedef struct {          /* optional routing outputs, device pointers, each may be NULL */
@@ -134,6 +125,13 @@ typedef struct {
   double decay;           /* score_e <- decay * score_e + count_e; default 0.9 */
   int32_t max_promotions; /* per layer per update; default 8 */
   int32_t overlap;        /* 0: synchronous update; 1: pipelined update (see moe_cache_update) */
+  const int32_t* want_resident; /* NULL: the frequency policy. Else host [E] (one layer) or
+                              [L][E] (layer = -1): 1 = the expert must read from HBM after
+                              the update, 0 = from its host copy; at most hbm_slots ones per
+                              layer. The update evicts every resident expert not wanted,
+                              then copies every wanted non-resident into the lowest free
+                              slots in ascending expert id (max_promotions does not apply);
+                              scores still take the counts. Always synchronous. */
 } moe_cache_policy;
 
 /* Kernel classes timed by the profiling hooks. */
@@ -154,24 +152,64 @@ typedef struct {
   double total_ms[MOE_K_COUNT];  /* summed GPU time between the events around them */
 } moe_kernel_times;
 
-/* Canonical bytes of one expert for cfg: 3*H*I/2 + 6*H*I/G. */
+typedef struct {
+  int32_t device;           /* HIP device of the plan */
+  int32_t gpu_numa_node;    /* host NUMA node closest to the GPU, -1 if not reported */
+  int32_t host_pool_node;   /* NUMA node of the host pool's first page, -1 if unknown */
+  int32_t numa_bound;       /* 1 = the host pool was allocated under a policy preferring gpu_numa_node */
+  int64_t internal_expert_bytes; /* bytes of one expert in the library's layout */
+  int64_t host_pool_bytes;  /* pinned host bytes of all layers' host copies */
+  int64_t hbm_slot_bytes;   /* device bytes of all layers' HBM slots */
+  int64_t workspace_bytes;  /* device bytes of the forward workspace */
+} moe_plan_info;
+
+typedef struct {
+  double hbm_read_gbps;     /* streaming-read kernel over a device buffer */
+  double host_read_gbps;    /* the same kernel over pinned, device-mapped host memory */
+  double h2d_copy_gbps;     /* hipMemcpyAsync host -> device from pinned host memory */
+} moe_link_ceilings;
+
+/* Canonical bytes of one expert for cfg: 3*H*I/2 + 6*H*I/G.
+ * Errors: MOE_E_INVALID (cfg). */
 moe_status moe_expert_bytes(const moe_config* cfg, size_t* out);
 
-/* Validate cfg and allocate a plan: HBM slots for every layer, the pinned
- * device-mapped host pool (all experts of all layers), router weights and
- * the workspace for max_tokens. Weights are loaded by moe_plan_load_layer.
+/* Create a plan: HBM slots for every layer, the pinned device-mapped host pool
+ * (every expert of every layer), router weights and the workspace for
+ * max_tokens, then (when `layers` is given) load every layer's weights as
+ * moe_plan_load_layer does.
+ *   layers:      host [L] weights, or NULL to load layers later one by one.
+ *   initial_hbm: host [L][E], 1 = the expert starts in an HBM slot (at most
+ *                hbm_slots ones per layer), or NULL: experts 0..hbm_slots-1.
+ *                Ignored when layers is NULL.
+ * [763B] section "同一个思路，vLLM 原生方案反而跑不通": residency and read path
+ * are decided for each expert individually; [763B] section "显存缺口从哪里来":
+ * the experts left out of VRAM are read by GPU kernels from host memory in
+ * place; [24K] section 二: every expert pinned in host RAM, free VRAM a cache.
+ * The caller's host buffers may be freed when the call returns.
  * On failure *out is NULL and nothing stays allocated.
- * Errors: MOE_E_INVALID (cfg), MOE_E_NOMEM, MOE_E_HOST_NOMEM, MOE_E_HIP. */
-moe_status moe_plan_create(const moe_config* cfg, moe_stream stream, moe_plan** out);
+ * Errors: MOE_E_INVALID (cfg, weights, initial_hbm), MOE_E_NOMEM,
+ * MOE_E_HOST_NOMEM, MOE_E_HIP. */
+moe_status moe_plan_create(const moe_config* cfg, const moe_layer_weights* layers, const int32_t* initial_hbm,
+                           moe_stream stream, moe_plan** out);
 
-/* Copy one layer's weights into the plan (host pool for every expert, HBM slots
- * for the resident ones, router weights to the device) and reset that layer's
- * counters. The host buffers may be freed when the call returns (it
- * synchronises `stream`). Errors: MOE_E_INVALID, MOE_E_HIP. */
+/* Copy one layer's weights into the plan: repack every expert into the host
+ * pool, copy the initially resident ones into HBM slots, router weights to the
+ * device; reset that layer's counters and cache scores. Same sources as
+ * moe_plan_create.
+ *   initial_hbm: host [E] (1 = start in an HBM slot, at most hbm_slots ones) or
+ *                NULL: experts 0..hbm_slots-1.
+ * Synchronises `stream`; the host buffers may be freed when the call returns.
+ * Errors: MOE_E_INVALID, MOE_E_HIP. */
 moe_status moe_plan_load_layer(moe_plan* plan, int32_t layer, const moe_layer_weights* w,
-                               moe_stream stream);
+                               const int32_t* initial_hbm, moe_stream stream);
 
-/* Forward of one layer for T tokens, enqueued on `stream`.
+/* Forward of one layer for T tokens, enqueued on `stream`: router logits, top-k
+ * gate choice, grouping of the token-expert assignments by expert, each touched
+ * expert's SwiGLU FFN read from its HBM slot or in place from host memory, and
+ * the gate-weighted combine. [763B] section "显存缺口从哪里来": each token, in
+ * each layer, uses a few routed experts (6 of 384), and experts outside VRAM
+ * are read over PCIe by the GPU kernels; [24K] section "一、第一个坑:MoE 省算力,
+ * 不省内存": the gate picks them at run time.
  * x: device [T][H] act dtype. y: device [T][H] fp32 (written, not accumulated).
  * logits_in: device [T][E] fp32 or NULL; when given, routing uses it and the
  *   router is skipped (the ids then do not depend on the router's rounding).
@@ -182,8 +220,10 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
                              const float* logits_in, float* y, const moe_routing* route_out,
                              moe_stream stream);
 
-/* Expert-cache update of one layer (or all, layer = -1) from the assignment
- * counts since the last update: frequency scores decay and accumulate; the
+/* Expert-cache update of one layer (or all, layer = -1). [24K] section 二: free
+ * VRAM holds the most used experts, and the cache adapts the longer it runs; the
+ * pages give no policy, so the plain frequency reading is taken:
+ * scores decay and accumulate the assignment counts since the last update; the
  * hbm_slots highest-scored experts are wanted in HBM; up to max_promotions
  * wanted experts per layer are copied host -> HBM slot (DMA on `stream`),
  * each into an empty slot or the slot of the lowest-scored resident no longer
@@ -191,7 +231,8 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
  * switch is enqueued after the copies on `stream`, so forwards enqueued later
  * on the same stream see it and earlier ones finish on the old table; other
  * streams must order themselves with events. Synchronises `stream` first to
- * read the counts. policy NULL = defaults.
+ * read the counts. policy NULL = defaults. policy->want_resident replaces the
+ * frequency choice by the caller's set (see moe_cache_policy).
  * Pipelined form (policy->overlap = 1), for decode loops that update after every
  * step: the host does not wait for the step just enqueued. The counts of the
  * forwards since the last update are staged (one copy for all the layers) and
@@ -208,14 +249,24 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
 moe_status moe_cache_update(moe_plan* plan, int32_t layer, const moe_cache_policy* policy,
                             moe_stream stream);
 
-/* Counters of one layer, or summed over layers for layer = -1. Synchronises the device. */
+/* Counters of one layer, or summed over layers for layer = -1: hits and misses
+ * per assignment and expert bytes per link, the quantities [763B] section
+ * "显存缺口从哪里来" weighs (how often an offloaded expert is needed, and the
+ * PCIe bytes it costs). Synchronises the device. Errors: MOE_E_INVALID, MOE_E_HIP. */
 moe_status moe_plan_stats(moe_plan* plan, int32_t layer, moe_stats* out);
 
 /* Zero the counters of every layer (not the cache scores). Synchronises the device. */
 moe_status moe_plan_reset_stats(moe_plan* plan);
 
-/* Host [E] slot table of a layer: slot_of[e] = HBM slot, or -1 when read from host memory. */
+/* Host [E] slot table of a layer: slot_of[e] = HBM slot, or -1 when read from
+ * host memory (the per-expert plan of [763B] section "同一个思路，vLLM 原生方案
+ * 反而跑不通"). Does not synchronise. Errors: MOE_E_INVALID. */
 moe_status moe_plan_residency(moe_plan* plan, int32_t layer, int32_t* slot_of);
+
+/* Sizes and host-memory placement of a plan. [763B] section "PCIe 拓扑：容易被
+ * 忽略的性能变量": host memory on the GPU's NUMA node matters for the host link.
+ * Errors: MOE_E_INVALID. */
+moe_status moe_plan_get_info(moe_plan* plan, moe_plan_info* out);
 
 /* Profiling: enable != 0 starts recording a HIP event pair around every kernel
  * launch of moe_layer_forward on its stream (and drops earlier records);
@@ -227,6 +278,19 @@ moe_status moe_plan_profile(moe_plan* plan, int32_t enable);
  * Synchronises the device. Errors: MOE_E_INVALID, MOE_E_HIP. */
 moe_status moe_plan_kernel_times(moe_plan* plan, moe_kernel_times* out);
 
+/* Measured ceilings of the two links the experts are read over, on the current
+ * device ([763B] section "显存缺口从哪里来" gives PCIe 5.0 x16 at about 64 GB/s
+ * per direction against on-card memory; section "PCIe 拓扑" found the placement
+ * of host memory to matter): a streaming-read kernel over hbm_bytes of device
+ * memory and over host_bytes of pinned device-mapped host memory (on the GPU's
+ * NUMA node when reported), and hipMemcpyAsync of host_bytes host -> device.
+ * Each figure is the best of `iters` timed runs after one untimed run. The call
+ * allocates and frees its own buffers and synchronises `stream`.
+ * Errors: MOE_E_INVALID (sizes < 1 MiB or not multiples of 4 KiB, iters < 1),
+ * MOE_E_NOMEM, MOE_E_HOST_NOMEM, MOE_E_HIP. */
+moe_status moe_measure_link_ceilings(size_t hbm_bytes, size_t host_bytes, int32_t iters, moe_stream stream,
+                                     moe_link_ceilings* out);
+
 /* Free everything the plan owns (synchronises the device first). NULL is a no-op. */
 void moe_plan_destroy(moe_plan* plan);
 
@@ -234,6 +298,17 @@ const char* moe_status_str(moe_status s);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
+
+/* Test hook for the allocation-failure paths: after this call, the n-th next
+ * device allocation (kind 0) or pinned host allocation (kind 1) made by this
+ * library on any thread fails as if out of memory (n >= 1; n = 0 disarms).
+ * The failing call then returns MOE_E_NOMEM / MOE_E_HOST_NOMEM and frees what
+ * it had allocated. Errors: MOE_E_INVALID (kind or n out of range). */
+moe_status moe_debug_fail_alloc(int32_t kind, int32_t n);
+
+/* Test hook: the device and pinned host allocations this library currently holds
+ * (over all plans). Errors: MOE_E_INVALID (null argument). */
+moe_status moe_debug_live_allocs(int64_t* device, int64_t* host);
 
 #ifdef __cplusplus
 }

@@ -339,3 +339,32 @@ def cache_policy_step(score: np.ndarray, counts: np.ndarray, slot_of: np.ndarray
         slot_of[p] = s
         done.append((p, s))
     return score, slot_of, done, evicted
+
+
+def cache_set_resident(score: np.ndarray, counts: np.ndarray, slot_of: np.ndarray, want: np.ndarray, n_slots: int,
+                       decay: float):
+    """An expert-cache update to a residency set the caller chose: the per-expert plan
+    of page "763B MoE 塞进两张 96GB 显卡…", section "同一个思路，vLLM 原生方案反而跑不通",
+    where residency is decided expert by expert, applied to the cache slots of page
+    "我在 32GB 单卡上跑两万四千专家的 MoE…", section "二、跑起来靠的是分层,不是激活".
+
+    score_e <- decay * score_e + counts_e, as in cache_policy_step. Every resident not in
+    `want` is evicted (its slot freed); then every wanted non-resident, in ascending id,
+    takes the lowest free slot. At most n_slots experts may be wanted.
+    Returns (new_score, new_slot_of, [(expert, slot) promoted], [evicted experts]).
+    """
+    want = np.asarray(want).astype(bool)
+    assert want.sum() <= n_slots, "more experts wanted than slots"
+    score = decay * np.asarray(score, dtype=np.float64) + np.asarray(counts, dtype=np.float64)
+    slot_of = np.asarray(slot_of, dtype=np.int64).copy()
+    evicted = [e for e in range(slot_of.size) if slot_of[e] >= 0 and not want[e]]
+    for e in evicted:
+        slot_of[e] = -1
+    free = sorted(set(range(n_slots)) - set(int(v) for v in slot_of[slot_of >= 0]))
+    promoted = []
+    for e in range(slot_of.size):
+        if want[e] and slot_of[e] < 0:
+            s = free.pop(0)
+            slot_of[e] = s
+            promoted.append((e, s))
+    return score, slot_of, promoted, evicted

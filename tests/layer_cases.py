@@ -102,3 +102,52 @@ def valid_topk(logits_row, ids, k, tol):
     if rest.size and l[sel].min() < l[rest].max() - 2 * tol:
         return False
     return bool(np.all(np.diff(l[sel]) <= 2 * tol))
+
+
+def random_code_blobs(E, H, I, G, seed, p_minus8=0.3):
+    """Canonical blobs whose codes cover all 16 values of the format, with the code -8
+    (nibble 0x8) drawn with probability p_minus8 and the other 15 uniformly; fp16 group
+    scales near 0.8 / sqrt(32 K), so that g, u and o stay of order one. Packed by the
+    generator's C packer."""
+    rng = np.random.default_rng(seed)
+
+    def codes(rows, K):
+        q = rng.integers(-7, 8, size=(rows, K)).astype(np.int8)
+        q[rng.random((rows, K)) < p_minus8] = -8
+        return q
+
+    def scales(rows, K):
+        s = 0.8 / np.sqrt(32.0 * K) * rng.uniform(0.5, 1.5, size=(rows, K // G))
+        return s.astype(np.float16).view(np.uint16)
+
+    out = []
+    for _ in range(E):
+        out.append(synth.pack_blob(codes(I, H), codes(I, H), codes(H, I), scales(I, H), scales(I, H),
+                                   scales(H, I)))
+    return np.stack(out)
+
+
+def tie_logits(T, E, k, seed):
+    """Router logits [T, E] float32 with exact ties at the top-k cut and inside the
+    top k, and +0.0 / -0.0 pairs: values from a small set {-1, -0.5, 0, 0.5, 1}
+    with random zero signs; every 5th token has all logits zero (mixed signs, the
+    answer is experts 0..k-1), every 5th + 1 one high logit at the last expert and a
+    tie of every other expert at 0.5 or -0.0/+0.0, every 5th + 2 exactly k+1 experts
+    tied at the maximum (the cut falls inside the tie)."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([-1.0, -0.5, 0.0, 0.5, 1.0], np.float32)
+    L = rng.choice(vals, size=(T, E)).astype(np.float32)
+    for t in range(T):
+        kind = t % 5
+        if kind == 0:
+            L[t] = 0.0
+        elif kind == 1:
+            L[t] = 0.5 if t % 2 else 0.0
+            L[t, E - 1] = 1.0
+        elif kind == 2:
+            L[t] = -1.0
+            top = rng.choice(E, size=min(k + 1, E), replace=False)
+            L[t, top] = 0.0
+    neg = (L == 0) & (rng.random((T, E)) < 0.5)
+    L[neg] = -0.0
+    return L

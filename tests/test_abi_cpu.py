@@ -48,7 +48,7 @@ def test_expert_bytes_and_validation(lib):
         out = ctypes.c_size_t()
         assert lib.moe_expert_bytes(ctypes.byref(cfg), ctypes.byref(out)) == moe.MOE_E_INVALID
         h = ctypes.c_void_p(1)
-        assert lib.moe_plan_create(ctypes.byref(cfg), None, ctypes.byref(h)) == moe.MOE_E_INVALID
+        assert lib.moe_plan_create(ctypes.byref(cfg), None, None, None, ctypes.byref(h)) == moe.MOE_E_INVALID
         assert h.value is None
         assert len(lib.moe_last_error()) > 0
 
@@ -59,6 +59,41 @@ def test_status_strings_and_null_args(lib):
     assert lib.moe_layer_forward(None, 0, 1, None, None, None, None, None) == moe.MOE_E_INVALID
     assert lib.moe_cache_update(None, 0, None, None) == moe.MOE_E_INVALID
     lib.moe_plan_destroy(None)
+
+
+def _header_struct_fields(name):
+    txt = open(os.path.join(ROOT, "include", "moe_offload.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} %s;" % name, txt).group(1)
+    return re.findall(r"(\w[\w\s\*]*?)\s*\*?\s*(\w+)\s*(?:\[[^\]]*\])?\s*;", body)
+
+
+@pytest.mark.parametrize("cname,pyname", [("moe_layer_weights", "LayerWeights"), ("moe_routing", "Routing"),
+                                          ("moe_stats", "Stats"), ("moe_cache_policy", "CachePolicy"),
+                                          ("moe_plan_info", "PlanInfo"), ("moe_link_ceilings", "LinkCeilings"),
+                                          ("moe_kernel_times", "KernelTimes")])
+def test_binding_structs_match_header(cname, pyname):
+    """Every struct the binding mirrors has the header's field names, in order, and the
+    same size (ctypes lays fields out by the platform C ABI)."""
+    fields = [n for _, n in _header_struct_fields(cname)]
+    assert [n for n, _ in getattr(moe, pyname)._fields_] == fields, cname
+    sizes = {"moe_layer_weights": 24, "moe_routing": 56, "moe_stats": 72, "moe_cache_policy": 24,
+             "moe_plan_info": 48, "moe_link_ceilings": 24, "moe_kernel_times": 128}
+    assert ctypes.sizeof(getattr(moe, pyname)) == sizes[cname]
+
+
+def test_debug_fail_alloc_arguments(lib):
+    assert lib.moe_debug_fail_alloc(2, 1) == moe.MOE_E_INVALID
+    assert lib.moe_debug_fail_alloc(0, -1) == moe.MOE_E_INVALID
+    assert lib.moe_debug_fail_alloc(0, 0) == moe.MOE_OK
+    assert lib.moe_debug_fail_alloc(1, 0) == moe.MOE_OK
+
+
+def test_link_ceiling_arguments_validated(lib):
+    out = moe.LinkCeilings()
+    assert lib.moe_measure_link_ceilings(1 << 10, 1 << 20, 1, None, ctypes.byref(out)) == moe.MOE_E_INVALID
+    assert lib.moe_measure_link_ceilings(1 << 20, (1 << 20) + 1, 1, None, ctypes.byref(out)) == moe.MOE_E_INVALID
+    assert lib.moe_measure_link_ceilings(1 << 20, 1 << 20, 0, None, ctypes.byref(out)) == moe.MOE_E_INVALID
 
 
 def test_config_struct_matches_header():

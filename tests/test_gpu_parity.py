@@ -343,7 +343,7 @@ def test_prefill_offloaded_experts_staged(moe, T, seed):
 # ----------------------------------------------------------------------------- full-size DeepSeek-style layer
 
 DS_LAYER = dict(H=7168, I=2048, E=384, k=6, G=128, seed=2, alpha=1.0)
-DS_CHECKED = {1: [0], 4: [0, 3], 16: [5, 12]}  # batch -> tokens whose outputs are compared
+DS_CHECKED = {1: [0], 4: [0, 1, 2, 3], 16: [0, 2, 4, 6, 8, 10, 12, 14]}  # batch -> tokens whose outputs are compared
 
 
 @pytest.fixture(scope="module")
@@ -351,7 +351,8 @@ def deepseek_layer(moe):
     """The DeepSeek-style layer at its full size (H7168 I2048 E384 k6 G128, Zipf bias alpha
     1.0), one seeded batch per size. Experts that the checked tokens route to carry their
     generated weights; every other expert is filled with its own constant code byte and
-    small finite scales, so a read of a wrong expert changes the result."""
+    small finite scales, so a read of a wrong expert changes the result. The oracle's y on
+    the checked tokens is computed once here and shared by the plans tested below."""
     import concurrent.futures
     import synth
     d = DS_LAYER
@@ -376,51 +377,76 @@ def deepseek_layer(moe):
         for e, blob in zip(sorted(need), ex.map(lambda e: synth.expert_blobs(seed, 0, e, 1, H, I, G)[0],
                                                 sorted(need))):
             blobs[e] = blob
-    res = synth.coldest_host_plan(seed, 0, E, 0.7)  # 269 experts in HBM, the 115 coldest on the host
-    cfg = moe.make_config(H, I, E, k, G, "bf16", max_tokens=max(DS_CHECKED), hbm_slots=int(res.sum()))
-    plan = moe.Plan(cfg)
-    plan.load_layer(0, Wr_store, b, blobs, res)
-    for c in cases.values():
+    _say("  deepseek-shaped layer: %d generated experts" % len(need))
+    for T, c in cases.items():
         c.blobs = blobs
-    _say("  deepseek-shaped layer: %d generated experts, %d in HBM" % (len(need), int(res.sum())))
-    yield plan, cases, res
-    plan.destroy()
+        c.ref = LC.oracle_forward(c, logits_in=c.lg, tokens=np.array(DS_CHECKED[T]))
+        _say("  oracle y for batch %d (%d tokens) done" % (T, len(DS_CHECKED[T])))
+    res = synth.coldest_host_plan(seed, 0, E, 0.7)  # 269 experts in HBM, the 115 coldest on the host
+    return cases, blobs, res
 
 
-@pytest.mark.parametrize("T", sorted(DS_CHECKED))
-def test_deepseek_shaped_full_size(moe, deepseek_layer, T):
+def _deepseek_plan(moe, deepseek_layer, plan_kind):
+    cases, blobs, res = deepseek_layer
+    d = DS_LAYER
+    if plan_kind == "mixed":
+        slots, resident = int(res.sum()), res
+    else:  # every expert read from host memory over the host link
+        slots, resident = 0, np.zeros(d["E"], np.int32)
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", max_tokens=max(DS_CHECKED),
+                          hbm_slots=slots)
+    plan = moe.Plan(cfg)
+    c0 = cases[1]
+    plan.load_layer(0, c0.Wr_store, c0.b, blobs, resident)
+    return plan, resident
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("plan_kind", ["mixed", "host"])
+def test_deepseek_shaped_full_size(moe, deepseek_layer, plan_kind):
     """Full-size DeepSeek-style layer in the launch configuration the benchmark times
-    (70/30 plan, default dispatch: GEMVs with the 16-row fused down + combine at batches
-    1 and 4, the grouped MFMA GEMM at 16). Routing bit-exact against the oracle for every
-    token; y on the checked tokens, with the oracle's logits and with the library's router;
-    link counters against an exact recount."""
+    (default dispatch: GEMVs with the 16-row fused down + combine at batches 1 and 4, the
+    grouped MFMA GEMM at 16), on the 70/30 plan (the 115 coldest experts read from host
+    memory) and on the all-host plan (every expert over the host link). Routing bit-exact
+    against the oracle for every token; y on the checked tokens (8 of 16 at batch 16), with
+    the oracle's logits and with the library's router; link counters against an exact
+    recount."""
     import synth
-    plan, cases, res = deepseek_layer
-    c = cases[T]
-    toks = np.array(DS_CHECKED[T])
-    ref = LC.oracle_forward(c, logits_in=c.lg, tokens=toks)
-    rb = route_bufs(c)
-    plan.reset_stats()
-    y = run(plan, c, logits_in=c.lg, route=rb)
-    full = O.route(c.lg, c.k)
-    counts, offsets, srt, inv = O.align_permute(full[0], c.E)
-    np.testing.assert_array_equal(rb["topk_ids"].cpu().numpy().reshape(c.T, c.k), full[0])
-    np.testing.assert_array_equal(rb["counts"].cpu().numpy(), counts)
-    np.testing.assert_array_equal(rb["offsets"].cpu().numpy(), offsets)
-    np.testing.assert_array_equal(rb["sorted"].cpu().numpy(), srt)
-    np.testing.assert_array_equal(rb["inv"].cpu().numpy(), inv)
-    assert np.all(np.isfinite(y))
-    check_y(y[toks], ref["y"], "deepseek-shaped y, batch %d (tokens %s)" % (T, toks.tolist()))
-    st = plan.stats(0)
-    acc = O.link_accounting(full[0], res, synth.expert_bytes(c.H, c.I, c.G))
-    assert (st["hits"], st["misses"]) == (acc["hits"], acc["misses"])
-    assert (st["bytes_hbm"], st["bytes_host"]) == (acc["bytes_hbm"], acc["bytes_host"])
-    # the library's router: logits within fp32 accumulation error, y where the routing is clear
-    rb2 = route_bufs(c)
-    y2 = run(plan, c, route=rb2)
-    glog = rb2["logits"].cpu().numpy().reshape(c.T, c.E).astype(np.float64)
-    tol = 1e-5 * max(1.0, np.abs(c.lg).max())
-    assert np.abs(glog - c.lg).max() <= tol
-    clear = LC.routing_margins(c.lg, c.k)[toks] > 2 * tol
-    if clear.any():
-        check_y(y2[toks[clear]], ref["y"][clear], "deepseek-shaped y, library router, batch %d" % T)
+    cases = deepseek_layer[0]
+    plan, resident = _deepseek_plan(moe, deepseek_layer, plan_kind)
+    try:
+        for T in sorted(DS_CHECKED):
+            c = cases[T]
+            toks = np.array(DS_CHECKED[T])
+            ref = c.ref
+            rb = route_bufs(c)
+            plan.reset_stats()
+            y = run(plan, c, logits_in=c.lg, route=rb)
+            full = O.route(c.lg, c.k)
+            counts, offsets, srt, inv = O.align_permute(full[0], c.E)
+            np.testing.assert_array_equal(rb["topk_ids"].cpu().numpy().reshape(c.T, c.k), full[0])
+            np.testing.assert_array_equal(rb["counts"].cpu().numpy(), counts)
+            np.testing.assert_array_equal(rb["offsets"].cpu().numpy(), offsets)
+            np.testing.assert_array_equal(rb["sorted"].cpu().numpy(), srt)
+            np.testing.assert_array_equal(rb["inv"].cpu().numpy(), inv)
+            assert np.all(np.isfinite(y))
+            check_y(y[toks], ref["y"], "deepseek-shaped y, %s plan, batch %d (tokens %s)" % (
+                plan_kind, T, toks.tolist()))
+            st = plan.stats(0)
+            acc = O.link_accounting(full[0], resident, synth.expert_bytes(c.H, c.I, c.G))
+            assert (st["hits"], st["misses"]) == (acc["hits"], acc["misses"])
+            assert (st["bytes_hbm"], st["bytes_host"]) == (acc["bytes_hbm"], acc["bytes_host"])
+            if plan_kind == "host":
+                assert st["bytes_hbm"] == 0 and st["hits"] == 0
+            # the library's router: logits within fp32 accumulation error, y where the routing is clear
+            rb2 = route_bufs(c)
+            y2 = run(plan, c, route=rb2)
+            glog = rb2["logits"].cpu().numpy().reshape(c.T, c.E).astype(np.float64)
+            tol = 1e-5 * max(1.0, np.abs(c.lg).max())
+            assert np.abs(glog - c.lg).max() <= tol
+            clear = LC.routing_margins(c.lg, c.k)[toks] > 2 * tol
+            if clear.any():
+                check_y(y2[toks[clear]], ref["y"][clear], "deepseek-shaped y, library router, %s plan, batch %d" % (
+                    plan_kind, T))
+    finally:
+        plan.destroy()

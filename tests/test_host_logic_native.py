@@ -1,0 +1,222 @@
+"""The library's host-side logic (host_logic.cpp: configuration checks, the internal
+expert layout and repack, the expert-cache policies) built on its own with g++ under
+AddressSanitizer and UndefinedBehaviorSanitizer, driven through a pipe
+(tests/native/host_logic_check.cpp) and compared with the oracle and with an
+independent decoder of the internal layout written here from its documentation
+(host_logic.h). Any sanitizer report, or a leak at exit, fails the module."""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "expert_offloaded_ffn_moe_amd", "csrc")
+
+
+class Driver:
+    def __init__(self, exe):
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:exitcode=97",
+                   UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1:exitcode=98")
+        env.pop("LD_PRELOAD", None)
+        self.p = subprocess.Popen([exe], stdin=subprocess.PIPE, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                  text=True, env=env)
+
+    def ask(self, lines, n_out):
+        for ln in lines:
+            self.p.stdin.write(ln + "\n")
+        self.p.stdin.flush()
+        out = [self.p.stdout.readline().rstrip("\n") for _ in range(n_out)]
+        assert self.p.poll() is None, "driver exited: %s" % self.p.stderr.read()
+        return out
+
+    def close(self):
+        self.p.stdin.close()
+        rc = self.p.wait(timeout=60)
+        return rc, self.p.stderr.read()
+
+
+@pytest.fixture(scope="module")
+def drv(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.fail("g++ is required")
+    exe = str(tmp_path_factory.mktemp("hl") / "host_logic_check")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "host_logic.cpp"), os.path.join(ROOT, "tests", "native", "host_logic_check.cpp"),
+           "-o", exe]
+    subprocess.check_call(cmd)
+    d = Driver(exe)
+    yield d
+    rc, err = d.close()
+    assert rc == 0 and "ERROR" not in err and "runtime error" not in err, err
+
+
+SHAPES = [(256, 128, 32), (384, 96, 32), (512, 256, 64), (256, 256, 256), (2048, 768, 128)]
+
+
+def layout_expected(H, I, G):
+    """The documented rule: regions in order, each 256-byte aligned."""
+    up = lambda v: (v + 255) // 256 * 256
+    gu_t, gu_c, gu_g, dn_t, dn_c, dn_g = I // 32, H // 32, H // G, H // 64, I // 32, I // G
+    o1 = 0
+    o2 = up(o1 + gu_t * gu_c * 1024)
+    o3 = up(o2 + gu_t * gu_g * 128)
+    o4 = up(o3 + dn_t * dn_c * 1024)
+    end = up(o4 + dn_t * dn_g * 128)
+    return [gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o1, o2, o3, o4, end, 3 * H * I // 2 + 6 * H * I // G]
+
+
+@pytest.mark.parametrize("H,I,G", SHAPES)
+def test_layout(drv, H, I, G):
+    got = [int(v) for v in drv.ask(["layout %d %d %d" % (H, I, G)], 1)[0].split()]
+    assert got == layout_expected(H, I, G)
+
+
+def decode_codes(region, tiles, chunks):
+    """[tiles, 64 lanes, chunks * 32] int codes of a code region: dword d of a lane's 16
+    bytes covers K offsets 8d..8d+7, offset 8d+2j in bits 4j..4j+3 and 8d+2j+1 in bits
+    16+4j..19+4j, stored as n = q + 8."""
+    u = np.frombuffer(region.tobytes(), dtype="<u4").reshape(tiles, chunks, 64, 4)
+    q = np.empty((tiles, chunks, 64, 32), dtype=np.int16)
+    for d in range(4):
+        for j in range(4):
+            q[..., 8 * d + 2 * j] = ((u[..., d] >> (4 * j)) & 0xF).astype(np.int16) - 8
+            q[..., 8 * d + 2 * j + 1] = ((u[..., d] >> (16 + 4 * j)) & 0xF).astype(np.int16) - 8
+    return q.transpose(0, 2, 1, 3).reshape(tiles, 64, chunks * 32)
+
+
+def decode_scales(region, tiles, groups):
+    return np.frombuffer(region.tobytes(), dtype="<u2").reshape(tiles, groups, 64).transpose(0, 2, 1)
+
+
+@pytest.mark.parametrize("H,I,G", SHAPES)
+def test_repack_against_oracle_unpack(drv, tmp_path, H, I, G):
+    """Random bytes cover all 16 codes in both nibble positions; scales are random fp16 bits."""
+    rng = np.random.default_rng(H + I + G)
+    eb = O.expert_bytes(H, I, G)
+    blob = rng.integers(0, 256, size=eb, dtype=np.uint8)
+    src, dst = tmp_path / "c.bin", tmp_path / "i.bin"
+    blob.tofile(src)
+    assert drv.ask(["repack %d %d %d %s %s" % (H, I, G, src, dst)], 1) == ["done"]
+    lay = layout_expected(H, I, G)
+    gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o1, o2, o3, o4, end, _ = lay
+    internal = np.fromfile(dst, dtype=np.uint8)
+    assert internal.size == end
+    parts, _ = O.expert_layout(H, I, G)
+    part = lambda n: blob[parts[n][0]:parts[n][1]]
+    qg = O.unpack_int4(part("q_gate").reshape(I, H // 2))
+    qu = O.unpack_int4(part("q_up").reshape(I, H // 2))
+    qd = O.unpack_int4(part("q_down").reshape(H, I // 2))
+    assert set(np.unique(qg).tolist()) == set(range(-8, 8))
+    gu = decode_codes(internal[o1:o1 + gu_t * gu_c * 1024], gu_t, gu_c)
+    np.testing.assert_array_equal(gu[:, :32].reshape(I, H), qg)
+    np.testing.assert_array_equal(gu[:, 32:].reshape(I, H), qu)
+    dn = decode_codes(internal[o3:o3 + dn_t * dn_c * 1024], dn_t, dn_c)
+    np.testing.assert_array_equal(dn.reshape(H, I), qd)
+    sgu = decode_scales(internal[o2:o2 + gu_t * gu_g * 128], gu_t, gu_g)
+    np.testing.assert_array_equal(sgu[:, :32].reshape(I, H // G), part("s_gate").view("<u2").reshape(I, H // G))
+    np.testing.assert_array_equal(sgu[:, 32:].reshape(I, H // G), part("s_up").view("<u2").reshape(I, H // G))
+    sdn = decode_scales(internal[o4:o4 + dn_t * dn_g * 128], dn_t, dn_g)
+    np.testing.assert_array_equal(sdn.reshape(H, I // G), part("s_down").view("<u2").reshape(H, I // G))
+
+
+def _ints(v):
+    return " ".join(str(int(a)) for a in v)
+
+
+def _floats(v):
+    return " ".join(float(a).hex() for a in v)
+
+
+def _parse(out):
+    score = np.array([float.fromhex(t) for t in out[0].split()])
+    slot = np.array([int(t) for t in out[1].split()])
+    prom = [tuple(int(u) for u in t.split(":")) for t in out[2].split()]
+    ev = [int(t) for t in out[3].split()]
+    return score, slot, prom, ev
+
+
+def _random_state(rng, E, S):
+    slot = np.full(E, -1)
+    res = rng.choice(E, size=int(rng.integers(0, S + 1)), replace=False)
+    if S:
+        slot[res] = rng.choice(S, size=res.size, replace=False)
+    score = rng.random(E) * rng.integers(0, 5, size=E)  # ties at zero and repeated values
+    score[rng.random(E) < 0.3] = 1.0
+    counts = rng.integers(0, 4, size=E) * (rng.random(E) < 0.6)
+    return slot, score, counts
+
+
+def test_cache_policy_matches_oracle(drv):
+    rng = np.random.default_rng(5)
+    for it in range(300):
+        E = int(rng.integers(1, 70))
+        S = int(rng.integers(0, E + 1))
+        slot, score, counts = _random_state(rng, E, S)
+        decay, maxp = float(rng.choice([0.0, 0.5, 0.9, 1.0])), int(rng.integers(0, 10))
+        out = drv.ask(["policy %d %d %s %d" % (E, S, decay.hex(), maxp), _ints(counts), _floats(score),
+                       _ints(slot)], 4)
+        got = _parse(out)
+        want = O.cache_policy_step(score, counts, slot, S, decay, maxp)
+        np.testing.assert_array_equal(got[0], want[0])
+        np.testing.assert_array_equal(got[1], want[1])
+        assert got[2] == [(int(a), int(b)) for a, b in want[2]], it
+        assert got[3] == [int(a) for a in want[3]], it
+
+
+def test_cache_set_resident_matches_oracle(drv):
+    rng = np.random.default_rng(6)
+    for it in range(300):
+        E = int(rng.integers(1, 70))
+        S = int(rng.integers(0, E + 1))
+        slot, score, counts = _random_state(rng, E, S)
+        want = np.zeros(E, np.int32)
+        n_want = int(rng.integers(0, E + 1)) if it % 10 == 0 else int(rng.integers(0, S + 1))
+        want[rng.choice(E, size=n_want, replace=False)] = 1
+        out = drv.ask(["setres %d %d %s" % (E, S, (0.9).hex()), _ints(counts), _floats(score), _ints(slot),
+                       _ints(want)], 4)
+        if n_want > S:
+            assert out[0] == "refused"
+            continue
+        got = _parse(out)
+        ref = O.cache_set_resident(score, counts, slot, want, S, 0.9)
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+        assert got[2] == [(int(a), int(b)) for a, b in ref[2]]
+        assert got[3] == [int(a) for a in ref[3]]
+
+
+def _valid(H, I, E, k, G, L, act, T, S, gmin, stage):
+    """The configuration rules as the header states them."""
+    return (H > 0 and I > 0 and G in (32, 64, 128, 256) and H % 64 == 0 and I % 32 == 0 and H % G == 0
+            and I % G == 0 and 1 <= E <= 1024 and 1 <= k <= min(E, 32) and L >= 1 and act in (0, 1)
+            and 1 <= T <= (1 << 20) and T * k <= (1 << 22) and 0 <= S <= E and 0 <= stage <= E
+            and H <= 65536 and I <= 65536)
+
+
+def test_check_config_matches_stated_rules(drv):
+    rng = np.random.default_rng(7)
+    base = [2048, 768, 128, 8, 128, 1, 1, 16, 90, 0, 0]
+    cases = [base]
+    alts = {0: [0, -64, 64, 96, 65536, 65600], 1: [0, 32, 48, 96, 65536], 2: [0, 1, 1024, 1025], 3: [0, 1, 32, 33],
+            4: [16, 32, 48, 64, 256, 512], 5: [0, 1, 48], 6: [-1, 0, 1, 2], 7: [0, 1, 1 << 20, (1 << 20) + 1],
+            8: [-1, 0, 128, 129], 9: [-1, 0, 6], 10: [-1, 0, 128, 129]}
+    for i, vals in alts.items():
+        for v in vals:
+            c = list(base)
+            c[i] = v
+            cases.append(c)
+    for _ in range(200):
+        c = list(base)
+        for i in rng.choice(11, size=3, replace=False):
+            c[i] = int(rng.choice(alts[int(i)]))
+        cases.append(c)
+    for c in cases:
+        got = drv.ask(["check " + _ints(c)], 1)[0]
+        assert (got == "OK") == _valid(*c), (c, got)

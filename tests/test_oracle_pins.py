@@ -124,6 +124,34 @@ def test_round_bf16_ties_and_no_double_rounding():
     assert O.round_bf16(np.array([-v]))[0] == -(1 + 2 ** -7)
 
 
+def test_bf16_bits_to_f64_every_pattern_against_field_decode_and_torch():
+    """All 65,536 bf16 bit patterns: the oracle's widening equals (a) the value the
+    sign / 8-bit exponent / 7-bit fraction fields define, built with exact float64
+    arithmetic (normal: (1 + f/128) 2^(e-127); subnormal: f/128 2^-126; e = 255:
+    inf or NaN), and (b) torch's bfloat16 -> float64 conversion on the CPU."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    sign = np.where(bits >> 15, -1.0, 1.0)
+    e = ((bits >> 7) & 0xFF).astype(np.int64)
+    f = (bits & 0x7F).astype(np.float64)
+    want = np.where(e == 0, np.ldexp(f / 128.0, -126), np.ldexp(1.0 + f / 128.0, (e - 127).clip(-126, 127)))
+    want = sign * want
+    special = e == 255
+    want = np.where(special & (f == 0), sign * np.inf, want)
+    want = np.where(special & (f != 0), np.nan, want)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(want[ok]))  # -0.0 stays -0.0
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert np.isnan(ref[~ok]).all()
+    # spot values: 1.0, -2.0, the largest finite, the smallest subnormal
+    for b, v in [(0x3F80, 1.0), (0xC000, -2.0), (0x7F7F, float(np.ldexp(255.0, 120))), (0x0001, 2.0 ** -133)]:
+        assert O.bf16_bits_to_f64(np.array([b], np.uint16))[0] == v
+
+
 def test_round_act_f32_is_numpy_cast():
     v = np.array([1 / 3, 2 / 3, 1e-50, 1e300])
     np.testing.assert_array_equal(O.round_act(v, "f32"), v.astype(np.float32).astype(np.float64))
@@ -417,6 +445,43 @@ def test_cache_policy_converges_to_top_counts():
         assert sorted(slot_of[slot_of >= 0].tolist()) == list(range(S))  # slots stay a bijection
     top = set(np.argsort(-p, kind="stable")[:S].tolist())
     assert len(top & set(np.nonzero(slot_of >= 0)[0].tolist())) >= S - 2
+
+
+def test_cache_set_resident_hand_cases():
+    # residents 0 (slot 1) and 2 (slot 0); want {2, 3, 4} over 3 slots: 0 evicted (slot 1
+    # freed), 3 takes slot 1, 4 the never-used slot 2; 2 keeps slot 0
+    score, slot_of, done, ev = O.cache_set_resident(np.zeros(5), [1, 0, 2, 0, 0], [1, -1, 0, -1, -1],
+                                                    [0, 0, 1, 1, 1], 3, 0.5)
+    assert ev == [0] and done == [(3, 1), (4, 2)]
+    assert slot_of.tolist() == [-1, -1, 0, 1, 2]
+    assert score.tolist() == [1.0, 0.0, 2.0, 0.0, 0.0]
+    # want nothing: every resident goes back to its host copy, nothing promoted
+    _, slot_of, done, ev = O.cache_set_resident(np.zeros(3), [0, 0, 0], [0, 1, -1], [0, 0, 0], 2, 0.9)
+    assert done == [] and ev == [0, 1] and (slot_of == -1).all()
+    with pytest.raises(AssertionError):
+        O.cache_set_resident(np.zeros(3), [0, 0, 0], [-1, -1, -1], [1, 1, 1], 2, 0.9)
+
+
+def test_cache_set_resident_reaches_the_wanted_set():
+    """From random tables to random wanted sets: afterwards exactly the wanted experts
+    are resident, slots are distinct and in range, and a resident that stays wanted
+    keeps its slot."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        E, S = int(rng.integers(1, 40)), None
+        S = int(rng.integers(0, E + 1))
+        slot_of = np.full(E, -1)
+        res = rng.choice(E, size=int(rng.integers(0, S + 1)), replace=False)
+        slot_of[res] = rng.choice(S, size=res.size, replace=False) if S else []
+        want = np.zeros(E, np.int32)
+        want[rng.choice(E, size=int(rng.integers(0, S + 1)), replace=False)] = 1
+        _, new, done, ev = O.cache_set_resident(np.zeros(E), np.zeros(E), slot_of, want, S, 0.9)
+        assert ((new >= 0) == want.astype(bool)).all()
+        assert len(set(new[new >= 0].tolist())) == int(want.sum()) and (new < S).all()
+        kept = (slot_of >= 0) & want.astype(bool)
+        assert (new[kept] == slot_of[kept]).all()
+        assert sorted(ev) == sorted(np.nonzero((slot_of >= 0) & ~want.astype(bool))[0].tolist())
+        assert [e for e, _ in done] == sorted(np.nonzero((slot_of < 0) & want.astype(bool))[0].tolist())
 
 
 # ----------------------------------------------------------------------------- page structural figures
