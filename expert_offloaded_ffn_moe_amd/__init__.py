@@ -105,6 +105,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_debug_fail_alloc.argtypes = [i32, i32]
     lib.moe_debug_live_allocs.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
+    lib.moe_layer_forward_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
     lib.moe_cache_update.argtypes = [vp, i32, ctypes.POINTER(CachePolicy), vp]
     lib.moe_plan_stats.argtypes = [vp, i32, ctypes.POINTER(Stats)]
     lib.moe_plan_reset_stats.argtypes = [vp]
@@ -117,6 +118,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_last_error.restype = ctypes.c_char_p
     for fn in ("moe_expert_bytes", "moe_plan_create", "moe_plan_load_layer", "moe_layer_forward",
+               "moe_layer_forward_noalloc",
                "moe_cache_update", "moe_plan_stats", "moe_plan_reset_stats", "moe_plan_residency",
                "moe_plan_profile", "moe_plan_kernel_times", "moe_plan_get_info", "moe_measure_link_ceilings",
                "moe_debug_fail_alloc", "moe_debug_live_allocs"):
@@ -237,6 +239,18 @@ class Plan:
         _check(self.lib.moe_layer_forward(self.handle, layer, T, _ptr(x), _ptr(logits_in), _ptr(y),
                                           ctypes.byref(r) if r is not None else None, _stream(stream)),
                "moe_layer_forward")
+        return y
+
+    def forward_noalloc(self, layer, x, y, logits_in=None, route=None, stream=None):
+        """forward() through moe_layer_forward_noalloc: the workspace comes from the
+        library's static per-device array, and the call allocates nothing."""
+        T = int(x.shape[0])
+        r = None
+        if route is not None:
+            r = Routing(*[_ptr(route.get(n)) for n, _ in Routing._fields_])
+        _check(self.lib.moe_layer_forward_noalloc(self.handle, layer, T, _ptr(x), _ptr(logits_in), _ptr(y),
+                                                  ctypes.byref(r) if r is not None else None, _stream(stream)),
+               "moe_layer_forward_noalloc")
         return y
 
     def cache_update(self, layer=-1, decay=0.9, max_promotions=8, overlap=False, want_resident=None, stream=None):

@@ -16,11 +16,13 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "host_logic.h"
@@ -32,6 +34,17 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_last_error;
+
+// The workspace of moe_layer_forward_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. Host code never passes its name to a
+// kernel (on the host the name is only a stand-in): each device's address comes
+// from hipGetSymbolAddress, taken once with that device current, and only that
+// address is used.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
 
 // moe_debug_fail_alloc: countdown to the device (0) / pinned host (1) allocation that fails
 std::atomic<int> g_fail_alloc[2] = {{0}, {0}};
@@ -387,6 +400,73 @@ moe_status cache_update_pipelined(moe_plan* p, int l0, int l1, double decay, int
   return MOE_OK;
 }
 
+// The device address of `scratch` on the current device `dev`, taken (and its
+// arrival counters cleared) on the first call for that device. nullptr on failure.
+uint8_t* scratch_on(int dev, std::string* why) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *why = "device index out of range for the static workspace";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    *why = std::string("hipGetSymbolAddress of the static workspace failed: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  // the routing kernels' arrival counters (the first 256 bytes) start at zero; each
+  // launch leaves them at zero again when its last block finishes
+  launch_fill32(ptr, 0u, 64, nullptr);
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    *why = std::string("clearing the static workspace failed: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  return g_scratch_ptr[dev];
+}
+
+// A forward workspace for T tokens laid out from `base` in 256-byte aligned pieces,
+// arrival counters first; returns its size (base == nullptr: the size only). The
+// prefill staging slots stay the plan's own.
+size_t carve_workspace(const moe_plan* p, int T, uint8_t* base, Workspace* w) {
+  const moe_config& c = p->cfg;
+  const size_t E = c.num_experts, A = (size_t)T * c.top_k;
+  size_t off = 0;
+  auto take = [&](auto** ptr, size_t bytes) {
+    using Ptr = std::remove_pointer_t<decltype(ptr)>;
+    *ptr = base ? reinterpret_cast<Ptr>(base + off) : nullptr;
+    off += (bytes + 255) / 256 * 256;
+  };
+  take(&w->route_cnt, 64 * sizeof(unsigned));
+  take(&w->n_active, 64 * sizeof(int32_t));
+  take(&w->n_tiles, 64 * sizeof(int32_t));
+  take(&w->logits, (size_t)T * E * sizeof(float));
+  take(&w->xsum, (size_t)T * (c.hidden / c.group_size) * sizeof(float));
+  take(&w->ids, A * sizeof(int32_t));
+  take(&w->wts, A * sizeof(float));
+  take(&w->counts, E * sizeof(int32_t));
+  take(&w->offsets, (E + 1) * sizeof(int32_t));
+  take(&w->sorted, A * sizeof(int32_t));
+  take(&w->inv, A * sizeof(int32_t));
+  take(&w->active, E * sizeof(int32_t));
+  take(&w->act_pos, E * sizeof(int32_t));
+  take(&w->work, E * sizeof(WorkDesc));
+  take(&w->aptr, A * sizeof(uint8_t*));
+  take(&w->tiles, (A / kGemmRows + E + 1) * sizeof(int2));
+  take(&w->hist, (size_t)((T + kGroupTokens - 1) / kGroupTokens) * E * sizeof(int32_t));
+  take(&w->hpart, A * (c.inter / 32) * sizeof(float));
+  take(&w->o, A * c.hidden * sizeof(float));
+  uint8_t* h = nullptr;
+  take(&h, A * c.inter * p->act_size);
+  w->h = h;
+  w->stage = p->ws.stage;
+  w->gptr = p->ws.gptr;
+  return off;
+}
+
 // Arguments of one layer's weights: router and experts given, initial HBM set within the slots.
 moe_status check_layer_args(const moe_config& c, const moe_layer_weights* w, const int32_t* initial_hbm) {
   if (!w || !w->router_w || !w->experts) return fail(MOE_E_INVALID, "router_w and experts are required");
@@ -666,6 +746,13 @@ moe_status moe_plan_create(const moe_config* cfg, const moe_layer_weights* layer
     return fail(MOE_E_HIP, "device synchronize after allocation failed");
   }
   p->pool_node = page_node(p->layers[0].host_pool);
+  {  // the static workspace of moe_layer_forward_noalloc on this device
+    std::string why;
+    if (!scratch_on(p->device, &why)) {
+      free_plan(p);
+      return fail(MOE_E_HIP, why);
+    }
+  }
   if (layers)
     for (int l = 0; l < cfg->num_layers; ++l)
       TRY(load_layer_impl(p, l, &layers[l], initial_hbm ? initial_hbm + (size_t)l * E : nullptr,
@@ -697,24 +784,20 @@ moe_status moe_plan_get_info(moe_plan* p, moe_plan_info* out) {
   out->workspace_bytes = p->workspace_bytes;
   return MOE_OK;
 }
-moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
-                             const moe_routing* ro, moe_stream stream) {
-  if (!p) return fail(MOE_E_INVALID, "plan is null");
-  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
-  if (T < 0 || T > p->cfg.max_tokens) return fail(MOE_E_INVALID, "T out of range 0..max_tokens");
-  if (T == 0) return MOE_OK;
-  if (!x || !y) return fail(MOE_E_INVALID, "x and y are required");
-  if (!aligned16(x) || !aligned16(y) || (logits_in && !aligned16(logits_in)))
-    return fail(MOE_E_INVALID, "x, y and logits_in must be 16-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// The forward of moe_layer_forward on the workspace `w` (the plan's, or one carved
+// from the static scratch array for moe_layer_forward_noalloc).
+moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
+                        const moe_routing* ro, hipStream_t s, Workspace& w, bool own_ws) {
   Layer& ly = p->layers[layer];
-  if (!ly.loaded) return fail(MOE_E_INVALID, "layer not loaded");
   const moe_config& c = p->cfg;
   const int E = c.num_experts, H = c.hidden, I = c.inter, k = c.top_k, G = c.group_size;
   const int bf16 = c.act_dtype == MOE_ACT_BF16;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Workspace& w = p->ws;
   const int A = T * k;
-  if (p->debug_ws >= 2) poison_workspace(p, s);
+  if (own_ws && p->debug_ws >= 2) poison_workspace(p, s);
   WsTrack trk;
 #define LAUNCH_USES(kernel, reads, writes) \
   if (!trk.launch(kernel, reads, writes)) return fail(MOE_E_STATE, "internal dispatch error: " + trk.err)
@@ -985,6 +1068,47 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
     if (ro->inv) HIP_TRY(hipMemcpyAsync(ro->inv, w.inv, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, s));
   }
   return MOE_OK;
+}
+
+// Arguments shared by both forward entry points.
+moe_status check_forward_args(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
+                              const float* y) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (T < 0 || T > p->cfg.max_tokens) return fail(MOE_E_INVALID, "T out of range 0..max_tokens");
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_E_INVALID, "x and y are required");
+  if (!aligned16(x) || !aligned16(y) || (logits_in && !aligned16(logits_in)))
+    return fail(MOE_E_INVALID, "x, y and logits_in must be 16-byte aligned");
+  if (!p->layers[layer].loaded) return fail(MOE_E_INVALID, "layer not loaded");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
+                             const moe_routing* ro, moe_stream stream) {
+  moe_status st = check_forward_args(p, layer, T, x, logits_in, y);
+  if (st != MOE_OK || T == 0) return st;
+  return forward_impl(p, layer, T, x, logits_in, y, ro, static_cast<hipStream_t>(stream), p->ws, true);
+}
+
+moe_status moe_layer_forward_noalloc(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
+                                     float* y, const moe_routing* ro, moe_stream stream) {
+  moe_status st = check_forward_args(p, layer, T, x, logits_in, y);
+  if (st != MOE_OK || T == 0) return st;
+  Workspace w{};
+  const size_t need = carve_workspace(p, T, nullptr, &w);
+  if (need > kScratchBytes)
+    return fail(MOE_E_INVALID, "the workspace of this forward needs " + std::to_string(need) +
+                                   " bytes, more than the static workspace's " + std::to_string(kScratchBytes));
+  std::string why;
+  uint8_t* base = scratch_on(p->device, &why);  // set up by moe_plan_create on this device
+  if (!base) return fail(MOE_E_HIP, why);
+  carve_workspace(p, T, base, &w);
+  return forward_impl(p, layer, T, x, logits_in, y, ro, static_cast<hipStream_t>(stream), w, false);
 }
 
 moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* pol, moe_stream stream) {

@@ -220,6 +220,23 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
                              const float* logits_in, float* y, const moe_routing* route_out,
                              moe_stream stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. The
+ * same kernels and results (bitwise), with the forward's workspace (logits,
+ * routing tables, work descriptors, the intermediate h and the down outputs)
+ * carved from a static device array of the library instead of the plan's
+ * workspace; the call allocates nothing. The array holds 8 MiB per device
+ * (held until the process ends), which covers decode batches (a
+ * H7168/I2048/E384/k6 layer: about 200 KiB per token). One array serves every
+ * plan on a device and keeps the last call's contents: calls on one GPU that
+ * overlap in time (different streams, or host threads) race, so order them.
+ * The plan itself (weights, tables, counters) is created as usual.
+ * Errors: as moe_layer_forward; MOE_E_INVALID also when this forward's workspace
+ * exceeds 8 MiB (the message gives the bytes needed). */
+moe_status moe_layer_forward_noalloc(moe_plan* plan, int32_t layer, int32_t T, const void* x,
+                                     const float* logits_in, float* y, const moe_routing* route_out,
+                                     moe_stream stream);
+
 /* Expert-cache update of one layer (or all, layer = -1). [24K] section 二: free
  * VRAM holds the most used experts, and the cache adapts the longer it runs; the
  * pages give no policy, so the plain frequency reading is taken:
