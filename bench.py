@@ -2,31 +2,36 @@
 """Benchmark of the routed MoE FFN layer forward on one MI355X.
 
 A step is one forward of one layer (router -> top-k -> grouping by expert ->
-gate/up + SwiGLU -> down -> combine) for a batch of tokens. Steps walk through
-a stack of seeded layers (default 24), so that the experts a step reads were
-last read many steps (hundreds of MB) earlier and are not served from the
-256 MB Infinity Cache; every input is resident in HBM (or, for offloaded
-experts, in pinned host memory) before timing starts.
+gate/up + SwiGLU -> down -> combine) for one batch of seeded synthetic tokens.
+Steps walk through a stack of distinct seeded layers, so that the experts a step
+reads were last read hundreds of MB earlier and are not served from the 256 MB
+Infinity Cache; every input is resident (in HBM, or for offloaded experts in
+pinned host memory) before timing starts.
 
-Workloads (--workload):
-  decode    Qwen3-30B-A3B-shaped layer (H2048 I768 E128 k8 G128 bf16, Zipf bias
-            alpha 0.8), all experts in HBM; --batch 1 (default) or 4.
-  deepseek  H7168 I2048 E384 k6 G128 bf16, Zipf alpha 1.0, 70% of experts in HBM
-            and the coldest 30% read from host memory (--plan mixed | hbm | host).
-  prefill   the Qwen3 layer shape with 2048 (or --batch) tokens, bias-free routing.
-  cache     expert-cache decode run: 48 stacked Qwen3-shaped layers (Zipf alpha 0.8,
-            seeded per layer), HBM slots for 70% of each layer's experts, the rest read
-            from host memory; 256 single-token steps, a pipelined cache update after every step
-            from a cold start (slots hold experts 0..89), beside the static coldest-on-host
-            plan without updates. value = full-stack tokens/s.
-
-Prints one JSON line. value = layer-tokens/s over exactly --steps timed steps.
+The printed line (one JSON object) carries the headline workload, the
+DeepSeek-style layer (H7168 I2048 E384 k6, int4 G128, Zipf alpha 1.0) on its 70/30
+plan (the 115 coldest experts read in place from host memory) at batch 1, with
+--steps timed steps after --warmup untimed ones, 4 layers rotated. Nested under
+"configs", each with its own roofline and CPU-oracle baseline:
+  deepseek  the same layers on the 70/30, all-HBM and all-host plans at batches 1, 4, 16
+            (residency switched by moe_cache_update with want_resident)
+  qwen3     the Qwen3-30B-A3B-shaped layer (H2048 I768 E128 k8, alpha 0.8), all in HBM,
+            batches 1 and 4, 24 layers rotated
+  prefill   the Qwen3 layer shape at 2048 and 1024 tokens, bias-free routing, 4 layers
+  cache     48 stacked Qwen3-shaped layers, 90 HBM slots per layer, 256 single-token steps
+            from a cold start with a pipelined cache update after every step, beside the
+            static coldest-on-host plan (value: full-stack tokens/s)
+plus the measured link ceilings (streaming reads of HBM and of host-mapped memory,
+DMA host -> device) and where the host pool sits (NUMA).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -38,211 +43,454 @@ HBM_PEAK_GBS = 8000.0
 HOST_LINK_PEAK_GBS = 63.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 
+DIMS = {
+    "deepseek": dict(H=7168, I=2048, E=384, k=6, G=128, alpha=1.0, seed=2),
+    "qwen3": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.8, seed=1),
+    "prefill": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.0, seed=4),
+    "cache": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.8, seed=3),
+}
+NAMES = {"deepseek": "DeepSeek-style layer", "qwen3": "Qwen3-30B-A3B-shaped layer",
+         "prefill": "Qwen3-30B-A3B-shaped prefill", "cache": "expert-cache run"}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def workload_dims(args):
-    if args.workload in ("decode", "prefill", "cache"):
-        return dict(H=2048, I=768, E=128, k=8, G=128, act="bf16", alpha=0.0 if args.workload == "prefill" else 0.8,
-                    seed={"decode": 1, "prefill": 4, "cache": 3}[args.workload])
-    if args.workload == "deepseek":
-        return dict(H=7168, I=2048, E=384, k=6, G=128, act="bf16", alpha=1.0, seed=2)
-    raise SystemExit("unknown workload")
-
-
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 200, prefill 40, cache 256)")
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "deepseek", "prefill", "cache"])
-    ap.add_argument("--batch", type=int, default=None)
-    ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--plan", default="mixed", choices=["mixed", "hbm", "host"])
-    ap.add_argument("--sweep", default=None,
-                    help="comma list of plan:batch runs on the same generated layers, one JSON line each")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--max-promotions", type=int, default=8, help="cache workload: promotions per layer per update")
-    ap.add_argument("--decay", type=float, default=0.9, help="cache workload: score decay per update")
+    ap.add_argument("--steps", type=int, default=100, help="timed steps per decode/prefill measurement")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="deepseek,qwen3,prefill,cache",
+                    help="comma list of the workloads to run (the first one run gives the top-level line)")
+    ap.add_argument("--deepseek-layers", type=int, default=4)
+    ap.add_argument("--deepseek-runs", default="mixed:1,mixed:4,mixed:16,hbm:1,hbm:4,hbm:16,host:1,host:4,host:16",
+                    help="plan:batch runs of the DeepSeek-style layer, in order (plans mixed, hbm, host)")
+    ap.add_argument("--qwen3-layers", type=int, default=24)
+    ap.add_argument("--prefill-layers", type=int, default=4)
+    ap.add_argument("--cache-steps", type=int, default=256)
+    ap.add_argument("--max-promotions", type=int, default=8, help="cache run: promotions per layer per update")
+    ap.add_argument("--decay", type=float, default=0.9, help="cache run: score decay per update")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="CPU oracle time budget per configuration")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--copy-mb", type=float, default=None,
                     help="only run 10 device-to-device copies of this many MiB (a plain copy kernel of known "
                          "size, for scaling the memory counters of a profiler run), then exit")
-    ap.add_argument("--gemm-min-tokens", type=int, default=0,
-                    help="batches of at least this many tokens take the grouped MFMA GEMM (0: the library default)")
-    ap.add_argument("--stage-slots", type=int, default=0,
-                    help="prefill: HBM staging slots for the offloaded experts a batch touches (0 = read in place)")
-    ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
 
 
-def make_layers(d, L, keep_blobs):
+# ----------------------------------------------------------------------------- inputs
+
+
+def gen_layers(wl, n_layers):
     import synth
-    H, I, E, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "G", "act", "alpha", "seed"))
-    layers, t0 = [], time.time()
-    for l in range(L):
-        blobs = synth.expert_blobs(seed, l, 0, E, H, I, G)
-        Wr = synth.router_weight(seed, l, E, H, act)
-        b = synth.router_bias(seed, l, E, alpha)
-        layers.append(dict(Wr=Wr, b=b, blobs=blobs))
-        log("layer %d/%d generated (%.1fs)" % (l + 1, L, time.time() - t0))
-    return layers
+    d = DIMS[wl]
+    out, t0 = [], time.time()
+    for l in range(n_layers):
+        out.append(dict(Wr=synth.router_weight(d["seed"], l, d["E"], d["H"], "bf16"),
+                         b=synth.router_bias(d["seed"], l, d["E"], d["alpha"]),
+                         blobs=synth.expert_blobs(d["seed"], l, 0, d["E"], d["H"], d["I"], d["G"])))
+        log("%s: layer %d/%d generated (%.1fs)" % (wl, l + 1, n_layers, time.time() - t0))
+    return out
 
 
-def measured_traffic(kernel, workload, plan, batch):
-    """DRAM-side bytes per launch of `kernel` from a committed counter summary
-    (profiles/*_traffic.md, a `traffic:` line), or None when there is none for this
-    workload or the kernel's sources have changed since the counters were taken."""
-    import glob
-    import hashlib
+def device_inputs(wl, B, n):
+    """n seeded activation batches [B, H] (bf16) on the device, and their host bits."""
+    import numpy as np
+    import torch
+    import synth
+    d = DIMS[wl]
+    bits = [synth.activations(d["seed"], 1000 + 97 * B + i, B, d["H"], "bf16") for i in range(n)]
+    dev = [torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).cuda() for b in bits]
+    return dev, bits
 
+
+# ----------------------------------------------------------------------------- rooflines
+
+
+def measured_traffic(kernels, key):
+    """DRAM-side bytes per step of `kernels` (kernel classes, summed) from committed
+    counter summaries (profiles/*_traffic.md `traffic:` lines for the configuration
+    `key`), or None when one is missing or a kernel's sources have changed since the
+    counters were taken."""
     csrc = os.path.join(ROOT, "expert_offloaded_ffn_moe_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
-        for line in open(f, encoding="utf-8"):
-            if not line.startswith("traffic:"):
-                continue
-            kv = dict(t.split("=", 1) for t in line.split()[1:])
-            if (kv.get("kernel"), kv.get("workload"), kv.get("plan"), kv.get("batch")) != (
-                    kernel, workload, plan, str(batch)):
-                continue
-            h = hashlib.sha256()
-            for src in kv["sources"].split(","):
-                with open(os.path.join(csrc, src), "rb") as fh:
-                    h.update(fh.read())
-            if h.hexdigest()[:16] == kv["sha256_16"]:
-                return int(kv["bytes_per_launch"])
-    return None
+    total = 0
+    for kern in kernels:
+        found = None
+        for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+            for line in open(f, encoding="utf-8"):
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if (kv.get("kernel"), kv.get("config")) != (kern, key):
+                    continue
+                h = hashlib.sha256()
+                for src in kv["sources"].split(","):
+                    with open(os.path.join(csrc, src), "rb") as fh:
+                        h.update(fh.read())
+                if h.hexdigest()[:16] == kv["sha256_16"]:
+                    found = int(kv["bytes_per_launch"])
+        if found is None:
+            return None
+        total += found
+    return total
 
 
-def roofline(per_kernel, bytes_hbm, bytes_host, assignments, H, I):
-    """Roofline of the dominant expert kernel (largest total time over the profiled pass).
-
-    Expert kernels move weight bytes: gate/up reads 2/3 of each touched expert's bytes,
-    down 1/3. With every touched expert in HBM the peak is HBM's; with every one on the
-    host it is the host link's; with both, the peak is the rate at which those bytes would
-    move with each link at its own peak (time = hbm bytes / HBM + host bytes / link).
-    GEMM kernels are also priced in flops against bf16 MFMA: 2*A*H*2I for gate/up, 2*A*I*H
-    for down, with A = T*k routed token rows. A GEMM launch reports the bound it comes
-    closer to (flops for large batches, weight bytes for small ones), the other under
-    "other".
-    """
-    ffn = [n for n in ("gateup", "down", "gemm_gateup", "gemm_down", "stage") if n in per_kernel]
-    dom = max(ffn, key=lambda n: per_kernel[n]["avg_us"] * per_kernel[n]["launches"])
-    t = per_kernel[dom]["avg_us"] * 1e-6
-    staged = "stage" in per_kernel
-    if dom == "stage":  # the staging copy moves the touched offloaded experts over the host link once
-        hb, sb = 0.0, bytes_host
-    elif staged:  # the GEMMs then read every touched expert from HBM
-        share = 2.0 / 3.0 if dom == "gemm_gateup" else 1.0 / 3.0
-        hb, sb = share * (bytes_hbm + bytes_host), 0.0
-    else:
-        share = 2.0 / 3.0 if dom in ("gateup", "gemm_gateup") else 1.0 / 3.0
-        hb, sb = share * bytes_hbm, share * bytes_host
+def link_peak(hb, sb):
+    """(bound, peak GB/s) for hb HBM bytes and sb host-link bytes moved by one launch: the
+    rate at which those bytes would move with each link at its own peak."""
     if sb == 0:
-        bound, peak = "hbm", HBM_PEAK_GBS
-    elif hb == 0:
-        bound, peak = "host-link", HOST_LINK_PEAK_GBS
-    else:
-        bound = "hbm+host-link"
-        peak = (hb + sb) / (hb / HBM_PEAK_GBS + sb / HOST_LINK_PEAK_GBS)
+        return "hbm", HBM_PEAK_GBS
+    if hb == 0:
+        return "host-link", HOST_LINK_PEAK_GBS
+    return "hbm+host-link", (hb + sb) / (hb / HBM_PEAK_GBS + sb / HOST_LINK_PEAK_GBS)
+
+
+def roofline(per_kernel, bytes_hbm, bytes_host, A, H, I, key, staged=False):
+    """Roofline of the expert FFN of one step: gate/up + down summed (the GEMV pair on the
+    decode path, the grouped GEMM pair on the MFMA path). Algorithmic work per step: the
+    canonical bytes of every unique expert the step touches (split by the link it is read
+    over) and, for the GEMMs, 2*A*3*H*I flops (A = T*k routed rows). The GEMM pair reports
+    the bound it comes closer to (flops at prefill sizes, weight bytes for small batches),
+    the other under "other". Routing (router logits, top-k, grouping) is reported beside
+    it under "route_us", and the whole step under "step_us"."""
+    gemm = "gemm_gateup" in per_kernel
+    pair = ["gemm_gateup", "gemm_down"] if gemm else ["gateup", "down"]
+    names = {"gateup": "k_gateup", "down": "k_down_comb16/k_down_comb/k_down", "gemm_gateup": "k_gemm<gate/up>",
+             "gemm_down": "k_gemm<down>"}
+    t_us = sum(per_kernel[n]["avg_us"] for n in pair if n in per_kernel)
+    t = t_us * 1e-6
+    hb, sb = (float(bytes_hbm + bytes_host), 0.0) if staged else (float(bytes_hbm), float(bytes_host))
+    bound, peak = link_peak(hb, sb)
     achieved = (hb + sb) / t / 1e9
-    by_bytes = dict(bound=bound, kernel=dom, achieved=round(achieved, 1), peak=round(peak, 1), unit="GB/s",
-                    frac=round(achieved / peak, 4), traffic=None, alg_bytes_per_launch=int(hb + sb),
-                    alg_bytes_hbm=int(hb), alg_bytes_host=int(sb), avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
-    if not dom.startswith("gemm"):
+    by_bytes = dict(bound=bound, kernel=" + ".join(names[n] for n in pair), achieved=round(achieved, 1),
+                    peak=round(peak, 1), unit="GB/s", frac=round(achieved / peak, 4), traffic=None,
+                    alg_bytes_per_launch=int(hb + sb), alg_bytes_hbm=int(hb), alg_bytes_host=int(sb),
+                    avg_launch_us=round(t_us, 3))
+    route_us = sum(per_kernel[n]["avg_us"] for n in ("router", "route", "stage") if n in per_kernel)
+    step_us = sum(v["avg_us"] * v["launches"] for v in per_kernel.values()) / max(
+        1, per_kernel[pair[0]]["launches"])
+    extra = dict(route_us=round(route_us, 3), step_us=round(step_us, 3),
+                 kernels_us={n: round(v["avg_us"], 3) for n, v in per_kernel.items()})
+    traffic = measured_traffic(pair, key)
+    by_bytes["traffic"] = traffic
+    if not gemm:
+        by_bytes.update(extra)
         return by_bytes
-    flops = 2.0 * assignments * H * I * (2 if dom == "gemm_gateup" else 1)
+    flops = 2.0 * A * 3 * H * I
     tf = flops / t / 1e12
-    by_flops = dict(bound="mfma", kernel=dom, achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None, alg_flops_per_launch=int(flops),
-                    avg_launch_us=round(per_kernel[dom]["avg_us"], 3))
+    by_flops = dict(bound="mfma", kernel=by_bytes["kernel"], achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                    alg_flops_per_launch=int(flops), avg_launch_us=round(t_us, 3))
     main, other = (by_flops, by_bytes) if by_flops["frac"] >= by_bytes["frac"] else (by_bytes, by_flops)
     main["other"] = {k: other[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    main.update(extra)
     return main
 
 
-def run_one(args, d, layers, B, plan_kind, steps, warmup):
-    """Time `steps` forwards (layer i mod L) at batch B under one residency plan."""
-    import numpy as np
+# ----------------------------------------------------------------------------- measurement
+
+
+def time_steps(plan, n_layers, xs, y, steps, warmup):
+    """Warm-up, then exactly `steps` timed forwards (layer i mod n_layers, input i mod
+    len(xs)) between two device synchronisations; then a second pass of the same steps
+    with the dispatch's own HIP events for the per-kernel times. Returns (seconds,
+    stats of the timed pass, {kernel: launches, avg_us})."""
     import torch
-
-    import expert_offloaded_ffn_moe_amd as moe
-    import synth
-
-    H, I, E, k, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "k", "G", "act", "alpha", "seed"))
-    L = len(layers)
-    eb = synth.expert_bytes(H, I, G)
-    slots = {"mixed": int(round(0.7 * E)), "hbm": E, "host": 0}[plan_kind]
-    cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=slots,
-                          gemm_min_tokens=args.gemm_min_tokens, prefill_stage_slots=args.stage_slots)
-    plan = moe.Plan(cfg)
-    for l, ly in enumerate(layers):
-        res = synth.coldest_host_plan(seed, l, E, slots / E) if plan_kind == "mixed" else None
-        plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], res)
-    n_in = min(warmup + steps, 64)
-    xs_bits = [synth.activations(seed, 1000 + i, B, H, act) for i in range(n_in)]
-    xs = [torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda() for xb in xs_bits]
-    y = torch.empty((B, H), device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i):
-        plan.forward(i % L, xs[i % len(xs)], y, stream=stream)
+        plan.forward(i % n_layers, xs[i % len(xs)], y, stream=stream)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     plan.reset_stats()
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
+    t0 = time.perf_counter()
     for i in range(steps):
         step(warmup + i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    elapsed = time.perf_counter() - t0
     st = plan.stats(-1)
-    log("timed %d steps in %.4fs (plan %s, batch %d)" % (steps, elapsed, plan_kind, B))
-
-    # profiled pass: per-kernel times from events stamped by each dispatch
     plan.profile(True)
     for i in range(steps):
         step(warmup + i)
     kt = plan.kernel_times()
     plan.profile(False)
-    plan.destroy()
+    per_kernel = {n: dict(launches=v[0], avg_us=v[1] * 1e3 / v[0]) for n, v in kt.items() if v[0]}
+    return elapsed, st, per_kernel
 
-    ms_per_step = elapsed * 1e3 / steps
+
+def layer_result(wl, key, B, plan_kind, n_layers, steps, warmup, elapsed, st, per_kernel, slots):
+    d = DIMS[wl]
+    import synth
+    eb = synth.expert_bytes(d["H"], d["I"], d["G"])
     fwd = max(st["forwards"], 1)
-    bytes_hbm, bytes_host = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
-    per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
-    roof = roofline(per_kernel, bytes_hbm, bytes_host, B * k, H, I)
-    roof["traffic"] = measured_traffic(roof["kernel"], args.workload, plan_kind, B)
-    name = {"decode": "Qwen3-30B-A3B-shaped decode", "deepseek": "DeepSeek-style decode",
-            "prefill": "Qwen3-30B-A3B-shaped prefill"}[args.workload]
+    bh, bs = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
+    ms = elapsed * 1e3 / steps
+    roof = roofline(per_kernel, bh, bs, B * d["k"], d["H"], d["I"], key)
     return {
-        "metric": METRIC,
-        "value": round(B * steps / elapsed, 2),
-        "unit": "layer-tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "%s layer H%d I%d E%d k%d int4 G%d, batch %d, %d-layer rotation, plan %s" % (
-            name, H, I, E, k, G, B, L, plan_kind), "hbm_slots": slots, "prefill_stage_slots": args.stage_slots,
-            "alpha": alpha, "seed": seed},
+        "value": round(B * steps / elapsed, 2), "unit": "layer-tokens/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "workload": "%s H%d I%d E%d k%d int4 G%d, batch %d, plan %s (%d of %d experts in HBM), %d layers rotated"
+                    % (NAMES[wl], d["H"], d["I"], d["E"], d["k"], d["G"], B, plan_kind, slots, d["E"], n_layers),
         "roofline": roof,
-        "layer": {"expert_bytes_per_step_hbm": int(bytes_hbm), "expert_bytes_per_step_host": int(bytes_host),
-                  "unique_experts_per_step": round((bytes_hbm + bytes_host) / eb, 3),
-                  "layer_GBps_wall": round((bytes_hbm + bytes_host) / (ms_per_step * 1e-3) / 1e9, 1),
-                  "host_link_GBps_wall": round(bytes_host / (ms_per_step * 1e-3) / 1e9, 2),
-                  "hit_rate": round(st["hits"] / max(st["hits"] + st["misses"], 1), 5),
-                  "kernels_us": {n: round(v["avg_us"], 3) for n, v in per_kernel.items()}},
-        "_xs_bits": xs_bits,
+        "layer": {"expert_bytes_per_step_hbm": int(bh), "expert_bytes_per_step_host": int(bs),
+                  "unique_experts_per_step": round((bh + bs) / eb, 3),
+                  "layer_GBps_wall": round((bh + bs) / (ms * 1e-3) / 1e9, 1),
+                  "host_link_GBps_wall": round(bs / (ms * 1e-3) / 1e9, 2),
+                  "hit_rate": round(st["hits"] / max(st["hits"] + st["misses"], 1), 5)},
     }
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+
+
+def cpu_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwards=1, label=None, threads=None):
+    """The CPU oracle (float64 NumPy, unmodified) on a bounded sample of the same
+    workload: forwards of the given batches through the first two layers, until
+    `seconds` have passed (at least one). tokens: evaluate y only for these token rows of
+    each batch (routing still covers all), with the rate scaled to those rows. BLAS
+    threads are pinned to the cores this process may run on (or to `threads`)."""
+    import threadpoolctl
+    from oracle import moe_oracle as O
+    d = DIMS[wl]
+    cores = threads or cpu_cores()
+    n_l = min(2, len(layers))
+    done_tokens, n, t0 = 0, 0, time.perf_counter()
+    with threadpoolctl.threadpool_limits(limits=cores):
+        while n == 0 or time.perf_counter() - t0 < seconds:
+            ly = layers[n % n_l]
+            xb = batches_bits[n % len(batches_bits)]
+            O.layer_forward(O.bf16_bits_to_f64(xb), O.bf16_bits_to_f64(ly["Wr"]), ly["b"], ly["blobs"], d["H"],
+                            d["I"], d["E"], d["k"], d["G"], "bf16", tokens=tokens)
+            done_tokens += len(tokens) if tokens is not None else xb.shape[0]
+            n += 1
+    el = time.perf_counter() - t0
+    rate = done_tokens / el
+    sample = "%d forwards%s over %d of the layers, %.1fs (float64 NumPy oracle, %d BLAS threads)" % (
+        n, "" if tokens is None else " (y of %d token rows each)" % len(tokens), n_l, el, cores)
+    unit = "layer-tokens/s"
+    if per_step_forwards > 1:
+        rate /= per_step_forwards
+        unit = "tokens/s"
+        sample += "; scaled to full %d-layer steps" % per_step_forwards
+    if label:
+        sample += "; " + label
+    return {"value": round(rate, 5), "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+
+def run_deepseek(args, out):
+    """The DeepSeek-style layers, one plan with an HBM slot for every expert; the 70/30,
+    all-HBM and all-host residency sets are switched by moe_cache_update(want_resident)."""
+    import numpy as np
+    import torch
+    import expert_offloaded_ffn_moe_amd as moe
+    import synth
+    d = DIMS["deepseek"]
+    L = args.deepseek_layers
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=16,
+                          hbm_slots=d["E"])
+    plan = moe.Plan(cfg)
+    mixed = np.stack([synth.coldest_host_plan(d["seed"], l, d["E"], 0.7) for l in range(L)])
+    kept = None
+    for l, ly in enumerate(gen_layers("deepseek", L)):
+        plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], mixed[l])
+        if l == 0:
+            kept = [ly]
+    info = plan.info()
+    xs = {B: device_inputs("deepseek", B, min(args.warmup + args.steps, 64)) for B in (1, 4, 16)}
+    y = torch.empty((16, d["H"]), device="cuda")
+    res = {}
+    wants = {"mixed": mixed, "hbm": np.ones_like(mixed), "host": np.zeros_like(mixed)}
+    current = "mixed"
+    for item in args.deepseek_runs.split(","):
+        kind, B = item.split(":")
+        B = int(B)
+        if kind != current:
+            plan.cache_update(-1, want_resident=wants[kind])
+            current = kind
+        slots = int(wants[kind][0].sum())
+        steps = args.steps if kind != "host" else max(4, min(args.steps, 20))  # ~20 ms per all-host step at 16
+        el, st, pk = time_steps(plan, L, xs[B][0], y[:B], steps, args.warmup)
+        key = "deepseek_%s_b%d" % (kind, B)
+        r = layer_result("deepseek", key, B, kind, L, steps, args.warmup, el, st, pk, slots)
+        log("deepseek %s B%d: %.1f layer-tokens/s, %s" % (kind, B, r["value"], r["roofline"]["frac"]))
+        res[key] = r
+    plan.destroy()
+    if not args.no_cpu:
+        for B in (1, 4, 16):
+            keys = [key for key in res if key.endswith("_b%d" % B)]
+            if not keys:
+                continue
+            toks = [0, 1] if B == 16 else None
+            cb = cpu_baseline("deepseek", kept, xs[B][1][:4], args.cpu_seconds, tokens=toks,
+                              label="the oracle evaluates only the routed experts, so residency does not change it")
+            for key in keys:
+                res[key]["cpu_baseline"] = cb
+    out.update(res)
+    return {"plan_info": info}
+
+
+def run_qwen3(args, out):
+    import torch
+    import expert_offloaded_ffn_moe_amd as moe
+    d = DIMS["qwen3"]
+    L = args.qwen3_layers
+    layers = gen_layers("qwen3", L)
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=4,
+                          hbm_slots=d["E"])
+    plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in layers])
+    y = torch.empty((4, d["H"]), device="cuda")
+    res = {}
+    for B in (1, 4):
+        xs, bits = device_inputs("qwen3", B, min(args.warmup + args.steps, 64))
+        el, st, pk = time_steps(plan, L, xs, y[:B], args.steps, args.warmup)
+        r = layer_result("qwen3", "qwen3_hbm_b%d" % B, B, "hbm", L, args.steps, args.warmup, el, st, pk, d["E"])
+        log("qwen3 B%d: %.1f layer-tokens/s, %s" % (B, r["value"], r["roofline"]["frac"]))
+        if not args.no_cpu:
+            r["cpu_baseline"] = cpu_baseline("qwen3", layers, bits[:4], args.cpu_seconds)
+            if B == 1:
+                r["cpu_baseline"]["value_one_thread"] = cpu_baseline("qwen3", layers, bits[:4], args.cpu_seconds,
+                                                                     threads=1)["value"]
+        res["qwen3_hbm_b%d" % B] = r
+    plan.destroy()
+    out.update(res)
+
+
+def run_prefill(args, out):
+    import torch
+    import expert_offloaded_ffn_moe_amd as moe
+    d = DIMS["prefill"]
+    L = args.prefill_layers
+    layers = gen_layers("prefill", L)
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=2048,
+                          hbm_slots=d["E"])
+    plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in layers])
+    y = torch.empty((2048, d["H"]), device="cuda")
+    res = {}
+    steps = max(4, min(args.steps, 40))
+    for T in (2048, 1024):
+        xs, bits = device_inputs("prefill", T, 4)
+        el, st, pk = time_steps(plan, L, xs, y[:T], steps, min(args.warmup, 5))
+        r = layer_result("prefill", "prefill_t%d" % T, T, "hbm", L, steps, min(args.warmup, 5), el, st, pk, d["E"])
+        r["unit"] = "layer-tokens/s"
+        log("prefill T%d: %.0f layer-tokens/s, %s" % (T, r["value"], r["roofline"]["frac"]))
+        if not args.no_cpu:
+            r["cpu_baseline"] = cpu_baseline("prefill", layers, bits[:1], args.cpu_seconds, tokens=list(range(8)))
+        res["prefill_t%d" % T] = r
+    plan.destroy()
+    out.update(res)
+
+
+def run_cache(args, out):
+    """Expert-cache decode run over the stacked layers: the static coldest-on-host plan
+    (warm-up steps, then the timed steps, no updates), then the cached plan from its cold
+    start (slots hold experts 0..89) with a pipelined cache update after every step. One
+    step = one token through every layer; each (step, layer) takes its own seeded
+    activations (the bench's inputs, also checked against the oracle by the GPU tests)."""
+    import numpy as np
+    import torch
+    import expert_offloaded_ffn_moe_amd as moe
+    import synth
+    d = DIMS["cache"]
+    H, I, E, k, G = d["H"], d["I"], d["E"], d["k"], d["G"]
+    L, B, steps, warmup = 48, 1, args.cache_steps, args.warmup
+    S = int(round(0.7 * E))
+    layers = gen_layers("cache", L)
+    n_x = (warmup + steps) * L
+    xb = synth.activations(d["seed"], 7000, n_x * B, H, "bf16")
+    xs = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda().view(n_x, B, H)
+    y = torch.empty((B, H), device="cuda")
+    modes = {}
+    for mode in ("static", "cache"):
+        cfg = moe.make_config(H, I, E, k, G, "bf16", num_layers=L, max_tokens=B, hbm_slots=S)
+        init = (np.stack([synth.coldest_host_plan(d["seed"], l, E, S / E) for l in range(L)]) if mode == "static"
+                else None)
+        plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in layers], initial_hbm=init)
+        torch.cuda.synchronize()
+        first = 0
+        if mode == "static":
+            for i in range(warmup):
+                for l in range(L):
+                    plan.forward(l, xs[i * L + l], y)
+            torch.cuda.synchronize()
+            plan.reset_stats()
+            first = warmup
+        times = []
+        t_all = time.perf_counter()
+        for i in range(first, first + steps):
+            t0 = time.perf_counter()
+            for l in range(L):
+                plan.forward(l, xs[i * L + l], y)
+            if mode == "cache":
+                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
+            else:
+                torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_all
+        st = plan.stats(-1)
+        log("cache run, %s plan: %d steps x %d layers in %.3fs, hit rate %.4f" % (
+            mode, steps, L, elapsed, st["hits"] / max(st["hits"] + st["misses"], 1)))
+        plan.profile(True)  # per-kernel times over a further 16 steps in the same mode
+        for i in range(first, first + min(16, steps)):
+            for l in range(L):
+                plan.forward(l, xs[i * L + l], y)
+            if mode == "cache":
+                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
+        kt = plan.kernel_times()
+        plan.profile(False)
+        plan.destroy()
+        t = np.sort(np.array(times))
+        fwd = max(st["forwards"], 1)
+        pk = {n: dict(launches=v[0], avg_us=v[1] * 1e3 / v[0]) for n, v in kt.items() if v[0]}
+        modes[mode] = dict(
+            tokens_per_s=round(B * steps / elapsed, 2), step_ms_median=round(float(np.median(t)) * 1e3, 4),
+            step_ms_p95=round(float(np.percentile(t, 95)) * 1e3, 4),
+            tokens_per_s_median=round(B / float(np.median(t)), 2),
+            tokens_per_s_p5=round(B / float(np.percentile(t, 95)), 2),
+            hit_rate=round(st["hits"] / max(st["hits"] + st["misses"], 1), 5), hits=st["hits"], misses=st["misses"],
+            bytes_hbm_per_layer_step=int(st["bytes_hbm"] / fwd), bytes_host_per_layer_step=int(st["bytes_host"] / fwd),
+            bytes_copied=st["bytes_copied"], promotions=st["promotions"], evictions=st["evictions"],
+            roofline=roofline(pk, st["bytes_hbm"] / fwd, st["bytes_host"] / fwd, B * k, H, I, "cache_48_layers"))
+    c = modes["cache"]
+    r = {"value": c["tokens_per_s"], "unit": "tokens/s", "steps": steps, "warmup": 0,
+         "ms_per_step": round(1e3 * B / c["tokens_per_s"], 5),
+         "workload": "%s: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d int4 G%d, %d HBM slots per layer "
+                     "(rest host-mapped), batch %d, %d steps, cold start, pipelined cache update after every step "
+                     "(max %d promotions per layer, score decay %g)" % (
+                         NAMES["cache"], L, H, I, E, k, G, S, B, steps, args.max_promotions, args.decay),
+         "roofline": c.pop("roofline"), "cache_run": c, "static_plan": modes["static"]}
+    if not args.no_cpu:
+        # 2 steps x 48 layers of the same inputs, extrapolated to full steps
+        cb = cpu_baseline("cache", layers[:2], [xb[(i * L) * B:(i * L + 1) * B] for i in range(4)], args.cpu_seconds,
+                          per_step_forwards=L, label="extrapolated from forwards of single layers")
+        r["cpu_baseline"] = cb
+    out["cache_48_layers"] = r
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def topology():
+    try:
+        txt = subprocess.run(["rocm-smi", "--showtopo"], capture_output=True, text=True, timeout=30).stdout
+        numa = [ln.strip() for ln in txt.splitlines() if "Numa" in ln or "NUMA" in ln]
+    except Exception as e:  # rocm-smi is only informative here
+        numa = ["rocm-smi --showtopo unavailable: %s" % e]
+    nodes = sorted(glob.glob("/sys/devices/system/node/node[0-9]*"))
+    return {"host_numa_nodes": len(nodes), "rocm_smi_numa": numa[:8], "cpu_cores_available": cpu_cores()}
 
 
 def main():
@@ -265,184 +513,54 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 10}), flush=True)
         return
-    d = workload_dims(args)
-    if args.steps is None:
-        args.steps = {"decode": 200, "deepseek": 200, "prefill": 40, "cache": 256}[args.workload]
-    L = args.layers or {"decode": 24, "deepseek": 3, "prefill": 4, "cache": 48}[args.workload]
-    layers = make_layers(d, L, keep_blobs=True)
-    if args.workload == "cache":
-        out, xs_bits = run_cache(args, d, layers)
-        if not args.no_cpu:
-            cb = cpu_baseline(args, d, args.batch or 1, L, layers, xs_bits)
-            cb["value"] = round(cb["value"] / L, 6)
-            cb["unit"] = "tokens/s"
-            cb["sample"] += "; value scaled to full %d-layer steps" % L
-            out["cpu_baseline"] = cb
-        print(json.dumps(out), flush=True)
-        return
-    default_plan = args.plan if args.workload == "deepseek" else "hbm"
-    if args.sweep:
-        runs = []
-        for item in args.sweep.split(","):
-            pk, bs = item.split(":")
-            runs.append((pk, int(bs)))
-    else:
-        runs = [(default_plan, args.batch or (2048 if args.workload == "prefill" else 1))]
-    for i, (pk, B) in enumerate(runs):
-        out = run_one(args, d, layers, B, pk, args.steps, args.warmup)
-        xs_bits = out.pop("_xs_bits")
-        if not args.no_cpu and i == 0:
-            out["cpu_baseline"] = cpu_baseline(args, d, B, L, layers, xs_bits)
-        print(json.dumps(out), flush=True)
-
-
-def run_cache(args, d, layers):
-    """Expert-cache decode run over the stacked layers: the static plan first (warm-up
-    steps, then the timed steps, no updates), then the cached plan from its cold start
-    with a pipelined cache update after every step. One step = one token batch through every layer;
-    each (step, layer) takes its own seeded activations."""
-    import numpy as np
-    import torch
-
     import expert_offloaded_ffn_moe_amd as moe
-    import synth
 
-    H, I, E, k, G, act, alpha, seed = (d[n] for n in ("H", "I", "E", "k", "G", "act", "alpha", "seed"))
-    L, B, steps, warmup = len(layers), args.batch or 1, args.steps, args.warmup
-    S = int(round(0.7 * E))
-    eb = synth.expert_bytes(H, I, G)
-    n_x = (warmup + steps) * L
-    xb = synth.activations(seed, 7000, n_x * B, H, act)
-    xs = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda().view(n_x, B, H)
-    y = torch.empty((B, H), device="cuda")
-    out = {}
-    for mode in ("static", "cache"):
-        cfg = moe.make_config(H, I, E, k, G, act, num_layers=L, max_tokens=B, hbm_slots=S)
-        plan = moe.Plan(cfg)
-        for l, ly in enumerate(layers):
-            res = synth.coldest_host_plan(seed, l, E, S / E) if mode == "static" else None
-            plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], res)
-        torch.cuda.synchronize()
-        first = 0
-        if mode == "static":
-            for i in range(warmup):
-                for l in range(L):
-                    plan.forward(l, xs[i * L + l], y)
-            torch.cuda.synchronize()
-            plan.reset_stats()
-            first = warmup
-        times = []
-        t_all = time.perf_counter()
-        for i in range(first, first + steps):
-            t0 = time.perf_counter()
-            for l in range(L):
-                plan.forward(l, xs[i * L + l], y)
-            if mode == "cache":
-                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)  # pipelined
-            else:
-                torch.cuda.synchronize()
-            times.append(time.perf_counter() - t0)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t_all
-        st = plan.stats(-1)
-        log("%s plan: %d steps x %d layers in %.3fs, hit rate %.4f" % (
-            mode, steps, L, elapsed, st["hits"] / max(st["hits"] + st["misses"], 1)))
-        # profiled pass over a further 16 steps (same mode)
-        plan.profile(True)
-        n_prof = min(16, steps)
-        for i in range(first, first + n_prof):
-            for l in range(L):
-                plan.forward(l, xs[i * L + l], y)
-            if mode == "cache":
-                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
-        kt = plan.kernel_times()
-        plan.profile(False)
-        plan.destroy()
-        t = np.sort(np.array(times))
-        fwd = max(st["forwards"], 1)
-        per_kernel = {n: dict(launches=v[0], avg_us=(v[1] * 1e3 / v[0])) for n, v in kt.items() if v[0]}
-        out[mode] = dict(
-            tokens_per_s=round(B * steps / elapsed, 2),
-            step_ms_median=round(float(np.median(t)) * 1e3, 4),
-            step_ms_p95=round(float(np.percentile(t, 95)) * 1e3, 4),
-            tokens_per_s_median=round(B / float(np.median(t)), 2),
-            tokens_per_s_p5=round(B / float(np.percentile(t, 95)), 2),
-            hit_rate=round(st["hits"] / max(st["hits"] + st["misses"], 1), 5),
-            hits=st["hits"], misses=st["misses"],
-            bytes_hbm_per_layer_step=int(st["bytes_hbm"] / fwd), bytes_host_per_layer_step=int(st["bytes_host"] / fwd),
-            bytes_copied=st["bytes_copied"], promotions=st["promotions"], evictions=st["evictions"],
-            kernels_us={n: round(v["avg_us"], 3) for n, v in per_kernel.items()},
-            roofline=roofline(per_kernel, st["bytes_hbm"] / fwd, st["bytes_host"] / fwd, B * k, H, I))
-    c = out["cache"]
-    res = {
+    extra = {"topology": topology()}
+    log("topology:", extra["topology"])
+    if not args.no_ceilings:
+        ceil = {}
+        for label, hbm, host in (("1GiB", 1 << 30, 256 << 20), ("136MB", 136 << 20, 64 << 20),
+                                 ("13MB", 13 << 20, 16 << 20)):
+            c = moe.measure_link_ceilings(hbm, host, 5)
+            ceil["hbm_read_%s_GBps" % label] = round(c["hbm_read_gbps"], 1)
+            if label == "1GiB":
+                ceil["host_mapped_read_256MiB_GBps"] = round(c["host_read_gbps"], 2)
+                ceil["h2d_copy_256MiB_GBps"] = round(c["h2d_copy_gbps"], 2)
+        extra["measured_ceilings"] = ceil
+        log("ceilings:", ceil)
+    configs = {}
+    order = [w.strip() for w in args.only.split(",") if w.strip()]
+    for wl in order:
+        r = {"deepseek": run_deepseek, "qwen3": run_qwen3, "prefill": run_prefill, "cache": run_cache}[wl](
+            args, configs)
+        if r:
+            extra.update(r)
+    head_key = {"deepseek": "deepseek_mixed_b1", "qwen3": "qwen3_hbm_b1", "prefill": "prefill_t2048",
+                "cache": "cache_48_layers"}[order[0]]
+    head = configs[head_key]
+    line = {
         "metric": METRIC,
-        "value": c["tokens_per_s"],
-        "unit": "tokens/s",
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": 0,
-        "ms_per_step": round(1e3 * B / c["tokens_per_s"], 5),
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "expert-cache decode run: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d "
-                               "int4 G%d, %d HBM slots per layer (rest host-mapped), batch %d, %d steps, cold start, "
-                               "pipelined cache update after every step (max %d promotions per layer, score decay %g)" % (
-                                   L, H, I, E, k, G, S, B, steps, args.max_promotions, args.decay),
-                   "alpha": alpha, "seed": seed},
-        "roofline": c["roofline"],
-        "cache_run": {n: v for n, v in c.items() if n != "roofline"},
-        "static_plan": out["static"],
+        "data": "synthetic (seeded; random-init int4 experts of the named shapes)",
+        "config": {"workload": head["workload"], "key": head_key,
+                   "arithmetic": "int4 weight codes (exact in the bf16 dot products and MFMA), fp16 group scales, "
+                                 "bf16 activations, fp32 accumulation, fp32 y"},
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "layer": head.get("layer"),
+        "configs": {k: v for k, v in configs.items() if k != head_key},
     }
-    xs_bits = [xb[(i * L) * B:(i * L + 1) * B] for i in range(min(8, warmup + steps))]
-    return res, xs_bits
-
-
-def cpu_baseline(args, d, B, L, layers_host, xs_bits):
-    """The CPU oracle (float64, unmodified) on a bounded sample of the same steps."""
-    import numpy as np
-
-    from oracle import moe_oracle as O
-
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] + [1])
-    except Exception:
-        threads = 1
-    H, I, E, k, G, act = (d[n] for n in ("H", "I", "E", "k", "G", "act"))
-    n_layers = min(2, len(layers_host))
-    tokens, t0, i = 0, time.perf_counter(), 0
-    while time.perf_counter() - t0 < args.cpu_seconds:
-        l = i % n_layers
-        Wr, b, blobs = layers_host[l]["Wr"], layers_host[l]["b"], layers_host[l]["blobs"]
-        x = O.bf16_bits_to_f64(xs_bits[i % len(xs_bits)])
-        O.layer_forward(x, O.bf16_bits_to_f64(Wr), b, blobs, H, I, E, k, G, act)
-        tokens += B
-        i += 1
-    el = time.perf_counter() - t0
-    log("cpu oracle: %d forwards in %.1fs" % (i, el))
-    out = {"value": round(tokens / el, 4), "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
-           "sample": "%d forwards of batch %d over %d of the %d layers (float64 NumPy oracle, %.1fs)" % (
-               i, B, n_layers, L, el)}
-    # the same oracle pinned to one thread, on a shorter sample
-    try:
-        import threadpoolctl
-        with threadpoolctl.threadpool_limits(limits=1):
-            tok1, t1, j = 0, time.perf_counter(), 0
-            while time.perf_counter() - t1 < args.cpu_seconds / 3:
-                l = j % n_layers
-                Wr, b, blobs = layers_host[l]["Wr"], layers_host[l]["b"], layers_host[l]["blobs"]
-                x = O.bf16_bits_to_f64(xs_bits[j % len(xs_bits)])
-                O.layer_forward(x, O.bf16_bits_to_f64(Wr), b, blobs, H, I, E, k, G, act)
-                tok1 += B
-                j += 1
-            out["value_one_thread"] = round(tok1 / (time.perf_counter() - t1), 4)
-    except Exception as e:  # the one-thread figure is extra; the baseline above stands without it
-        log("cpu oracle, one thread: skipped (%s)" % e)
-    return out
+    line.update(extra)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
