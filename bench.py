@@ -67,6 +67,9 @@ def parse_args():
     ap.add_argument("--deepseek-layers", type=int, default=4)
     ap.add_argument("--deepseek-runs", default="mixed:1,mixed:4,mixed:16,hbm:1,hbm:4,hbm:16,host:1,host:4,host:16",
                     help="plan:batch runs of the DeepSeek-style layer, in order (plans mixed, hbm, host)")
+    ap.add_argument("--lowbit", default="3,2", help="code widths below 4 bits also run on the DeepSeek-style layers")
+    ap.add_argument("--lowbit-runs", default="mixed:1,mixed:4,hbm:1,host:1",
+                    help="plan:batch runs of the DeepSeek-style layers at each lower code width")
     ap.add_argument("--qwen3-layers", type=int, default=24)
     ap.add_argument("--prefill-layers", type=int, default=4)
     ap.add_argument("--cache-steps", type=int, default=256)
@@ -224,10 +227,10 @@ def time_steps(plan, n_layers, xs, y, steps, warmup):
     return elapsed, st, per_kernel
 
 
-def layer_result(wl, key, B, plan_kind, n_layers, steps, warmup, elapsed, st, per_kernel, slots):
+def layer_result(wl, key, B, plan_kind, n_layers, steps, warmup, elapsed, st, per_kernel, slots, bits=4):
     d = DIMS[wl]
     import synth
-    eb = synth.expert_bytes(d["H"], d["I"], d["G"])
+    eb = synth.expert_bytes(d["H"], d["I"], d["G"], bits)
     fwd = max(st["forwards"], 1)
     bh, bs = st["bytes_hbm"] / fwd, st["bytes_host"] / fwd
     ms = elapsed * 1e3 / steps
@@ -235,8 +238,9 @@ def layer_result(wl, key, B, plan_kind, n_layers, steps, warmup, elapsed, st, pe
     return {
         "value": round(B * steps / elapsed, 2), "unit": "layer-tokens/s", "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 5),
-        "workload": "%s H%d I%d E%d k%d int4 G%d, batch %d, plan %s (%d of %d experts in HBM), %d layers rotated"
-                    % (NAMES[wl], d["H"], d["I"], d["E"], d["k"], d["G"], B, plan_kind, slots, d["E"], n_layers),
+        "workload": "%s H%d I%d E%d k%d %d-bit codes G%d, batch %d, plan %s (%d of %d experts in HBM), %d layers "
+                    "rotated" % (NAMES[wl], d["H"], d["I"], d["E"], d["k"], bits, d["G"], B, plan_kind, slots, d["E"],
+                                 n_layers),
         "roofline": roof,
         "layer": {"expert_bytes_per_step_hbm": int(bh), "expert_bytes_per_step_host": int(bs),
                   "unique_experts_per_step": round((bh + bs) / eb, 3),
@@ -253,7 +257,8 @@ def cpu_cores():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwards=1, label=None, threads=None):
+def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwards=1, label=None, threads=None,
+                 bits=4):
     """The CPU oracle (float64 NumPy, unmodified) on a bounded sample of the same
     workload: forwards of the given batches through the first two layers, until
     `seconds` have passed (at least one). tokens: evaluate y only for these token rows of
@@ -270,7 +275,7 @@ def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwar
             ly = layers[n % n_l]
             xb = batches_bits[n % len(batches_bits)]
             O.layer_forward(O.bf16_bits_to_f64(xb), O.bf16_bits_to_f64(ly["Wr"]), ly["b"], ly["blobs"], d["H"],
-                            d["I"], d["E"], d["k"], d["G"], "bf16", tokens=tokens)
+                            d["I"], d["E"], d["k"], d["G"], "bf16", tokens=tokens, bits=bits)
             done_tokens += len(tokens) if tokens is not None else xb.shape[0]
             n += 1
     el = time.perf_counter() - t0
@@ -304,8 +309,12 @@ def run_deepseek(args, out):
     plan = moe.Plan(cfg)
     mixed = np.stack([synth.coldest_host_plan(d["seed"], l, d["E"], 0.7) for l in range(L)])
     kept = None
+    widths = [int(b) for b in args.lowbit.split(",") if b.strip()]
+    low = {b: [] for b in widths}
     for l, ly in enumerate(gen_layers("deepseek", L)):
         plan.load_layer(l, ly["Wr"], ly["b"], ly["blobs"], mixed[l])
+        for b in widths:  # the same layers with their codes cut to b bits (seeded synthetic b-bit experts)
+            low[b].append(dict(Wr=ly["Wr"], b=ly["b"], blobs=synth.cut_codes(ly["blobs"], d["H"], d["I"], d["G"], b)))
         if l == 0:
             kept = [ly]
     info = plan.info()
@@ -328,9 +337,33 @@ def run_deepseek(args, out):
         log("deepseek %s B%d: %.1f layer-tokens/s, %s" % (kind, B, r["value"], r["roofline"]["frac"]))
         res[key] = r
     plan.destroy()
+    for b in widths:
+        cfgb = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=16,
+                               hbm_slots=d["E"], weight_bits=b)
+        plan = moe.Plan(cfgb, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in low[b]], initial_hbm=mixed)
+        current = "mixed"
+        for item in args.lowbit_runs.split(","):
+            kind, B = item.split(":")
+            B = int(B)
+            if kind != current:
+                plan.cache_update(-1, want_resident=wants[kind])
+                current = kind
+            steps = args.steps if kind != "host" else max(4, min(args.steps, 20))
+            el, st, pk = time_steps(plan, L, xs[B][0], y[:B], steps, args.warmup)
+            key = "deepseek%dbit_%s_b%d" % (b, kind, B)
+            r = layer_result("deepseek", key, B, kind, L, steps, args.warmup, el, st, pk, int(wants[kind][0].sum()),
+                             bits=b)
+            log("deepseek %d-bit %s B%d: %.1f layer-tokens/s, %s" % (b, kind, B, r["value"], r["roofline"]["frac"]))
+            res[key] = r
+        plan.destroy()
+        if not args.no_cpu:
+            cb = cpu_baseline("deepseek", low[b][:1], xs[1][1][:4], args.cpu_seconds, bits=b)
+            for key in [kk for kk in res if kk.startswith("deepseek%dbit_" % b) and kk.endswith("_b1")]:
+                res[key]["cpu_baseline"] = cb
+        low[b] = None
     if not args.no_cpu:
         for B in (1, 4, 16):
-            keys = [key for key in res if key.endswith("_b%d" % B)]
+            keys = [key for key in res if key.endswith("_b%d" % B) and "bit_" not in key]
             if not keys:
                 continue
             toks = [0, 1] if B == 16 else None

@@ -22,7 +22,8 @@ class Config(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32), ("num_layers", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("hbm_slots", ctypes.c_int32),
-                ("gemm_min_tokens", ctypes.c_int32), ("prefill_stage_slots", ctypes.c_int32)]
+                ("gemm_min_tokens", ctypes.c_int32), ("prefill_stage_slots", ctypes.c_int32),
+                ("weight_bits", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -175,9 +176,9 @@ def debug_live_allocs():
 
 
 def make_config(H, I, E, k, G, act="bf16", num_layers=1, max_tokens=16, hbm_slots=None, gemm_min_tokens=0,
-                prefill_stage_slots=0):
+                prefill_stage_slots=0, weight_bits=4):
     return Config(H, I, E, k, G, num_layers, ACT_BF16 if act == "bf16" else ACT_F32, max_tokens,
-                  E if hbm_slots is None else hbm_slots, gemm_min_tokens, prefill_stage_slots)
+                  E if hbm_slots is None else hbm_slots, gemm_min_tokens, prefill_stage_slots, weight_bits)
 
 
 def expert_bytes(cfg: Config) -> int:

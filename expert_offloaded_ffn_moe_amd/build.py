@@ -14,7 +14,8 @@ BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "k_route.hip", "k_gemv.hip", "k_gemv_gateup_bf16.hip", "k_gemv_gateup_f32.hip",
-           "k_gemv_down_bf16.hip", "k_gemv_down_f32.hip", "k_gemm.hip", "k_stage.hip", "k_util.hip", "host_logic.cpp"]
+           "k_gemv_down_bf16.hip", "k_gemv_down_f32.hip", "k_gemm.hip", "k_stage.hip", "k_util.hip", "k_gemv_lowbit_gateup.hip",
+           "k_gemv_lowbit_down.hip", "host_logic.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 # packed fp32 math is kept out of every kernel
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

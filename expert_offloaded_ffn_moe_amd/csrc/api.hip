@@ -604,7 +604,7 @@ moe_status moe_expert_bytes(const moe_config* cfg, size_t* out) {
   if (!cfg || !out) return fail(MOE_E_INVALID, "null argument");
   const std::string why = check_config(*cfg);
   if (!why.empty()) return fail(MOE_E_INVALID, why);
-  *out = (size_t)make_layout(cfg->hidden, cfg->inter, cfg->group_size).canonical_bytes;
+  *out = (size_t)make_layout(cfg->hidden, cfg->inter, cfg->group_size, cfg_bits(*cfg)).canonical_bytes;
   return MOE_OK;
 }
 
@@ -626,7 +626,7 @@ moe_status moe_plan_create(const moe_config* cfg, const moe_layer_weights* layer
   moe_plan* p = new moe_plan();
   p->cfg = *cfg;
   if (p->cfg.gemm_min_tokens == 0) p->cfg.gemm_min_tokens = kGemmMinTokensDefault;
-  p->L = make_layout(cfg->hidden, cfg->inter, cfg->group_size);
+  p->L = make_layout(cfg->hidden, cfg->inter, cfg->group_size, cfg_bits(*cfg));
   p->act_size = cfg->act_dtype == MOE_ACT_BF16 ? 2 : 4;
   if (hipGetDevice(&p->device) != hipSuccess) {
     delete p;
@@ -838,13 +838,16 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   // one-launch routing for small batches (its router walks the tokens one by one;
   // past a few bf16 tokens the MFMA router and the multi-block grouping are faster)
   const bool decode = T <= (bf16 ? kRouteDecodeMaxTokensBf16 : kRouteSmallMaxTokens) && A <= kRouteSmallMaxAssign;
-  const bool prefill = bf16 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
+  // the grouped MFMA GEMMs and the fused down + combine kernels take 4-bit codes only;
+  // 2- and 3-bit layers run every batch on the dequant-GEMVs
+  const bool int4 = p->L.bits == 4;
+  const bool prefill = bf16 && int4 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
   rt.work = prefill ? nullptr : w.work;
   // a few tokens: down projection and combine in one launch (K split over the free
   // waves), when its (H/64) x T workgroups still keep the CUs streaming; below that
   // the per-expert down GEMV spreads the same bytes over more workgroups
   const int down_splits = std::max(1, std::min(16 / k, (int)p->L.dn_groups));
-  const bool fuse_small = bf16 && decode && T <= kDownCombMaxTokens && k <= 16;
+  const bool fuse_small = bf16 && int4 && decode && T <= kDownCombMaxTokens && k <= 16;
   const bool fuse_down = fuse_small && (H / 64) * T >= kDownCombMinGroups;
   // fewer 64-row tiles than that: the same fusion on 16-row tiles of H, with the
   // K chunks of each wave spread over its four 16-lane quarters
@@ -986,7 +989,9 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     ga.out = w.h;
     ga.outpart = w.hpart;
     ga.off_codes = p->L.off_gu_codes;
+    ga.off_hi = p->L.off_gu_hi;
     ga.off_scales = p->L.off_gu_scales;
+    ga.bits = (int)p->L.bits;
     ga.chunks = (int)p->L.gu_chunks;
     ga.groups = (int)p->L.gu_groups;
     ga.tiles = (int)p->L.gu_tiles;
@@ -1007,6 +1012,7 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     da.out = w.o;
     da.outpart = nullptr;
     da.off_codes = p->L.off_dn_codes;
+    da.off_hi = p->L.off_dn_hi;
     da.off_scales = p->L.off_dn_scales;
     da.chunks = (int)p->L.dn_chunks;
     da.groups = (int)p->L.dn_groups;

@@ -8,28 +8,35 @@ namespace moe {
 
 static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-Layout make_layout(int64_t H, int64_t I, int64_t G) {
+Layout make_layout(int64_t H, int64_t I, int64_t G, int64_t bits) {
   Layout L;
   L.H = H;
   L.I = I;
   L.G = G;
+  L.bits = bits;
+  L.kc = bits == 4 ? 32 : 64;
   L.gu_tiles = I / 32;
-  L.gu_chunks = H / 32;
+  L.gu_chunks = H / L.kc;
   L.gu_groups = H / G;
   L.dn_tiles = H / 64;
-  L.dn_chunks = I / 32;
+  L.dn_chunks = I / L.kc;
   L.dn_groups = I / G;
+  const int64_t hi_block = bits == 3 ? 512 : 0;
   int64_t off = 0;
   L.off_gu_codes = off;
   off = round_up(off + L.gu_tiles * L.gu_chunks * 1024, 256);
+  L.off_gu_hi = off;
+  off = round_up(off + L.gu_tiles * L.gu_chunks * hi_block, 256);
   L.off_gu_scales = off;
   off = round_up(off + L.gu_tiles * L.gu_groups * 128, 256);
   L.off_dn_codes = off;
   off = round_up(off + L.dn_tiles * L.dn_chunks * 1024, 256);
+  L.off_dn_hi = off;
+  off = round_up(off + L.dn_tiles * L.dn_chunks * hi_block, 256);
   L.off_dn_scales = off;
   off = round_up(off + L.dn_tiles * L.dn_groups * 128, 256);
   L.bytes = off;
-  L.canonical_bytes = 3 * H * I / 2 + 6 * H * I / G;
+  L.canonical_bytes = 3 * H * I * bits / 8 + 6 * H * I / G;
   return L;
 }
 
@@ -51,6 +58,13 @@ std::string check_config(const moe_config& c) {
   if (c.prefill_stage_slots < 0 || c.prefill_stage_slots > c.num_experts)
     return "prefill_stage_slots must be in 0..num_experts";
   if (c.hidden > 65536 || c.inter > 65536) return "hidden and inter must be <= 65536";
+  const int bits = c.weight_bits == 0 ? 4 : c.weight_bits;
+  if (bits != 2 && bits != 3 && bits != 4) return "weight_bits must be 0 (4), 2, 3 or 4";
+  if (bits < 4) {
+    if (c.act_dtype != MOE_ACT_BF16) return "2- and 3-bit weights need bf16 activations";
+    if (c.group_size < 64) return "2- and 3-bit weights need group_size 64, 128 or 256";
+    if (c.inter % 64) return "2- and 3-bit weights need inter to be a multiple of 64";
+  }
   return "";
 }
 
@@ -78,7 +92,7 @@ static inline void chunk16(const uint8_t* src, uint8_t* dst) {
   }
 }
 
-void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
+static void repack_expert4(const Layout& L, const uint8_t* canon, uint8_t* out) {
   const int64_t H = L.H, I = L.I, G = L.G;
   const uint8_t* q_gate = canon;
   const uint8_t* q_up = q_gate + I * H / 2;
@@ -117,6 +131,79 @@ void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
       }
     }
   }
+}
+
+// Code i of a canonical row of b-bit codes: bits [b*i, b*i+b) of the row's
+// little-endian bit string (bit j = bit j % 8 of byte j / 8).
+static inline uint32_t code_at(const uint8_t* row, int64_t i, int64_t b) {
+  const int64_t bit = i * b;
+  uint32_t w = row[bit >> 3];
+  if ((bit & 7) + b > 8) w |= (uint32_t)row[(bit >> 3) + 1] << 8;
+  return (w >> (bit & 7)) & ((1u << b) - 1u);
+}
+
+// The 16-byte low-plane word and (3-bit codes) the 8-byte high-plane word of one
+// lane for the 64 codes of `row` starting at K offset k0.
+static void lane_words_lowbit(const uint8_t* row, int64_t k0, int64_t b, uint8_t* lo16, uint8_t* hi8) {
+  uint32_t lo[4] = {0, 0, 0, 0}, hi[2] = {0, 0};
+  for (int d = 0; d < 4; ++d)
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t n0 = code_at(row, k0 + 16 * d + 2 * j, b), n1 = code_at(row, k0 + 16 * d + 2 * j + 1, b);
+      lo[d] |= ((n0 & 3u) << (2 * j)) | ((n1 & 3u) << (16 + 2 * j));
+    }
+  std::memcpy(lo16, lo, 16);
+  if (!hi8) return;
+  for (int e = 0; e < 2; ++e)
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t n0 = code_at(row, k0 + 32 * e + 2 * i, b), n1 = code_at(row, k0 + 32 * e + 2 * i + 1, b);
+      hi[e] |= ((n0 >> 2) << i) | ((n1 >> 2) << (16 + i));
+    }
+  std::memcpy(hi8, hi, 8);
+}
+
+static void repack_expert_lowbit(const Layout& L, const uint8_t* canon, uint8_t* out) {
+  const int64_t H = L.H, I = L.I, G = L.G, b = L.bits, kc = L.kc;
+  const int64_t rb_h = H * b / 8, rb_i = I * b / 8;  // canonical bytes per row, K = H / K = I
+  const uint8_t* q_gate = canon;
+  const uint8_t* q_up = q_gate + I * rb_h;
+  const uint8_t* q_down = q_up + I * rb_h;
+  const uint16_t* s_gate = reinterpret_cast<const uint16_t*>(q_down + H * rb_i);
+  const uint16_t* s_up = s_gate + I * (H / G);
+  const uint16_t* s_down = s_up + I * (H / G);
+  std::memset(out, 0, (size_t)L.bytes);
+  const bool three = b == 3;
+  for (int64_t t = 0; t < L.gu_tiles; ++t)
+    for (int lane = 0; lane < 64; ++lane) {
+      const bool up = lane >= 32;
+      const int64_t row = 32 * t + (lane & 31);
+      const uint8_t* src = (up ? q_up : q_gate) + row * rb_h;
+      for (int64_t c = 0; c < L.gu_chunks; ++c) {
+        const int64_t blk = (t * L.gu_chunks + c) * 64 + lane;
+        lane_words_lowbit(src, c * kc, b, out + L.off_gu_codes + blk * 16, three ? out + L.off_gu_hi + blk * 8 : nullptr);
+      }
+      const uint16_t* srow = (up ? s_up : s_gate) + row * (H / G);
+      for (int64_t g = 0; g < H / G; ++g)
+        std::memcpy(out + L.off_gu_scales + ((t * L.gu_groups + g) * 64 + lane) * 2, srow + g, 2);
+    }
+  for (int64_t t = 0; t < L.dn_tiles; ++t)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int64_t row = 64 * t + lane;
+      const uint8_t* src = q_down + row * rb_i;
+      for (int64_t c = 0; c < L.dn_chunks; ++c) {
+        const int64_t blk = (t * L.dn_chunks + c) * 64 + lane;
+        lane_words_lowbit(src, c * kc, b, out + L.off_dn_codes + blk * 16, three ? out + L.off_dn_hi + blk * 8 : nullptr);
+      }
+      const uint16_t* srow = s_down + row * (I / G);
+      for (int64_t g = 0; g < I / G; ++g)
+        std::memcpy(out + L.off_dn_scales + ((t * L.dn_groups + g) * 64 + lane) * 2, srow + g, 2);
+    }
+}
+
+void repack_expert(const Layout& L, const uint8_t* canon, uint8_t* out) {
+  if (L.bits == 4)
+    repack_expert4(L, canon, out);
+  else
+    repack_expert_lowbit(L, canon, out);
 }
 
 void cache_policy_step(int32_t E, int32_t n_slots, double decay, int32_t max_promotions,

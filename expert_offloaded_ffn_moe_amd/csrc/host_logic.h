@@ -15,26 +15,37 @@ namespace moe {
 
 // Internal expert layout (all regions 256-byte aligned inside one blob).
 //
-// Gate/up codes: tiles of 32 output positions; tile t, chunk c (32 values of K=H)
+// Codes travel in 16-byte lane words: a word holds kc = 32 values of K for 4-bit
+// codes and kc = 64 values for 2- and 3-bit codes (their low two bits; the third
+// bit of 3-bit codes sits in a separate 8-byte "high plane" word per lane).
+// Gate/up codes: tiles of 32 output positions; tile t, chunk c (kc values of K=H)
 // is a 1 KiB block of 64 lanes x 16 bytes. Lane l < 32 holds gate row 32t+l,
-// lane l >= 32 up row 32t+l-32, K range [32c, 32c+32).
-// Down codes: tiles of 64 output rows; tile t, chunk c (32 values of K=I) is a
+// lane l >= 32 up row 32t+l-32, K range [kc*c, kc*c+kc).
+// Down codes: tiles of 64 output rows; tile t, chunk c (kc values of K=I) is a
 // 1 KiB block, lane l holds row 64t+l.
-// Inside a lane's 16 bytes, dword d covers K offsets [8d, 8d+8): the value at
+// Inside a 4-bit lane word, dword d covers K offsets [8d, 8d+8): the value at
 // offset 8d+2j sits in bits [4j, 4j+4), at 8d+2j+1 in bits [16+4j, 20+4j),
 // stored as n = q + 8 (0..15).
+// Inside a 2- or 3-bit lane word, dword d covers K offsets [16d, 16d+16): the low
+// two bits of code n at offset 16d+2j sit in bits [2j, 2j+2), at 16d+2j+1 in bits
+// [16+2j, 18+2j). In the 3-bit high-plane word (same block order, 512 bytes per
+// block), dword e covers offsets [32e, 32e+32): bit 2 of the code at 32e+2i is bit
+// i, at 32e+2i+1 bit 16+i.
 // Scales: per tile, one 128-byte row per quantisation group: lane l's fp16
 // scale of that group for its row at bytes [2l, 2l+2).
 struct Layout {
-  int64_t H = 0, I = 0, G = 0;
+  int64_t H = 0, I = 0, G = 0, bits = 4, kc = 32;
   int64_t gu_tiles = 0, gu_chunks = 0, gu_groups = 0;
   int64_t dn_tiles = 0, dn_chunks = 0, dn_groups = 0;
-  int64_t off_gu_codes = 0, off_gu_scales = 0, off_dn_codes = 0, off_dn_scales = 0;
+  int64_t off_gu_codes = 0, off_gu_hi = 0, off_gu_scales = 0, off_dn_codes = 0, off_dn_hi = 0, off_dn_scales = 0;
   int64_t bytes = 0;            // internal blob size (multiple of 256)
-  int64_t canonical_bytes = 0;  // 3*H*I/2 + 6*H*I/G
+  int64_t canonical_bytes = 0;  // 3*H*I*bits/8 + 6*H*I/G
 };
 
-Layout make_layout(int64_t H, int64_t I, int64_t G);
+Layout make_layout(int64_t H, int64_t I, int64_t G, int64_t bits = 4);
+
+// Bits per weight code of cfg (weight_bits, 0 meaning 4).
+inline int cfg_bits(const moe_config& c) { return c.weight_bits == 0 ? 4 : c.weight_bits; }
 
 // Checks cfg; returns an empty string when valid, else the reason.
 std::string check_config(const moe_config& c);

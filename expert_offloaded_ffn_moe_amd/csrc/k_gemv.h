@@ -22,9 +22,18 @@
 // sum q x = 16 * (sum v x - 1.5 * sum x), with sum x precomputed per group, so
 // the int4 weight is exact and only fp32 accumulation rounds.
 // fp32 activations: q is converted exactly to fp32 and used in fmaf.
+//
+// 2- and 3-bit codes (the lower-bit formats: odd levels q = 2n - (2^b - 1)): a lane
+// word holds 64 values of K, their low two bits at mantissa bits 5..6 (2-bit,
+// v = 1 + n/4) or 4..5 (3-bit, v = 1 + n/8, the third bit from the high-plane word
+// at mantissa bit 6), one shift and mask per pair of values as for 4-bit codes.
+// Over a group, sum q x = A (sum v x - C sum x) with (A, C) = (16, 1.5) for 4-bit
+// codes, (8, 1.375) for 2-bit and (16, 1.4375) for 3-bit, all exact in fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -98,6 +107,36 @@ static __device__ __forceinline__ float chunk_dot_f32(const u32x4& wv, const P& 
 
 typedef __attribute__((address_space(1))) const u32x4 guint4;    // global-memory views, so
 typedef __attribute__((address_space(1))) const uint16_t gushort;  // loads are global_load, not flat
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 guint2;
+
+// K values per 16-byte lane word, and the group-sum constants of the bf16 path.
+template <int BITS> constexpr int kChunkK = BITS == 4 ? 32 : 64;
+template <int BITS> constexpr float kFixA = BITS == 2 ? 8.f : 16.f;
+template <int BITS> constexpr float kFixC = BITS == 4 ? 1.5f : BITS == 3 ? 1.4375f : 1.375f;
+
+// x << sh for sh >= 0, x >> -sh otherwise (sh a constant after unrolling)
+static __device__ __forceinline__ uint32_t shift_by(uint32_t x, int sh) { return sh >= 0 ? x << sh : x >> -sh; }
+
+// acc + sum_i v_i x_i over the 64 values of a 2- or 3-bit lane word: dword d pair j
+// (values 16d+2j, 16d+2j+1) against x pair 8d+j; for 3-bit codes the third bit of
+// that pair is bit i = 8 (d & 1) + j (and 16 + i) of high-plane dword d >> 1.
+template <int BITS, typename P>
+static __device__ __forceinline__ float chunk_dot_bf16_low(const u32x4& wv, const u32x2& hv, const P& xr, float acc) {
+  const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+  const uint32_t h[2] = {hv.x, hv.y};
+  constexpr int kDst = BITS == 2 ? 5 : 4;  // mantissa bit of the code's lowest bit
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t v = (shift_by(w[d], kDst - 2 * j) & ((3u << kDst) | (3u << (16 + kDst)))) | 0x3F803F80u;
+      if (BITS == 3) v |= shift_by(h[d >> 1], 6 - (8 * (d & 1) + j)) & 0x00400040u;
+      acc = dot2(v, xr[8 * d + j], acc);
+    }
+  }
+  return acc;
+}
 
 constexpr int kBatch = 8;   // chunks whose loads are issued together
 constexpr int kMaxW = 16;   // waves per workgroup at most
@@ -117,17 +156,21 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 
 // Activation chunk c of row `row` (element offset): XS == 0 reads it from global
 // memory (wave-uniform address, scalar loads), XS == 1 from the LDS copy.
-template <int XS>
-static __device__ __forceinline__ float chunk_dot_bf16_src(const u32x4& wv, const void* in, int64_t row, int c,
-                                                           float acc) {
+template <int XS, int BITS = 4>
+static __device__ __forceinline__ float chunk_dot_bf16_src(const u32x4& wv, const u32x2& hv, const void* in,
+                                                           int64_t row, int c, float acc) {
+  constexpr int NX = kChunkK<BITS> / 2;  // x pairs per lane word
   if (XS) {
-    lds_u32* xr = (lds_u32*)in + row / 2 + c * 16;
-    uint32_t v[16];
+    lds_u32* xr = (lds_u32*)in + row / 2 + c * NX;
+    uint32_t v[NX];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = xr[i];
-    return chunk_dot_bf16(wv, v, acc);
+    for (int i = 0; i < NX; ++i) v[i] = xr[i];
+    if (BITS == 4) return chunk_dot_bf16(wv, v, acc);
+    return chunk_dot_bf16_low<BITS>(wv, hv, v, acc);
   }
-  return chunk_dot_bf16(wv, static_cast<const uint32_t*>(in) + row / 2 + c * 16, acc);
+  const uint32_t* xg = static_cast<const uint32_t*>(in) + row / 2 + c * NX;
+  if (BITS == 4) return chunk_dot_bf16(wv, xg, acc);
+  return chunk_dot_bf16_low<BITS>(wv, hv, xg, acc);
 }
 
 template <int XS>
@@ -143,31 +186,41 @@ static __device__ __forceinline__ float chunk_dot_f32_src(const u32x4& wv, const
   return chunk_dot_f32(wv, static_cast<const float*>(in) + row + c * 32, acc);
 }
 
-// One batch: kBatch code chunks (GB groups) and their scales, loaded unconditionally
-// with indices clamped to the wave's last chunk/group (repeats hit in cache).
-template <int CPG>
+// One batch: kBatch code chunks (GB groups) and their scales (and, for 3-bit codes,
+// the chunks' high-plane words), loaded unconditionally with indices clamped to the
+// wave's last chunk/group (repeats hit in cache).
+template <int CPG, int BITS = 4>
 struct Batch {
   static constexpr int NB = CPG > kBatch ? CPG : kBatch;
   static constexpr int GB = NB / CPG;
   u32x4 wv[NB];
+  u32x2 hv[BITS == 3 ? NB : 1];
   uint16_t sb[GB];
-  __device__ __forceinline__ void load(guint4* codes, gushort* scales, int gb, int g1) {
+  __device__ __forceinline__ void load(guint4* codes, guint2* his, gushort* scales, int gb, int g1) {
     const int c_last = g1 * CPG - 1;
 #pragma unroll
     for (int q = 0; q < GB; ++q) sb[q] = scales[(size_t)min(gb + q, g1 - 1) * 64];
 #pragma unroll
     for (int i = 0; i < NB; ++i) wv[i] = codes[(size_t)min(gb * CPG + i, c_last) * 64];
+    if (BITS == 3) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) hv[i] = his[(size_t)min(gb * CPG + i, c_last) * 64];
+    } else {
+      hv[0] = u32x2{0u, 0u};
+    }
   }
+  __device__ __forceinline__ const u32x2& high(int i) const { return hv[BITS == 3 ? i : 0]; }
 };
 
 // Arithmetic of one batch starting at group gb: groups past g1 repeat the last
 // group and count with weight 0 (no branch, so loads issued earlier stay ahead).
-template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS>
-static __device__ __forceinline__ void batch_math(const Batch<CPG>& bt, const void* __restrict__ in,
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4>
+static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS>& bt, const void* __restrict__ in,
                                                   const float* __restrict__ insum, const int64_t* rows,
                                                   const int64_t* sum_rows, int mc, int gb, int g1, float* acc) {
+  constexpr int SPG = CPG * kChunkK<BITS> / 32;  // 32-value sums (down: h chunk sums) per group
 #pragma unroll
-  for (int q = 0; q < Batch<CPG>::GB; ++q) {
+  for (int q = 0; q < Batch<CPG, BITS>::GB; ++q) {
     const int g = min(gb + q, g1 - 1);
     const float keep = (gb + q < g1) ? 1.f : 0.f;
     float accg[MT];
@@ -180,7 +233,8 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG>& bt, const vo
       for (int m = 0; m < MT; ++m) {
         if (m < mc) {
           if (BF16)
-            accg[m] = chunk_dot_bf16_src<XS>(bt.wv[q * CPG + cc], in, rows[m], c, accg[m]);
+            accg[m] = chunk_dot_bf16_src<XS, BITS>(bt.wv[q * CPG + cc], bt.high(q * CPG + cc), in, rows[m], c,
+                                                   accg[m]);
           else
             accg[m] = chunk_dot_f32_src<XS>(bt.wv[q * CPG + cc], in, rows[m], c, accg[m]);
         }
@@ -195,11 +249,11 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG>& bt, const vo
           if (SUMS_PER_CHUNK) {
             xs = 0.f;
 #pragma unroll
-            for (int cc = 0; cc < CPG; ++cc) xs += insum[sum_rows[m] + g * CPG + cc];
+            for (int cc = 0; cc < SPG; ++cc) xs += insum[sum_rows[m] + g * SPG + cc];
           } else {
             xs = insum[sum_rows[m] + g];
           }
-          acc[m] = fmaf(16.f * s, accg[m] - 1.5f * xs, acc[m]);
+          acc[m] = fmaf(kFixA<BITS> * s, accg[m] - kFixC<BITS> * xs, acc[m]);
         } else {
           acc[m] = fmaf(s, accg[m], acc[m]);
         }
@@ -214,15 +268,15 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG>& bt, const vo
 // Each batch issues all of its loads before its arithmetic. (Issuing the next
 // batch's loads ahead of the current batch's arithmetic measured slower here:
 // the second register set costs more occupancy than the overlap gains.)
-template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS>
-static __device__ __forceinline__ void k_loop(guint4* codes, gushort* scales, const void* __restrict__ in,
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4>
+static __device__ __forceinline__ void k_loop(guint4* codes, guint2* his, gushort* scales, const void* __restrict__ in,
                                               const float* __restrict__ insum, const int64_t* rows,
                                               const int64_t* sum_rows, int mc, int g0, int g1, float* acc) {
-  constexpr int GB = Batch<CPG>::GB;
+  constexpr int GB = Batch<CPG, BITS>::GB;
   for (int gb = g0; gb < g1; gb += GB) {
-    Batch<CPG> A;
-    A.load(codes, scales, gb, g1);
-    batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
+    Batch<CPG, BITS> A;
+    A.load(codes, his, scales, gb, g1);
+    batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS, BITS>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
   }
 }
 
@@ -241,9 +295,9 @@ static __device__ __forceinline__ void stage_rows(const void* __restrict__ src, 
 
 // The rows of one active expert and one output tile, MT token rows per pass
 // (red: the workgroup's [W][MT][64] partial sums in LDS).
-template <int BF16, int MT, int CPG, int XS>
+template <int BF16, int MT, int CPG, int XS, int BITS>
 static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, int W, int wave, int lane, int tile,
-                                                     const WorkDesc* d, int M, int p0, guint4* codes,
+                                                     const WorkDesc* d, int M, int p0, guint4* codes, guint2* his,
                                                      gushort* scales, const int32_t* __restrict__ sorted,
                                                      const void* __restrict__ x, const float* __restrict__ xsum,
                                                      void* __restrict__ h, float* __restrict__ hpart, int groups,
@@ -272,9 +326,9 @@ static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, in
       }
       stage_rows(x, src16, mc, len16);
       __syncthreads();
-      k_loop<BF16, MT, CPG, false, XS>(codes, scales, moe_dyn_lds, xsum, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, moe_dyn_lds, xsum, rows, sum_rows, mc, g0, g1, acc);
     } else {
-      k_loop<BF16, MT, CPG, false, XS>(codes, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[(wave * MT + m) * 64 + lane] = acc[m];
@@ -308,13 +362,13 @@ static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, in
 // give an expert that holds a single token the one-token path, whose activation
 // row comes in through scalar loads with no LDS staging or barrier before the
 // weights: in a batch of a few tokens most experts hold one.
-template <int BF16, int MT, int CPG, int XS>
+template <int BF16, int MT, int CPG, int XS, int BITS>
 __global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __restrict__ work,
                                                    const int32_t* __restrict__ sorted,
                                                    const void* __restrict__ x, const float* __restrict__ xsum,
                                                    void* __restrict__ h, float* __restrict__ hpart,
-                                                   int64_t off_codes, int64_t off_scales, int chunks, int groups,
-                                                   int tiles, int H, int I, int k) {
+                                                   int64_t off_codes, int64_t off_hi, int64_t off_scales, int chunks,
+                                                   int groups, int tiles, int H, int I, int k) {
   __shared__ float red[kMaxW * MT * 64];
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -328,22 +382,23 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_gateup(const WorkDesc* __re
   M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
   const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  guint2* his = (guint2*)(base + off_hi) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
   if (MT > 1 && M == 1)
-    gateup_expert<BF16, 1, CPG, 0>(red, W, wave, lane, tile, d, M, p0, codes, scales, sorted, x, xsum, h, hpart,
-                                   groups, H, I, k);
+    gateup_expert<BF16, 1, CPG, 0, BITS>(red, W, wave, lane, tile, d, M, p0, codes, his, scales, sorted, x, xsum, h,
+                                         hpart, groups, H, I, k);
   else
-    gateup_expert<BF16, MT, CPG, XS>(red, W, wave, lane, tile, d, M, p0, codes, scales, sorted, x, xsum, h, hpart,
-                                     groups, H, I, k);
+    gateup_expert<BF16, MT, CPG, XS, BITS>(red, W, wave, lane, tile, d, M, p0, codes, his, scales, sorted, x, xsum, h,
+                                           hpart, groups, H, I, k);
 }
 
 // ----------------------------------------------------------------------------- down projection
 
-template <int BF16, int MT, int CPG, int XS>
+template <int BF16, int MT, int CPG, int XS, int BITS>
 __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __restrict__ work, const void* __restrict__ h,
                                                  const float* __restrict__ hpart, float* __restrict__ o,
-                                                 int64_t off_codes, int64_t off_scales, int chunks, int groups,
-                                                 int tiles, int H, int I) {
+                                                 int64_t off_codes, int64_t off_hi, int64_t off_scales, int chunks,
+                                                 int groups, int tiles, int H, int I) {
   __shared__ float red[kMaxW][MT][64];
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -357,6 +412,7 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
   M = __builtin_amdgcn_readfirstlane(M);    // wave-uniform again for the compiler
   const int p0 = d->p0;
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
+  guint2* his = (guint2*)(base + off_hi) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
   const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
 
@@ -382,9 +438,9 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
       }
       stage_rows(h, src16, mc, len16);
       __syncthreads();
-      k_loop<BF16, MT, CPG, true, XS>(codes, scales, moe_dyn_lds, hpart, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, moe_dyn_lds, hpart, rows, sum_rows, mc, g0, g1, acc);
     } else {
-      k_loop<BF16, MT, CPG, true, XS>(codes, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
@@ -399,5 +455,80 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
   }
 }
 
+
+// ----------------------------------------------------------------------------- launch
+
+// Launch shape of one dequant-GEMV launch, chosen by the policy in k_gemv.hip:
+// tokens per pass (mt), waves per workgroup, activations staged in LDS or not.
+struct GemvShape {
+  int mt, waves;
+  bool lds;
+};
+
+template <int BF16, int MT, int CPG, int BITS>
+static void gateup_launch3(const GemvArgs& a, const GemvShape& sh, int grid, const Timing& tm, hipStream_t s) {
+  const size_t lds = (size_t)MT * a.H * (BF16 ? 2 : 4);
+  if (sh.lds)
+    launch_timed(k_gateup<BF16, MT, CPG, 1, BITS>, dim3(grid), dim3(64 * sh.waves), lds, s, tm, a.work, a.sorted, a.in,
+                 a.insum, a.out, a.outpart, a.off_codes, a.off_hi, a.off_scales, a.chunks, a.groups, a.tiles, a.H,
+                 a.I, a.k);
+  else
+    launch_timed(k_gateup<BF16, MT, CPG, 0, BITS>, dim3(grid), dim3(64 * sh.waves), 0, s, tm, a.work, a.sorted, a.in,
+                 a.insum, a.out, a.outpart, a.off_codes, a.off_hi, a.off_scales, a.chunks, a.groups, a.tiles, a.H,
+                 a.I, a.k);
+}
+
+template <int BF16, int MT, int CPG, int BITS>
+static void down_launch3(const GemvArgs& a, const GemvShape& sh, int grid, const Timing& tm, hipStream_t s) {
+  float* o = static_cast<float*>(a.out);
+  const size_t lds = (size_t)MT * a.I * (BF16 ? 2 : 4);
+  if (sh.lds)
+    launch_timed(k_down<BF16, MT, CPG, 1, BITS>, dim3(grid), dim3(64 * sh.waves), lds, s, tm, a.work, a.in, a.insum,
+                 o, a.off_codes, a.off_hi, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
+  else
+    launch_timed(k_down<BF16, MT, CPG, 0, BITS>, dim3(grid), dim3(64 * sh.waves), 0, s, tm, a.work, a.in, a.insum, o,
+                 a.off_codes, a.off_hi, a.off_scales, a.chunks, a.groups, a.tiles, a.H, a.I);
+}
+
+// Chunks of a quantisation group: G / 32 (4-bit codes: 1, 2, 4, 8) or G / 64 (2-, 3-bit: 1, 2, 4).
+template <int BF16, int MT, int BITS, bool DOWN>
+static void gemv_cpg(const GemvArgs& a, const GemvShape& sh, int grid, const Timing& tm, hipStream_t s) {
+  auto go = [&](auto cpg_c) {
+    constexpr int C = decltype(cpg_c)::value;
+    if constexpr (DOWN)
+      down_launch3<BF16, MT, C, BITS>(a, sh, grid, tm, s);
+    else
+      gateup_launch3<BF16, MT, C, BITS>(a, sh, grid, tm, s);
+  };
+  const int cpg = a.G / kChunkK<BITS>;
+  if (cpg <= 1) return go(std::integral_constant<int, 1>{});
+  if (cpg == 2) return go(std::integral_constant<int, 2>{});
+  if constexpr (BITS == 4) {
+    if (cpg == 4) return go(std::integral_constant<int, 4>{});
+    // G = 256 with two tokens: the 4-token kernel (the 2-token one spills)
+    if constexpr (MT == 2)
+      return gemv_cpg<BF16, 4, BITS, DOWN>(a, sh, grid, tm, s);
+    else
+      return go(std::integral_constant<int, 8>{});
+  } else {
+    return go(std::integral_constant<int, 4>{});
+  }
+}
+
+// Every (tokens per pass, chunks per group, staging) instance of one kernel family;
+// instantiated once per (activation dtype, code width) in its own source file. The
+// 8-token down GEMV of 3-bit codes spills, so 3-bit down passes take 4 tokens.
+template <int BF16, int BITS, bool DOWN>
+void run_gemv(const GemvArgs& a, const GemvShape& sh, int grid, const Timing& tm, hipStream_t s) {
+  constexpr int MT8 = (BITS == 3 && DOWN) ? 4 : 8;
+  switch (sh.mt) {
+    case 1: return gemv_cpg<BF16, 1, BITS, DOWN>(a, sh, grid, tm, s);
+    case 2:
+      if constexpr (BF16 && DOWN && BITS == 4) return gemv_cpg<BF16, 2, BITS, DOWN>(a, sh, grid, tm, s);
+      return gemv_cpg<BF16, 4, BITS, DOWN>(a, sh, grid, tm, s);
+    case 4: return gemv_cpg<BF16, 4, BITS, DOWN>(a, sh, grid, tm, s);
+    default: return gemv_cpg<BF16, MT8, BITS, DOWN>(a, sh, grid, tm, s);
+  }
+}
 
 }  // namespace moe

@@ -1,53 +1,6 @@
-// Instantiations of the decode dequant-GEMV kernels: gate/up + SwiGLU, f32 activations.
+// Instances of the decode dequant-GEMV: gate/up + SwiGLU, fp32 activations, 4-bit codes.
 #include "k_gemv.h"
 
 namespace moe {
-
-// waves per workgroup: about kBatch chunks of K per wave, at most kMaxW waves
-static int waves_for(const GemvArgs& a, int mt) {
-  const int chunks = a.groups * (a.G / 32);
-  const int wmax = kMaxThreads<1> / 64 >> (mt > 1 ? 1 : 0);  // within the variant's launch bound
-  return std::max(1, std::min(std::min(wmax, a.groups), (chunks + kBatch - 1) / kBatch));
-}
-
-// Activations from an LDS copy when an expert carries several tokens or K is
-// long (measured faster there), and the rows fit in 64 KiB; else scalar loads.
-static bool use_lds(size_t bytes, int mt, int K) { return bytes <= 65536 && (mt >= 2 || K >= 4096); }
-
-// No two-token variant for fp32 rows: it needs more than 256 VGPRs and spills, so
-// experts with 2 tokens take the 4-token kernel (rows past the count are skipped).
-static int pick_mt(int max_tok) { return max_tok <= 1 ? 1 : max_tok <= 4 ? 4 : 8; }
-
-template <int MT, int CPG>
-static void gateup_w(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
-  const size_t lds = (size_t)MT * a.H * 4;
-  if (use_lds(lds, MT, a.H))
-    launch_timed(k_gateup<0, MT, CPG, 1>, dim3(grid), dim3(64 * W), lds, s, tm, a.work,
-                 a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
-                 a.groups, a.tiles, a.H, a.I, a.k);
-  else
-    launch_timed(k_gateup<0, MT, CPG, 0>, dim3(grid), dim3(64 * W), 0, s, tm, a.work,
-                 a.sorted, a.in, a.insum, a.out, a.outpart, a.off_codes, a.off_scales, a.chunks,
-                 a.groups, a.tiles, a.H, a.I, a.k);
-}
-
-template <int MT>
-static void gateup_cpg(const GemvArgs& a, int W, int grid, const Timing& tm, hipStream_t s) {
-  switch (a.G / 32) {
-    case 1: return gateup_w<MT, 1>(a, W, grid, tm, s);
-    case 2: return gateup_w<MT, 2>(a, W, grid, tm, s);
-    case 4: return gateup_w<MT, 4>(a, W, grid, tm, s);
-    default: return gateup_w<MT, 8>(a, W, grid, tm, s);
-  }
-}
-
-void launch_gateup_f32(const GemvArgs& a, int max_tok, int grid, const Timing& tm, hipStream_t s) {
-  const int W = waves_for(a, pick_mt(max_tok));
-  switch (pick_mt(max_tok)) {
-    case 1: return gateup_cpg<1>(a, W, grid, tm, s);
-    case 4: return gateup_cpg<4>(a, W, grid, tm, s);
-    default: return gateup_cpg<8>(a, W, grid, tm, s);
-  }
-}
-
+template void run_gemv<0, 4, false>(const GemvArgs&, const GemvShape&, int, const Timing&, hipStream_t);
 }  // namespace moe

@@ -77,10 +77,11 @@ struct GemvArgs {
   const float* insum;          // gate/up: xsum [T][H/G]; down: hpart [T*k][I/32] (bf16 path)
   void* out;                   // gate/up: h [T*k][I] act dtype; down: o [T*k][H] fp32
   float* outpart;              // gate/up: hpart [T*k][I/32] (bf16 path); down: unused
-  int64_t off_codes, off_scales;
-  int chunks, groups;          // K chunks of 32 and quantisation groups per row
+  int64_t off_codes, off_hi, off_scales;  // code words, 3-bit high planes, scales (offsets in the blob)
+  int chunks, groups;          // 16-byte lane words of K and quantisation groups per row
   int tiles;                   // tiles per expert
   int H, I, G, k, T;
+  int bits;                    // bits per weight code: 4, 3 or 2
 };
 
 struct GemmArgs {

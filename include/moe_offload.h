@@ -24,11 +24,16 @@
  * is read from HBM, every other expert is read by the kernels directly from its
  * host copy over the host link. moe_cache_update moves experts between the two.
  *
- * Canonical expert blob (the weight format of this ABI), per expert:
- *   q_gate[I][H/2] | q_up[I][H/2] | q_down[H][I/2] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G]
- * K is contiguous. Byte j of a row = (q[2j] & 0xF) | (q[2j+1] & 0xF) << 4;
- * nibbles are two's complement (-8..7). Scales are IEEE fp16; s[n][g] covers
- * k in [g*G, (g+1)*G). The library repacks blobs into its own layout.
+ * Canonical expert blob (the weight format of this ABI), per expert, for b =
+ * weight_bits bits per code:
+ *   q_gate[I][H*b/8] | q_up[I][H*b/8] | q_down[H][I*b/8] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G]
+ * K is contiguous. Code i of a row is the unsigned n at bits [b*i, b*i+b) of the
+ * row's little-endian bit string (bit j = bit j % 8 of byte j / 8); for b = 4
+ * that is byte j = (q[2j] & 0xF) | (q[2j+1] & 0xF) << 4. The weight code q:
+ *   b = 4: two's complement, q = n - 16 * (n >= 8), -8..7;
+ *   b = 3, 2: odd symmetric levels, q = 2n - (2^b - 1): -7, -5, ..., 7 / -3, -1, 1, 3.
+ * Scales are IEEE fp16; s[n][g] covers k in [g*G, (g+1)*G); the weight is q * s.
+ * The library repacks blobs into its own layout.
  *
  * Conventions for every call:
  *  - Return a moe_status; nothing is thrown across the ABI. moe_last_error()
@@ -91,6 +96,12 @@ typedef struct {
                               the experts in use in VRAM slots; [125B] section
                               "真正卡死容量的是一块计算缓冲" sizes prefill micro-batches
                               at 1024/2048 tokens, which makes in-place re-reads large */
+  int32_t weight_bits;     /* bits per weight code: 4 (0 = 4), 3 or 2. [763B] section "显存缺口从
+                              哪里来" packs the experts at 3 bits, [24K] section 二 at about 2
+                              bits; neither layout is given, so the library defines its own (see
+                              the canonical blob below). 2 and 3 bits need bf16 activations,
+                              group_size >= 64 and inter a multiple of 64; their forwards run
+                              on the dequant-GEMVs for every batch size (no MFMA path) */
 } moe_config;
 
 typedef struct {
@@ -169,7 +180,7 @@ typedef struct {
   double h2d_copy_gbps;     /* hipMemcpyAsync host -> device from pinned host memory */
 } moe_link_ceilings;
 
-/* Canonical bytes of one expert for cfg: 3*H*I/2 + 6*H*I/G.
+/* Canonical bytes of one expert for cfg: 3*H*I*b/8 + 6*H*I/G (b = weight_bits).
  * Errors: MOE_E_INVALID (cfg). */
 moe_status moe_expert_bytes(const moe_config* cfg, size_t* out);
 

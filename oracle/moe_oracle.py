@@ -58,6 +58,22 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Canonical b-bit decode along the last axis (the lower-bit formats; the pages name
+    3-bit and about 2-bit packages without giving their layouts, so this is the library's
+    own format). Code i of a row is the unsigned n at bits [b*i, b*i+b) of the row's
+    little-endian bit string (bit j = bit j % 8 of byte j // 8). The weight code is
+    q = n - 16 (n >= 8) for b = 4 (two's complement) and q = 2n - (2^b - 1) for b = 3, 2
+    (odd levels, symmetric about zero)."""
+    if bits == 4:
+        return unpack_int4(packed)
+    p = np.asarray(packed, dtype=np.uint8)
+    stream = np.unpackbits(p, axis=-1, bitorder="little")  # bit j of byte i at 8i + j
+    fields = stream.reshape(p.shape[:-1] + (-1, bits)).astype(np.int16)
+    n = (fields * (1 << np.arange(bits, dtype=np.int16))).sum(axis=-1)
+    return (2 * n - ((1 << bits) - 1)).astype(np.int8)
+
+
 def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """IEEE binary16 bit patterns to float64 (exact)."""
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
@@ -69,11 +85,11 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u32.view(np.float32).astype(np.float64)
 
 
-def expert_layout(H: int, I: int, G: int):
-    """Byte ranges of the canonical expert blob, in order:
-    q_gate[I][H/2] | q_up[I][H/2] | q_down[H][I/2] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G].
+def expert_layout(H: int, I: int, G: int, bits: int = 4):
+    """Byte ranges of the canonical expert blob, in order (b = bits per code):
+    q_gate[I][H*b/8] | q_up[I][H*b/8] | q_down[H][I*b/8] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G].
     """
-    sizes = [("q_gate", I * H // 2), ("q_up", I * H // 2), ("q_down", H * I // 2),
+    sizes = [("q_gate", I * H * bits // 8), ("q_up", I * H * bits // 8), ("q_down", H * I * bits // 8),
              ("s_gate", 2 * I * (H // G)), ("s_up", 2 * I * (H // G)), ("s_down", 2 * H * (I // G))]
     out, off = {}, 0
     for name, n in sizes:
@@ -82,8 +98,8 @@ def expert_layout(H: int, I: int, G: int):
     return out, off
 
 
-def expert_bytes(H: int, I: int, G: int) -> int:
-    return expert_layout(H, I, G)[1]
+def expert_bytes(H: int, I: int, G: int, bits: int = 4) -> int:
+    return expert_layout(H, I, G, bits)[1]
 
 
 def dequant(q: np.ndarray, s: np.ndarray, G: int) -> np.ndarray:
@@ -93,9 +109,9 @@ def dequant(q: np.ndarray, s: np.ndarray, G: int) -> np.ndarray:
     return q * np.repeat(s, G, axis=1)
 
 
-def expert_weights(blob: np.ndarray, H: int, I: int, G: int):
+def expert_weights(blob: np.ndarray, H: int, I: int, G: int, bits: int = 4):
     """Dequantised (Wg [I,H], Wu [I,H], Wd [H,I]) of one canonical blob, float64."""
-    lay, total = expert_layout(H, I, G)
+    lay, total = expert_layout(H, I, G, bits)
     blob = np.asarray(blob, dtype=np.uint8)
     assert blob.size == total, (blob.size, total)
 
@@ -103,9 +119,9 @@ def expert_weights(blob: np.ndarray, H: int, I: int, G: int):
         a, b = lay[name]
         return blob[a:b]
 
-    qg = unpack_int4(part("q_gate").reshape(I, H // 2))
-    qu = unpack_int4(part("q_up").reshape(I, H // 2))
-    qd = unpack_int4(part("q_down").reshape(H, I // 2))
+    qg = unpack_codes(part("q_gate").reshape(I, H * bits // 8), bits)
+    qu = unpack_codes(part("q_up").reshape(I, H * bits // 8), bits)
+    qd = unpack_codes(part("q_down").reshape(H, I * bits // 8), bits)
     sg = fp16_bits_to_f64(part("s_gate").view(np.uint16).reshape(I, H // G))
     su = fp16_bits_to_f64(part("s_up").view(np.uint16).reshape(I, H // G))
     sd = fp16_bits_to_f64(part("s_down").view(np.uint16).reshape(H, I // G))
@@ -229,13 +245,13 @@ def expert_ffn(x_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, 
 class ExpertStore:
     """Dequantised experts of one layer, decoded on first use (float64)."""
 
-    def __init__(self, blobs: np.ndarray, H: int, I: int, G: int):
-        self.blobs, self.H, self.I, self.G = blobs, H, I, G
+    def __init__(self, blobs: np.ndarray, H: int, I: int, G: int, bits: int = 4):
+        self.blobs, self.H, self.I, self.G, self.bits = blobs, H, I, G, bits
         self._cache = {}
 
     def get(self, e: int):
         if e not in self._cache:
-            self._cache[e] = expert_weights(self.blobs[e], self.H, self.I, self.G)
+            self._cache[e] = expert_weights(self.blobs[e], self.H, self.I, self.G, self.bits)
         return self._cache[e]
 
     def drop(self, e: int):
@@ -244,12 +260,13 @@ class ExpertStore:
 
 def layer_forward(x: np.ndarray, Wr: np.ndarray | None, b: np.ndarray | None, blobs: np.ndarray,
                   H: int, I: int, E: int, k: int, G: int, act: str,
-                  logits_in: np.ndarray | None = None, tokens=None):
+                  logits_in: np.ndarray | None = None, tokens=None, bits: int = 4):
     """One routed MoE FFN layer, plain definition, float64.
 
     x: [T, H] float64 values of the activations (already in the activation dtype).
     logits_in: if given ([T, E] float32), routing uses these logits instead of the router.
     tokens: optional subset of token indices whose y rows are evaluated (routing is for all).
+    bits: bits per weight code of the blobs (4, 3 or 2; see unpack_codes).
 
     Returns a dict with logits (float32), ids, w, counts, offsets, sorted, inv and y
     ([len(tokens), H] float64). Each FFN_e(x_t) is evaluated on its own; experts are
@@ -267,7 +284,7 @@ def layer_forward(x: np.ndarray, Wr: np.ndarray | None, b: np.ndarray | None, bl
     for t in toks:
         for j in range(k):
             need.setdefault(int(ids[t, j]), []).append((t, j))
-    store = ExpertStore(blobs, H, I, G)
+    store = ExpertStore(blobs, H, I, G, bits)
     o = {}
     for e in sorted(need):
         Wg, Wu, Wd = store.get(e)

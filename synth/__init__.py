@@ -57,6 +57,12 @@ def _load():
     lib.synth_expert_bytes.restype = i64
     lib.synth_expert_bytes.argtypes = [i32, i32, i32]
     lib.synth_experts.argtypes = [u64, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.synth_expert_bytes_b.restype = i64
+    lib.synth_expert_bytes_b.argtypes = [i32, i32, i32, i32]
+    lib.synth_quantize_row_odd.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.synth_pack_bits.argtypes = [vp, i64, i32, vp]
+    lib.synth_experts_b.argtypes = [u64, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.synth_cut_codes.argtypes = [vp, i64, i32, i32, i32, i32, vp]
     lib.synth_expert_tensor_f32.argtypes = [u64, i32, i32, i32, i32, i32, f32, vp]
     _lib = lib
     return lib
@@ -118,16 +124,56 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
     return out
 
 
-def expert_bytes(H: int, I: int, G: int) -> int:
-    return int(_load().synth_expert_bytes(H, I, G))
+def expert_bytes(H: int, I: int, G: int, bits: int = 4) -> int:
+    if bits == 4:
+        return int(_load().synth_expert_bytes(H, I, G))
+    return int(_load().synth_expert_bytes_b(H, I, G, bits))
 
 
 def expert_blobs(base: int, layer: int, e0: int, n: int, H: int, I: int, G: int,
-                 std: float = 0.02) -> np.ndarray:
-    """Canonical blobs of experts [e0, e0+n) of a layer, uint8 [n, expert_bytes]."""
-    out = np.empty((n, expert_bytes(H, I, G)), dtype=np.uint8)
-    _load().synth_experts(base, layer, e0, n, H, I, G, std, _ptr(out))
+                 std: float = 0.02, bits: int = 4) -> np.ndarray:
+    """Canonical blobs of experts [e0, e0+n) of a layer, uint8 [n, expert_bytes]. bits = 3, 2:
+    the same seeded weights quantised onto odd levels (synth_quantize_row_odd)."""
+    out = np.empty((n, expert_bytes(H, I, G, bits)), dtype=np.uint8)
+    if bits == 4:
+        _load().synth_experts(base, layer, e0, n, H, I, G, std, _ptr(out))
+    else:
+        _load().synth_experts_b(base, layer, e0, n, H, I, G, std, bits, _ptr(out))
     return out
+
+
+def cut_codes(blobs4: np.ndarray, H: int, I: int, G: int, bits: int) -> np.ndarray:
+    """b-bit blobs from 4-bit blobs of the same shape (top b bits of each offset code, scales
+    copied): seeded synthetic lower-bit experts for throughput runs, without regenerating."""
+    blobs4 = np.ascontiguousarray(blobs4, dtype=np.uint8)
+    out = np.empty((blobs4.shape[0], expert_bytes(H, I, G, bits)), dtype=np.uint8)
+    _load().synth_cut_codes(_ptr(blobs4), blobs4.shape[0], H, I, G, bits, _ptr(out))
+    return out
+
+
+def quantize_rows_odd(w: np.ndarray, G: int, bits: int):
+    """Odd-level fixture quantiser on rows of w (float32 [R, K]) -> (codes n uint8 [R, K],
+    fp16 bits [R, K/G]); the weight code is q = 2n - (2^bits - 1)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, K = w.shape
+    n = np.empty((R, K), dtype=np.uint8)
+    s = np.empty((R, K // G), dtype=np.uint16)
+    lib = _load()
+    for r in range(R):
+        lib.synth_quantize_row_odd(w[r].ctypes.data, K, G, bits, n[r].ctypes.data, s[r].ctypes.data)
+    return n, s
+
+
+def pack_codes(n: np.ndarray, bits: int) -> np.ndarray:
+    """Canonical packing of unsigned b-bit codes n along the last axis (little-endian bit string)."""
+    n = np.ascontiguousarray(n, dtype=np.uint8)
+    K = n.shape[-1]
+    rows = n.reshape(-1, K)
+    out = np.empty((rows.shape[0], K * bits // 8), dtype=np.uint8)
+    lib = _load()
+    for r in range(rows.shape[0]):
+        lib.synth_pack_bits(rows[r].ctypes.data, K, bits, out[r].ctypes.data)
+    return out.reshape(n.shape[:-1] + (K * bits // 8,))
 
 
 def expert_tensor_f32(base: int, layer: int, expert: int, tensor: int, rows: int, K: int,
@@ -138,9 +184,11 @@ def expert_tensor_f32(base: int, layer: int, expert: int, tensor: int, rows: int
     return out
 
 
-def pack_blob(q_gate, q_up, q_down, s_gate, s_up, s_down) -> np.ndarray:
-    """Assemble one canonical blob from codes (int8) and fp16 scale bits (uint16)."""
-    parts = [pack_int4(q_gate).ravel(), pack_int4(q_up).ravel(), pack_int4(q_down).ravel(),
+def pack_blob(q_gate, q_up, q_down, s_gate, s_up, s_down, bits: int = 4) -> np.ndarray:
+    """Assemble one canonical blob from codes and fp16 scale bits (uint16): bits = 4 takes
+    signed codes q (int8, -8..7); bits = 3, 2 take unsigned codes n (0 .. 2^bits - 1)."""
+    pk = pack_int4 if bits == 4 else (lambda n: pack_codes(n, bits))
+    parts = [pk(q_gate).ravel(), pk(q_up).ravel(), pk(q_down).ravel(),
              np.ascontiguousarray(s_gate, dtype=np.uint16).view(np.uint8).ravel(),
              np.ascontiguousarray(s_up, dtype=np.uint16).view(np.uint8).ravel(),
              np.ascontiguousarray(s_down, dtype=np.uint16).view(np.uint8).ravel()]

@@ -155,6 +155,42 @@ int64_t synth_expert_bytes(int H, int I, int G) {
   return (int64_t)3 * H * I / 2 + (int64_t)2 * 3 * H * I / G;
 }
 
+int64_t synth_expert_bytes_b(int H, int I, int G, int b) {
+  return (int64_t)3 * H * I * b / 8 + (int64_t)2 * 3 * H * I / G;
+}
+
+/*
+ * Fixture quantiser onto b-bit odd levels (b = 2, 3), one row of K weights:
+ *   L = 2^b - 1; amax = max |w| over the group; s = fp16_rne(amax / L);
+ *   n = clamp(rint_half_even((w / float(s) + L) / 2), 0, 2^b - 1), so that
+ *   q = 2n - L is the odd level nearest to w / s; s == 0 gives n = 2^(b-1) (q = 1, weight 0).
+ * Codes n go to n[K], scales to s[K/G] (fp16 bits).
+ */
+void synth_quantize_row_odd(const float* w, int K, int G, int b, uint8_t* n, uint16_t* s) {
+  const float L = (float)((1 << b) - 1);
+  for (int g = 0; g < K / G; ++g) {
+    const float* wg = w + (int64_t)g * G;
+    float amax = 0.f;
+    for (int i = 0; i < G; ++i) amax = fmaxf(amax, fabsf(wg[i]));
+    uint16_t sh = synth_f32_to_f16(amax / L);
+    float sf = synth_f16_to_f32(sh);
+    s[g] = sh;
+    for (int i = 0; i < G; ++i) {
+      float r = (sf == 0.f) ? (float)(1 << (b - 1)) : nearbyintf((wg[i] / sf + L) * 0.5f);
+      r = fminf(fmaxf(r, 0.f), (float)((1 << b) - 1));
+      n[(int64_t)g * G + i] = (uint8_t)r;
+    }
+  }
+}
+
+/* Canonical b-bit packing: code i at bits [b*i, b*i+b) of the little-endian bit string out. */
+void synth_pack_bits(const uint8_t* n, int64_t count, int b, uint8_t* out) {
+  memset(out, 0, (size_t)((count * b + 7) / 8));
+  for (int64_t i = 0; i < count; ++i)
+    for (int j = 0; j < b; ++j)
+      if ((n[i] >> j) & 1u) out[(i * b + j) >> 3] |= (uint8_t)(1u << ((i * b + j) & 7));
+}
+
 /*
  * One canonical expert blob:
  *   q_gate[I][H/2] | q_up[I][H/2] | q_down[H][I/2] | s_gate[I][H/G] | s_up[I][H/G] | s_down[H][I/G]
@@ -180,6 +216,75 @@ static void expert_blob(uint64_t base, int layer, int expert, int H, int I, int 
       synth_quantize_row(wrow, K, G, qrow, sd_out + (int64_t)r * (K / G));
       synth_pack_int4(qrow, K, qd_out + (int64_t)r * (K / 2));
     }
+  }
+}
+
+/* The same expert's weights quantised onto b-bit odd levels (b = 2, 3), canonical b-bit rows. */
+static void expert_blob_b(uint64_t base, int layer, int expert, int H, int I, int G, float stdv, int b,
+                          uint8_t* out, float* wrow, uint8_t* nrow) {
+  int64_t qg = (int64_t)I * H * b / 8, qd = (int64_t)H * I * b / 8;
+  uint8_t* q_gate = out;
+  uint8_t* q_up = out + qg;
+  uint8_t* q_down = out + 2 * qg;
+  uint16_t* s_gate = (uint16_t*)(out + 2 * qg + qd);
+  uint16_t* s_up = s_gate + (int64_t)I * (H / G);
+  uint16_t* s_down = s_up + (int64_t)I * (H / G);
+  for (int t = 0; t < 3; ++t) {
+    int rows = (t < 2) ? I : H, K = (t < 2) ? H : I;
+    uint8_t* qd_out = (t == 0) ? q_gate : (t == 1) ? q_up : q_down;
+    uint16_t* sd_out = (t == 0) ? s_gate : (t == 1) ? s_up : s_down;
+    uint64_t key = synth_key(base, 1, (uint64_t)layer, (uint64_t)expert, (uint64_t)t);
+    for (int r = 0; r < rows; ++r) {
+      synth_normal_f32(key, (int64_t)r * K, K, 0.f, stdv, wrow);
+      synth_quantize_row_odd(wrow, K, G, b, nrow, sd_out + (int64_t)r * (K / G));
+      synth_pack_bits(nrow, K, b, qd_out + (int64_t)r * K * b / 8);
+    }
+  }
+}
+
+/* Blobs of experts [e0, e0+n) with b bits per code (b = 4: synth_experts). */
+void synth_experts_b(uint64_t base, int layer, int e0, int n, int H, int I, int G, float stdv, int b, uint8_t* out) {
+  int64_t eb = synth_expert_bytes_b(H, I, G, b);
+  int K = H > I ? H : I;
+#pragma omp parallel
+  {
+    float* wrow = (float*)malloc(sizeof(float) * (size_t)K);
+    uint8_t* nrow = (uint8_t*)malloc((size_t)K);
+#pragma omp for schedule(dynamic, 1)
+    for (int e = 0; e < n; ++e)
+      expert_blob_b(base, layer, e0 + e, H, I, G, stdv, b, out + (int64_t)e * eb, wrow, nrow);
+    free(wrow);
+    free(nrow);
+  }
+}
+
+/*
+ * b-bit blobs (b = 2, 3) from 4-bit blobs of the same shape, for throughput runs that
+ * need a lower-bit copy of layers already generated: each code keeps the top b bits of
+ * its offset form (n_b = (q + 8) >> (4 - b)), the fp16 scales are copied. A seeded
+ * synthetic b-bit expert of the same shape (not a re-quantisation of the weights).
+ */
+void synth_cut_codes(const uint8_t* in4, int64_t n_experts, int H, int I, int G, int b, uint8_t* out) {
+  const int64_t eb4 = synth_expert_bytes(H, I, G), ebb = synth_expert_bytes_b(H, I, G, b);
+  const int64_t codes4 = (int64_t)3 * H * I / 2, codesb = (int64_t)3 * H * I * b / 8;
+  const int64_t rows = (int64_t)2 * I + H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t e = 0; e < n_experts; ++e) {
+    const uint8_t* src = in4 + e * eb4;
+    uint8_t* dst = out + e * ebb;
+    memset(dst, 0, (size_t)codesb);
+    for (int64_t r = 0; r < rows; ++r) {
+      const int K = r < 2 * I ? H : I;
+      const int64_t o4 = r < 2 * I ? r * (H / 2) : 2 * (int64_t)I * (H / 2) + (r - 2 * I) * (I / 2);
+      const int64_t ob = r < 2 * I ? r * ((int64_t)H * b / 8) : 2 * (int64_t)I * H * b / 8 + (r - 2 * I) * ((int64_t)I * b / 8);
+      for (int i = 0; i < K; ++i) {
+        const uint32_t nib = (src[o4 + i / 2] >> (4 * (i & 1))) & 0xFu;
+        const uint32_t nb = (nib ^ 8u) >> (4 - b);
+        for (int j = 0; j < b; ++j)
+          if ((nb >> j) & 1u) dst[ob + (((int64_t)i * b + j) >> 3)] |= (uint8_t)(1u << ((i * b + j) & 7));
+      }
+    }
+    memcpy(dst + codesb, src + codes4, (size_t)(eb4 - codes4));
   }
 }
 

@@ -34,9 +34,10 @@ class Case:
     Wr: np.ndarray = None        # [E, H] float64 values
     b: np.ndarray = None         # [E] float32
     blobs: np.ndarray = None     # [E, expert_bytes] uint8
+    bits: int = 4                # bits per weight code of the blobs
 
 
-def make_case(H, I, E, k, G, act, T, seed, alpha=0.0, layer=0, std=0.02, only_experts=None, x_stream=0):
+def make_case(H, I, E, k, G, act, T, seed, alpha=0.0, layer=0, std=0.02, only_experts=None, x_stream=0, bits=4):
     """A seeded layer. only_experts: if given, only those experts get generated weights;
     every other expert is filled with seeded random bytes (valid codes, finite scales)
     so that reading a wrong expert changes the result."""
@@ -50,19 +51,20 @@ def make_case(H, I, E, k, G, act, T, seed, alpha=0.0, layer=0, std=0.02, only_ex
         c.x = c.x_bits.astype(np.float64)
         c.Wr = c.Wr_store.astype(np.float64)
     c.b = synth.router_bias(seed, layer, E, alpha)
-    eb = synth.expert_bytes(H, I, G)
+    c.bits = bits
+    eb = synth.expert_bytes(H, I, G, bits)
     if only_experts is None:
-        c.blobs = synth.expert_blobs(seed, layer, 0, E, H, I, G, std)
+        c.blobs = synth.expert_blobs(seed, layer, 0, E, H, I, G, std, bits=bits)
     else:
         rng = np.random.default_rng(seed * 7919 + layer)
         c.blobs = rng.integers(0, 256, size=(E, eb), dtype=np.uint8)
-        lay, _ = O.expert_layout(H, I, G)
+        lay, _ = O.expert_layout(H, I, G, bits)
         # finite, small scales in the filler experts
         a0 = lay["s_gate"][0]
         c.blobs[:, a0:] = np.frombuffer(np.full((E * (eb - a0)) // 2, 0x2000, np.uint16).tobytes(),
                                         np.uint8).reshape(E, eb - a0)
         for e in sorted(set(int(v) for v in only_experts)):
-            c.blobs[e] = synth.expert_blobs(seed, layer, e, 1, H, I, G, std)[0]
+            c.blobs[e] = synth.expert_blobs(seed, layer, e, 1, H, I, G, std, bits=bits)[0]
     return c
 
 
@@ -72,7 +74,7 @@ def oracle_logits(c: Case) -> np.ndarray:
 
 def oracle_forward(c: Case, logits_in=None, tokens=None):
     return O.layer_forward(c.x, c.Wr, c.b, c.blobs, c.H, c.I, c.E, c.k, c.G, c.act, logits_in=logits_in,
-                           tokens=tokens)
+                           tokens=tokens, bits=getattr(c, "bits", 4))
 
 
 def rel_l2(a, ref):
@@ -104,26 +106,29 @@ def valid_topk(logits_row, ids, k, tol):
     return bool(np.all(np.diff(l[sel]) <= 2 * tol))
 
 
-def random_code_blobs(E, H, I, G, seed, p_minus8=0.3):
-    """Canonical blobs whose codes cover all 16 values of the format, with the code -8
-    (nibble 0x8) drawn with probability p_minus8 and the other 15 uniformly; fp16 group
-    scales near 0.8 / sqrt(32 K), so that g, u and o stay of order one. Packed by the
-    generator's C packer."""
+def random_code_blobs(E, H, I, G, seed, p_minus8=0.3, bits=4):
+    """Canonical blobs whose codes cover every value of the format: for 4-bit codes the code
+    -8 (nibble 0x8) drawn with probability p_minus8 and the other 15 uniformly; for 2- and
+    3-bit codes every n uniformly. fp16 group scales near 0.8 / sqrt(K E[q^2]), so that g, u
+    and o stay of order one. Packed by the generator's C packers."""
     rng = np.random.default_rng(seed)
+    eq2 = {4: 32.0, 3: 21.0, 2: 5.0}[bits]
 
     def codes(rows, K):
+        if bits < 4:
+            return rng.integers(0, 1 << bits, size=(rows, K)).astype(np.uint8)
         q = rng.integers(-7, 8, size=(rows, K)).astype(np.int8)
         q[rng.random((rows, K)) < p_minus8] = -8
         return q
 
     def scales(rows, K):
-        s = 0.8 / np.sqrt(32.0 * K) * rng.uniform(0.5, 1.5, size=(rows, K // G))
+        s = 0.8 / np.sqrt(eq2 * K) * rng.uniform(0.5, 1.5, size=(rows, K // G))
         return s.astype(np.float16).view(np.uint16)
 
     out = []
     for _ in range(E):
         out.append(synth.pack_blob(codes(I, H), codes(I, H), codes(H, I), scales(I, H), scales(I, H),
-                                   scales(H, I)))
+                                   scales(H, I), bits=bits))
     return np.stack(out)
 
 

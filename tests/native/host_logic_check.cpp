@@ -3,12 +3,12 @@
 // tests/test_host_logic_native.py. One command per input line; every answer is one
 // line. Floats travel as C99 hex literals, so values cross the pipe exactly.
 //
-//   layout H I G                      -> the Layout fields
-//   repack H I G in_path out_path     -> internal blob of the canonical blob in in_path
+//   layout H I G B                    -> the Layout fields (B bits per code)
+//   repack H I G B in_path out_path   -> internal blob of the canonical blob in in_path
 //   policy E S decay maxp             -> then lines: counts, score, slot_of
 //                                        answers: score, slot_of, promoted pairs, evicted
 //   setres E S decay                  -> then lines: counts, score, slot_of, want
-//   check H I E k G L act T S gmin stage -> "OK" or the reason
+//   check H I E k G L act T S gmin stage bits -> "OK" or the reason
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -62,19 +62,19 @@ int main() {
     std::string cmd;
     in >> cmd;
     if (cmd == "layout") {
-      int64_t H, I, G;
-      in >> H >> I >> G;
-      const Layout L = make_layout(H, I, G);
-      std::printf("%lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld\n", (long long)L.gu_tiles,
-                  (long long)L.gu_chunks, (long long)L.gu_groups, (long long)L.dn_tiles, (long long)L.dn_chunks,
-                  (long long)L.dn_groups, (long long)L.off_gu_codes, (long long)L.off_gu_scales,
-                  (long long)L.off_dn_codes, (long long)L.off_dn_scales, (long long)L.bytes,
-                  (long long)L.canonical_bytes);
+      int64_t H, I, G, B;
+      in >> H >> I >> G >> B;
+      const Layout L = make_layout(H, I, G, B);
+      std::printf("%lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld %lld\n", (long long)L.kc,
+                  (long long)L.gu_tiles, (long long)L.gu_chunks, (long long)L.gu_groups, (long long)L.dn_tiles,
+                  (long long)L.dn_chunks, (long long)L.dn_groups, (long long)L.off_gu_codes, (long long)L.off_gu_hi,
+                  (long long)L.off_gu_scales, (long long)L.off_dn_codes, (long long)L.off_dn_hi,
+                  (long long)L.off_dn_scales, (long long)L.bytes, (long long)L.canonical_bytes);
     } else if (cmd == "repack") {
-      int64_t H, I, G;
+      int64_t H, I, G, B;
       std::string ip, op;
-      in >> H >> I >> G >> ip >> op;
-      const Layout L = make_layout(H, I, G);
+      in >> H >> I >> G >> B >> ip >> op;
+      const Layout L = make_layout(H, I, G, B);
       std::vector<uint8_t> src((size_t)L.canonical_bytes), dst((size_t)L.bytes);
       FILE* f = std::fopen(ip.c_str(), "rb");
       if (!f || std::fread(src.data(), 1, src.size(), f) != src.size()) return 2;
@@ -111,7 +111,7 @@ int main() {
     } else if (cmd == "check") {
       moe_config c{};
       in >> c.hidden >> c.inter >> c.num_experts >> c.top_k >> c.group_size >> c.num_layers >> c.act_dtype >>
-          c.max_tokens >> c.hbm_slots >> c.gemm_min_tokens >> c.prefill_stage_slots;
+          c.max_tokens >> c.hbm_slots >> c.gemm_min_tokens >> c.prefill_stage_slots >> c.weight_bits;
       const std::string why = check_config(c);
       std::printf("%s\n", why.empty() ? "OK" : why.c_str());
     } else if (cmd.empty()) {

@@ -57,72 +57,99 @@ def drv(tmp_path_factory):
     assert rc == 0 and "ERROR" not in err and "runtime error" not in err, err
 
 
-SHAPES = [(256, 128, 32), (384, 96, 32), (512, 256, 64), (256, 256, 256), (2048, 768, 128)]
+SHAPES = [(256, 128, 32, 4), (384, 96, 32, 4), (512, 256, 64, 4), (256, 256, 256, 4), (2048, 768, 128, 4),
+          (256, 128, 64, 2), (512, 256, 128, 2), (256, 128, 64, 3), (384, 192, 64, 3), (2048, 768, 128, 3)]
 
 
-def layout_expected(H, I, G):
-    """The documented rule: regions in order, each 256-byte aligned."""
+def layout_expected(H, I, G, B):
+    """The documented rule: 16-byte lane words of kc = 32 (4-bit) or 64 (2-, 3-bit) values,
+    regions in order (gate/up codes, gate/up high planes, gate/up scales, the same for
+    down), each 256-byte aligned; high planes (512 bytes per block) only for 3-bit codes."""
     up = lambda v: (v + 255) // 256 * 256
-    gu_t, gu_c, gu_g, dn_t, dn_c, dn_g = I // 32, H // 32, H // G, H // 64, I // 32, I // G
-    o1 = 0
-    o2 = up(o1 + gu_t * gu_c * 1024)
-    o3 = up(o2 + gu_t * gu_g * 128)
-    o4 = up(o3 + dn_t * dn_c * 1024)
-    end = up(o4 + dn_t * dn_g * 128)
-    return [gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o1, o2, o3, o4, end, 3 * H * I // 2 + 6 * H * I // G]
+    kc = 32 if B == 4 else 64
+    hib = 512 if B == 3 else 0
+    gu_t, gu_c, gu_g, dn_t, dn_c, dn_g = I // 32, H // kc, H // G, H // 64, I // kc, I // G
+    o_guc = 0
+    o_guh = up(o_guc + gu_t * gu_c * 1024)
+    o_gus = up(o_guh + gu_t * gu_c * hib)
+    o_dnc = up(o_gus + gu_t * gu_g * 128)
+    o_dnh = up(o_dnc + dn_t * dn_c * 1024)
+    o_dns = up(o_dnh + dn_t * dn_c * hib)
+    end = up(o_dns + dn_t * dn_g * 128)
+    return [kc, gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o_guc, o_guh, o_gus, o_dnc, o_dnh, o_dns, end,
+            3 * H * I * B // 8 + 6 * H * I // G]
 
 
-@pytest.mark.parametrize("H,I,G", SHAPES)
-def test_layout(drv, H, I, G):
-    got = [int(v) for v in drv.ask(["layout %d %d %d" % (H, I, G)], 1)[0].split()]
-    assert got == layout_expected(H, I, G)
+@pytest.mark.parametrize("H,I,G,B", SHAPES)
+def test_layout(drv, H, I, G, B):
+    got = [int(v) for v in drv.ask(["layout %d %d %d %d" % (H, I, G, B)], 1)[0].split()]
+    assert got == layout_expected(H, I, G, B)
 
 
-def decode_codes(region, tiles, chunks):
-    """[tiles, 64 lanes, chunks * 32] int codes of a code region: dword d of a lane's 16
-    bytes covers K offsets 8d..8d+7, offset 8d+2j in bits 4j..4j+3 and 8d+2j+1 in bits
-    16+4j..19+4j, stored as n = q + 8."""
+def decode_codes(region, tiles, chunks, B=4, hi_region=None):
+    """[tiles, 64 lanes, chunks * kc] int codes q of a code region (and, for 3-bit codes,
+    its high-plane region). 4-bit: dword d of a lane's 16 bytes covers K offsets
+    8d..8d+7, offset 8d+2j in bits 4j..4j+3 and 8d+2j+1 in bits 16+4j..19+4j, stored as
+    n = q + 8. 2-, 3-bit: dword d covers offsets 16d..16d+15, the low two bits of the
+    code at 16d+2j in bits 2j..2j+1 and of 16d+2j+1 in bits 16+2j..17+2j; high-plane
+    dword e covers offsets 32e..32e+31, bit 2 of the code at 32e+2i in bit i and of
+    32e+2i+1 in bit 16+i; q = 2n - (2^B - 1)."""
     u = np.frombuffer(region.tobytes(), dtype="<u4").reshape(tiles, chunks, 64, 4)
-    q = np.empty((tiles, chunks, 64, 32), dtype=np.int16)
+    if B == 4:
+        q = np.empty((tiles, chunks, 64, 32), dtype=np.int16)
+        for d in range(4):
+            for j in range(4):
+                q[..., 8 * d + 2 * j] = ((u[..., d] >> (4 * j)) & 0xF).astype(np.int16) - 8
+                q[..., 8 * d + 2 * j + 1] = ((u[..., d] >> (16 + 4 * j)) & 0xF).astype(np.int16) - 8
+        return q.transpose(0, 2, 1, 3).reshape(tiles, 64, chunks * 32)
+    n = np.zeros((tiles, chunks, 64, 64), dtype=np.int16)
     for d in range(4):
-        for j in range(4):
-            q[..., 8 * d + 2 * j] = ((u[..., d] >> (4 * j)) & 0xF).astype(np.int16) - 8
-            q[..., 8 * d + 2 * j + 1] = ((u[..., d] >> (16 + 4 * j)) & 0xF).astype(np.int16) - 8
-    return q.transpose(0, 2, 1, 3).reshape(tiles, 64, chunks * 32)
+        for j in range(8):
+            n[..., 16 * d + 2 * j] = (u[..., d] >> (2 * j)) & 3
+            n[..., 16 * d + 2 * j + 1] = (u[..., d] >> (16 + 2 * j)) & 3
+    if B == 3:
+        h = np.frombuffer(hi_region.tobytes(), dtype="<u4").reshape(tiles, chunks, 64, 2)
+        for e in range(2):
+            for i in range(16):
+                n[..., 32 * e + 2 * i] |= (((h[..., e] >> i) & 1) << 2).astype(np.int16)
+                n[..., 32 * e + 2 * i + 1] |= (((h[..., e] >> (16 + i)) & 1) << 2).astype(np.int16)
+    q = 2 * n - ((1 << B) - 1)
+    return q.transpose(0, 2, 1, 3).reshape(tiles, 64, chunks * 64)
 
 
 def decode_scales(region, tiles, groups):
     return np.frombuffer(region.tobytes(), dtype="<u2").reshape(tiles, groups, 64).transpose(0, 2, 1)
 
 
-@pytest.mark.parametrize("H,I,G", SHAPES)
-def test_repack_against_oracle_unpack(drv, tmp_path, H, I, G):
-    """Random bytes cover all 16 codes in both nibble positions; scales are random fp16 bits."""
-    rng = np.random.default_rng(H + I + G)
-    eb = O.expert_bytes(H, I, G)
+@pytest.mark.parametrize("H,I,G,B", SHAPES)
+def test_repack_against_oracle_unpack(drv, tmp_path, H, I, G, B):
+    """Random bytes cover every code value in every position; scales are random fp16 bits."""
+    rng = np.random.default_rng(H + I + G + B)
+    eb = O.expert_bytes(H, I, G, B)
     blob = rng.integers(0, 256, size=eb, dtype=np.uint8)
     src, dst = tmp_path / "c.bin", tmp_path / "i.bin"
     blob.tofile(src)
-    assert drv.ask(["repack %d %d %d %s %s" % (H, I, G, src, dst)], 1) == ["done"]
-    lay = layout_expected(H, I, G)
-    gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o1, o2, o3, o4, end, _ = lay
+    assert drv.ask(["repack %d %d %d %d %s %s" % (H, I, G, B, src, dst)], 1) == ["done"]
+    kc, gu_t, gu_c, gu_g, dn_t, dn_c, dn_g, o_guc, o_guh, o_gus, o_dnc, o_dnh, o_dns, end, _ = \
+        layout_expected(H, I, G, B)
     internal = np.fromfile(dst, dtype=np.uint8)
     assert internal.size == end
-    parts, _ = O.expert_layout(H, I, G)
+    parts, _ = O.expert_layout(H, I, G, B)
     part = lambda n: blob[parts[n][0]:parts[n][1]]
-    qg = O.unpack_int4(part("q_gate").reshape(I, H // 2))
-    qu = O.unpack_int4(part("q_up").reshape(I, H // 2))
-    qd = O.unpack_int4(part("q_down").reshape(H, I // 2))
-    assert set(np.unique(qg).tolist()) == set(range(-8, 8))
-    gu = decode_codes(internal[o1:o1 + gu_t * gu_c * 1024], gu_t, gu_c)
+    qg = O.unpack_codes(part("q_gate").reshape(I, H * B // 8), B)
+    qu = O.unpack_codes(part("q_up").reshape(I, H * B // 8), B)
+    qd = O.unpack_codes(part("q_down").reshape(H, I * B // 8), B)
+    assert len(np.unique(qg)) == 1 << B
+    hi = lambda o, t, c: internal[o:o + t * c * 512] if B == 3 else None
+    gu = decode_codes(internal[o_guc:o_guc + gu_t * gu_c * 1024], gu_t, gu_c, B, hi(o_guh, gu_t, gu_c))
     np.testing.assert_array_equal(gu[:, :32].reshape(I, H), qg)
     np.testing.assert_array_equal(gu[:, 32:].reshape(I, H), qu)
-    dn = decode_codes(internal[o3:o3 + dn_t * dn_c * 1024], dn_t, dn_c)
+    dn = decode_codes(internal[o_dnc:o_dnc + dn_t * dn_c * 1024], dn_t, dn_c, B, hi(o_dnh, dn_t, dn_c))
     np.testing.assert_array_equal(dn.reshape(H, I), qd)
-    sgu = decode_scales(internal[o2:o2 + gu_t * gu_g * 128], gu_t, gu_g)
+    sgu = decode_scales(internal[o_gus:o_gus + gu_t * gu_g * 128], gu_t, gu_g)
     np.testing.assert_array_equal(sgu[:, :32].reshape(I, H // G), part("s_gate").view("<u2").reshape(I, H // G))
     np.testing.assert_array_equal(sgu[:, 32:].reshape(I, H // G), part("s_up").view("<u2").reshape(I, H // G))
-    sdn = decode_scales(internal[o4:o4 + dn_t * dn_g * 128], dn_t, dn_g)
+    sdn = decode_scales(internal[o_dns:o_dns + dn_t * dn_g * 128], dn_t, dn_g)
     np.testing.assert_array_equal(sdn.reshape(H, I // G), part("s_down").view("<u2").reshape(H, I // G))
 
 
@@ -192,21 +219,23 @@ def test_cache_set_resident_matches_oracle(drv):
         assert got[3] == [int(a) for a in ref[3]]
 
 
-def _valid(H, I, E, k, G, L, act, T, S, gmin, stage):
+def _valid(H, I, E, k, G, L, act, T, S, gmin, stage, bits):
     """The configuration rules as the header states them."""
+    b = 4 if bits == 0 else bits
+    low_ok = b == 4 or (act == 1 and G >= 64 and I % 64 == 0)
     return (H > 0 and I > 0 and G in (32, 64, 128, 256) and H % 64 == 0 and I % 32 == 0 and H % G == 0
             and I % G == 0 and 1 <= E <= 1024 and 1 <= k <= min(E, 32) and L >= 1 and act in (0, 1)
             and 1 <= T <= (1 << 20) and T * k <= (1 << 22) and 0 <= S <= E and 0 <= stage <= E
-            and H <= 65536 and I <= 65536)
+            and H <= 65536 and I <= 65536 and b in (2, 3, 4) and low_ok)
 
 
 def test_check_config_matches_stated_rules(drv):
     rng = np.random.default_rng(7)
-    base = [2048, 768, 128, 8, 128, 1, 1, 16, 90, 0, 0]
+    base = [2048, 768, 128, 8, 128, 1, 1, 16, 90, 0, 0, 0]
     cases = [base]
     alts = {0: [0, -64, 64, 96, 65536, 65600], 1: [0, 32, 48, 96, 65536], 2: [0, 1, 1024, 1025], 3: [0, 1, 32, 33],
             4: [16, 32, 48, 64, 256, 512], 5: [0, 1, 48], 6: [-1, 0, 1, 2], 7: [0, 1, 1 << 20, (1 << 20) + 1],
-            8: [-1, 0, 128, 129], 9: [-1, 0, 6], 10: [-1, 0, 128, 129]}
+            8: [-1, 0, 128, 129], 9: [-1, 0, 6], 10: [-1, 0, 128, 129], 11: [-1, 0, 1, 2, 3, 4, 5, 8]}
     for i, vals in alts.items():
         for v in vals:
             c = list(base)
@@ -214,7 +243,7 @@ def test_check_config_matches_stated_rules(drv):
             cases.append(c)
     for _ in range(200):
         c = list(base)
-        for i in rng.choice(11, size=3, replace=False):
+        for i in rng.choice(12, size=3, replace=False):
             c[i] = int(rng.choice(alts[int(i)]))
         cases.append(c)
     for c in cases:

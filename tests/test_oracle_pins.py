@@ -72,11 +72,70 @@ def test_dequant_group_indexing_brute_force():
             assert W[r, k] == q[r, k] * s[r, k // G]
 
 
+def _decode_bitstring(row_bytes, K, bits):
+    """n codes of a canonical row, read off the row as one little-endian integer."""
+    v = int.from_bytes(bytes(row_bytes), "little")
+    return [(v >> (bits * i)) & ((1 << bits) - 1) for i in range(K)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_unpack_codes_every_code_at_every_alignment(bits):
+    """Every pair of adjacent codes at every bit offset within a byte (3-bit codes cross
+    byte boundaries), packed by the C packer and read back by the oracle, against a
+    decode of the row as one integer and the format's q rule."""
+    rng = np.random.default_rng(bits)
+    L = 1 << bits
+    rows = []
+    for pos in range(8):
+        for a in range(L):
+            for c in range(L):
+                n = rng.integers(0, L, size=32).astype(np.uint8)
+                n[pos], n[pos + 1] = a, c
+                rows.append(n)
+    n = np.stack(rows)
+    packed = synth.pack_codes(n, bits) if bits < 4 else synth.pack_int4(
+        np.where(n >= 8, n.astype(np.int16) - 16, n).astype(np.int8))
+    q = O.unpack_codes(packed, bits)
+    for r in range(0, n.shape[0], 7):
+        nn = _decode_bitstring(packed[r], 32, bits)
+        assert nn == n[r].tolist()
+    want = (n.astype(np.int16) - 16 * (n >= 8)) if bits == 4 else (2 * n.astype(np.int16) - (L - 1))
+    np.testing.assert_array_equal(q, want)
+    if bits == 4:
+        np.testing.assert_array_equal(q, O.unpack_int4(packed))
+    else:
+        assert sorted(set(q.ravel().tolist())) == list(range(-(L - 1), L, 2))  # the odd levels
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_odd_level_quantiser_and_dequant(bits):
+    """The generator's odd-level quantiser: |w - q s| <= s (1 + 2^-10) with q the nearest odd
+    level; the expert blob of the generator holds exactly these codes and scales; q * s is
+    exact in float32."""
+    H, I, G = 128, 64, 64
+    L = (1 << bits) - 1
+    blob = synth.expert_blobs(9, 0, 3, 1, H, I, G, std=0.02, bits=bits)[0]
+    Wg, Wu, Wd = O.expert_weights(blob, H, I, G, bits)
+    for t, W, rows, K in ((0, Wg, I, H), (1, Wu, I, H), (2, Wd, H, I)):
+        w = synth.expert_tensor_f32(9, 0, 3, t, rows, K)
+        n, sb = synth.quantize_rows_odd(w, G, bits)
+        s = O.fp16_bits_to_f64(sb)
+        q = 2 * n.astype(np.float64) - L
+        np.testing.assert_array_equal(W, q * np.repeat(s, G, axis=1))
+        err = np.abs(w.astype(np.float64) - W)
+        assert (err <= np.repeat(s, G, axis=1) * (1 + 2 ** -10) + 1e-12).all()
+        p32 = (q.astype(np.float32) * np.repeat(s, G, axis=1).astype(np.float32)).astype(np.float64)
+        np.testing.assert_array_equal(p32, W)
+
+
 def test_expert_layout_sizes():
     assert O.expert_bytes(256, 128, 32) == 55296
     assert O.expert_bytes(2048, 768, 128) == 2433024
     assert O.expert_bytes(7168, 2048, 128) == 22708224
     assert O.expert_bytes(2048, 768, 128) == synth.expert_bytes(2048, 768, 128)
+    for bits in (2, 3):
+        assert O.expert_bytes(7168, 2048, 128, bits) == 3 * 7168 * 2048 * bits // 8 + 6 * 7168 * 2048 // 128
+        assert O.expert_bytes(7168, 2048, 128, bits) == synth.expert_bytes(7168, 2048, 128, bits)
 
 
 def test_expert_weights_split_matches_generator_tensors():
@@ -317,8 +376,8 @@ def test_ffn_identity_expert_closed_form():
     np.testing.assert_allclose(y, ref, rtol=1e-15, atol=0)
 
 
-def tiny_layer(seed, H=64, I=32, E=6, G=32):
-    blobs = synth.expert_blobs(100 + seed, 0, 0, E, H, I, G, std=0.05)
+def tiny_layer(seed, H=64, I=32, E=6, G=32, bits=4):
+    blobs = synth.expert_blobs(100 + seed, 0, 0, E, H, I, G, std=0.05, bits=bits)
     rng = np.random.default_rng(seed)
     x = O.round_bf16(rng.standard_normal((7, H)))
     Wr = O.round_bf16(rng.standard_normal((E, H)) * 0.1)
@@ -326,13 +385,13 @@ def tiny_layer(seed, H=64, I=32, E=6, G=32):
     return blobs, x, Wr, b
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 6])
-def test_layer_matches_dense_brute_force(k):
+@pytest.mark.parametrize("k,bits", [(1, 4), (2, 4), (3, 4), (6, 4), (2, 3), (3, 2)])
+def test_layer_matches_dense_brute_force(k, bits):
     """Every expert on every token (einsum over all experts at once), masked by top-k."""
-    H, I, E, G = 64, 32, 6, 32
-    blobs, x, Wr, b = tiny_layer(k, H, I, E, G)
-    res = O.layer_forward(x, Wr, b, blobs, H, I, E, k, G, "bf16")
-    Ws = [O.expert_weights(blobs[e], H, I, G) for e in range(E)]
+    H, I, E, G = 64, 64 if bits < 4 else 32, 6, 64 if bits < 4 else 32
+    blobs, x, Wr, b = tiny_layer(k, H, I, E, G, bits)
+    res = O.layer_forward(x, Wr, b, blobs, H, I, E, k, G, "bf16", bits=bits)
+    Ws = [O.expert_weights(blobs[e], H, I, G, bits) for e in range(E)]
     Wg = np.stack([w[0] for w in Ws]); Wu = np.stack([w[1] for w in Ws]); Wd = np.stack([w[2] for w in Ws])
     g = np.einsum("eih,th->tei", Wg, x)
     u = np.einsum("eih,th->tei", Wu, x)

@@ -60,3 +60,23 @@ def test_zipf_bias():
     b = synth.router_bias(1, 3, 128, 0.8)
     np.testing.assert_allclose(b, -0.8 * np.log(r), rtol=1e-6)
     assert not np.array_equal(r, synth.zipf_ranks(1, 4, 128))  # per-layer permutation
+
+
+def test_cut_codes_keeps_top_bits_and_scales():
+    """The lower-bit copies the benchmark makes of generated 4-bit layers: every code is the
+    top b bits of the 4-bit offset code (q + 8), read back by the oracle's decoders, and
+    the fp16 scales are unchanged."""
+    from oracle import moe_oracle as O
+    H, I, G = 256, 128, 64
+    b4 = synth.expert_blobs(5, 0, 0, 2, H, I, G)
+    lay4, _ = O.expert_layout(H, I, G, 4)
+    for bits in (2, 3):
+        bb = synth.cut_codes(b4, H, I, G, bits)
+        layb, _ = O.expert_layout(H, I, G, bits)
+        assert bb.shape == (2, O.expert_bytes(H, I, G, bits))
+        for e in range(2):
+            for nm in ("q_gate", "q_up", "q_down"):
+                q4 = O.unpack_int4(b4[e, lay4[nm][0]:lay4[nm][1]].reshape(1, -1)).astype(np.int16)
+                qb = O.unpack_codes(bb[e, layb[nm][0]:layb[nm][1]].reshape(1, -1), bits).astype(np.int16)
+                np.testing.assert_array_equal(qb, 2 * ((q4 + 8) >> (4 - bits)) - ((1 << bits) - 1))
+            np.testing.assert_array_equal(bb[e, layb["s_gate"][0]:], b4[e, lay4["s_gate"][0]:])
