@@ -68,6 +68,10 @@ def parse_args():
     ap.add_argument("--deepseek-runs", default="mixed:1,mixed:4,mixed:16,hbm:1,hbm:4,hbm:16,host:1,host:4,host:16",
                     help="plan:batch runs of the DeepSeek-style layer, in order (plans mixed, hbm, host)")
     ap.add_argument("--lowbit", default="3,2", help="code widths below 4 bits also run on the DeepSeek-style layers")
+    ap.add_argument("--host-runs", default="misses:1,misses:4,misses:16,layer:1,layer:4",
+                    help="DeepSeek-style runs with host computation: misses:B = the 70/30 plan with the host cores "
+                         "computing the offloaded experts; layer:B = one layer in four computed entirely by the "
+                         "host cores, the rest all in HBM (layer-granular placement)")
     ap.add_argument("--lowbit-runs", default="mixed:1,mixed:4,hbm:1,host:1",
                     help="plan:batch runs of the DeepSeek-style layers at each lower code width")
     ap.add_argument("--qwen3-layers", type=int, default=24)
@@ -336,6 +340,25 @@ def run_deepseek(args, out):
         r = layer_result("deepseek", key, B, kind, L, steps, args.warmup, el, st, pk, slots)
         log("deepseek %s B%d: %.1f layer-tokens/s, %s" % (kind, B, r["value"], r["roofline"]["frac"]))
         res[key] = r
+    for item in [it for it in args.host_runs.split(",") if it.strip()]:
+        kind, B = item.split(":")
+        B = int(B)
+        if kind == "misses":  # 70/30 residency, offloaded experts computed by the host cores
+            plan.cache_update(-1, want_resident=wants["mixed"])
+            plan.set_host_compute(-1, moe.HOST_COMPUTE_MISSES)
+            current, slots, label = "mixed", int(wants["mixed"][0].sum()), "mixed, offloaded experts on host cores"
+        else:  # layer-granular: layer 0 entirely on the host cores, layers 1.. all in HBM
+            plan.cache_update(-1, want_resident=wants["hbm"])
+            plan.set_host_compute(-1, moe.HOST_COMPUTE_NONE)
+            plan.set_host_compute(0, moe.HOST_COMPUTE_LAYER)
+            current, slots, label = "hbm", d["E"], "all in HBM, 1 of %d layers on host cores" % L
+        el, st, pk = time_steps(plan, L, xs[B][0], y[:B], args.steps, args.warmup)
+        key = "deepseek_host%s_b%d" % (kind, B)
+        r = layer_result("deepseek", key, B, label, L, args.steps, args.warmup, el, st, pk, slots)
+        r["layer"]["host_computed_experts_per_step"] = round(st["host_computed"] / max(st["forwards"], 1), 4)
+        log("deepseek host %s B%d: %.1f layer-tokens/s" % (kind, B, r["value"]))
+        res[key] = r
+        plan.set_host_compute(-1, moe.HOST_COMPUTE_NONE)
     plan.destroy()
     for b in widths:
         cfgb = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=16,

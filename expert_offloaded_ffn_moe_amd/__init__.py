@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_offload.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_NOMEM, MOE_E_HOST_NOMEM, MOE_E_HIP, MOE_E_UNSUPPORTED, MOE_E_STATE = range(7)
 ACT_F32, ACT_BF16 = 0, 1
+HOST_COMPUTE_NONE, HOST_COMPUTE_MISSES, HOST_COMPUTE_LAYER = 0, 1, 2
 
 
 class Config(ctypes.Structure):
@@ -38,7 +39,7 @@ class Routing(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("forwards", "tokens", "hits", "misses", "bytes_hbm", "bytes_host",
-                                              "bytes_copied", "promotions", "evictions")]
+                                              "bytes_copied", "promotions", "evictions", "host_computed")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -104,6 +105,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.moe_measure_link_ceilings.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i32, vp, ctypes.POINTER(LinkCeilings)]
     lib.moe_debug_fail_alloc.argtypes = [i32, i32]
+    lib.moe_plan_set_host_compute.argtypes = [vp, i32, i32, i32]
     lib.moe_debug_live_allocs.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
     lib.moe_layer_forward_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
@@ -122,7 +124,7 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
                "moe_layer_forward_noalloc",
                "moe_cache_update", "moe_plan_stats", "moe_plan_reset_stats", "moe_plan_residency",
                "moe_plan_profile", "moe_plan_kernel_times", "moe_plan_get_info", "moe_measure_link_ceilings",
-               "moe_debug_fail_alloc", "moe_debug_live_allocs"):
+               "moe_debug_fail_alloc", "moe_debug_live_allocs", "moe_plan_set_host_compute"):
         getattr(lib, fn).restype = st
     _lib = lib
     return lib
@@ -263,6 +265,12 @@ class Plan:
         pol = CachePolicy(decay, max_promotions, 1 if overlap else 0, _ptr(want))
         _check(self.lib.moe_cache_update(self.handle, layer, ctypes.byref(pol), _stream(stream)),
                "moe_cache_update")
+
+    def set_host_compute(self, layer=-1, mode=HOST_COMPUTE_MISSES, threads=0):
+        """Where the layer's experts are computed: HOST_COMPUTE_NONE (the GPU, offloaded ones
+        read over the host link), HOST_COMPUTE_MISSES (the host cores compute the offloaded
+        ones), HOST_COMPUTE_LAYER (the host cores compute all of them)."""
+        _check(self.lib.moe_plan_set_host_compute(self.handle, layer, mode, threads), "moe_plan_set_host_compute")
 
     def info(self) -> dict:
         out = PlanInfo()

@@ -15,10 +15,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "k_route.hip", "k_gemv.hip", "k_gemv_gateup_bf16.hip", "k_gemv_gateup_f32.hip",
            "k_gemv_down_bf16.hip", "k_gemv_down_f32.hip", "k_gemm.hip", "k_stage.hip", "k_util.hip", "k_gemv_lowbit_gateup.hip",
-           "k_gemv_lowbit_down.hip", "host_logic.cpp"]
+           "k_gemv_lowbit_down.hip", "host_logic.cpp", "host_ffn.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 # packed fp32 math is kept out of every kernel
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# the host expert FFN is AVX-512 code; the library calls it only where the CPU has AVX-512
+HOST_FLAGS = {"host_ffn.cpp": ["-mavx512f", "-mavx512bw", "-mavx512vl", "-mf16c", "-mfma"]}
 
 
 def _compile(src: str) -> str:
@@ -27,7 +29,7 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         cmd = [HIPCC] + HIP_FLAGS + COMMON + ["-c", path, "-o", obj]
     else:
-        cmd = ["g++"] + COMMON + ["-Wall", "-c", path, "-o", obj]
+        cmd = ["g++"] + COMMON + ["-Wall", "-c", path, "-o", obj] + HOST_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))

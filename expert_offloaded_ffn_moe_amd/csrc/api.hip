@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <linux/mempolicy.h>
+#include <sched.h>
 #include <sys/syscall.h>
 #include <unistd.h>
 
@@ -25,6 +26,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "host_ffn.h"
 #include "host_logic.h"
 #include "kernels.h"
 #include "moe_offload.h"
@@ -88,6 +90,8 @@ struct Layer {
   std::vector<Promotion> pending;    // pipelined update: copies in flight, table still reads host
   bool loaded = false;
   int64_t bytes_copied = 0, promotions = 0, evictions = 0;
+  int host_mode = MOE_HOST_COMPUTE_NONE;  // moe_plan_set_host_compute
+  int64_t host_computed = 0;             // unique experts computed by the host cores, summed over forwards
 };
 
 struct Workspace {
@@ -151,6 +155,14 @@ struct moe_plan {
   hipEvent_t ev_counts[2] = {nullptr, nullptr}, ev_table[2] = {nullptr, nullptr}, ev_copy = nullptr;
   bool counts_recorded[2] = {false, false}, table_recorded[2] = {false, false}, copy_pending = false;
   unsigned update_seq = 0;
+  // host computation of experts: worker pool, pinned staging of the routing results,
+  // the activations and the host-computed o rows, and host scratch for packed rows
+  HostPool* host_pool = nullptr;
+  int32_t* hs_route = nullptr;  // n_active[2] | active[E] | offsets[E+1] | sorted[Tmax*k]
+  void* hs_x = nullptr;         // [Tmax][H] act dtype
+  float* hs_o = nullptr;        // [Tmax*k][H]
+  std::vector<float> hx, hh;    // packed x rows [Tmax*k][H], h rows [Tmax*k][I]
+  hipEvent_t ev_route = nullptr;
 };
 
 namespace {
@@ -250,6 +262,8 @@ void free_plan(moe_plan* p) {
   for (hipEvent_t e : {p->ev_counts[0], p->ev_counts[1], p->ev_table[0], p->ev_table[1], p->ev_copy})
     if (e) (void)hipEventDestroy(e);
   if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
+  if (p->ev_route) (void)hipEventDestroy(p->ev_route);
+  delete p->host_pool;
   for (void* q : p->dev_allocs) (void)hipFree(q);
   for (void* q : p->host_allocs) (void)hipHostFree(q);
   g_live[0] -= (int64_t)p->dev_allocs.size();
@@ -788,6 +802,55 @@ moe_status moe_plan_get_info(moe_plan* p, moe_plan_info* out) {
 
 namespace {
 
+// The host part of a forward on a host-compute layer: wait for the routing results,
+// compute the experts the GPU skipped (the host-read ones, or all) from their host
+// copies, and copy their o rows into the workspace at their sorted positions (each
+// expert's rows are contiguous there), on `s` after the GEMVs, before the combine.
+moe_status host_part(moe_plan* p, Layer& ly, int T, Workspace& w, hipStream_t s) {
+  const moe_config& c = p->cfg;
+  const int E = c.num_experts, H = c.hidden, k = c.top_k;
+  HIP_TRY(hipEventSynchronize(p->ev_route));
+  const int32_t* hr = p->hs_route;
+  const int n_act = hr[0], n_host = hr[1];
+  const int32_t* active = hr + 2;
+  const int32_t* offsets = hr + 2 + E;
+  const int32_t* sorted = hr + 3 + 2 * E;
+  const int n = ly.host_mode == MOE_HOST_COMPUTE_LAYER ? n_act : n_host;
+  if (n <= 0) return MOE_OK;
+  std::vector<const uint8_t*> blobs(n);
+  std::vector<int> M(n), xoff(n);
+  int rows = 0;
+  const bool bf16 = c.act_dtype == MOE_ACT_BF16;
+  for (int i = 0; i < n; ++i) {
+    const int e = active[i];
+    blobs[i] = ly.host_pool + (size_t)e * p->L.bytes;
+    M[i] = offsets[e + 1] - offsets[e];
+    xoff[i] = rows;
+    for (int r = 0; r < M[i]; ++r) {  // token rows of the expert, in sorted order, as fp32
+      const int t = sorted[offsets[e] + r] / k;
+      float* dst = p->hx.data() + (size_t)(rows + r) * H;
+      if (bf16) {
+        const uint16_t* src = static_cast<const uint16_t*>(p->hs_x) + (size_t)t * H;
+        for (int j = 0; j < H; ++j) {
+          const uint32_t u = (uint32_t)src[j] << 16;
+          std::memcpy(dst + j, &u, 4);
+        }
+      } else {
+        std::memcpy(dst, static_cast<const float*>(p->hs_x) + (size_t)t * H, sizeof(float) * H);
+      }
+    }
+    rows += M[i];
+  }
+  host_experts_ffn(p->L, n, blobs.data(), M.data(), xoff.data(), p->hx.data(), p->hh.data(), p->hs_o, bf16,
+                   *p->host_pool);
+  for (int i = 0; i < n; ++i)
+    HIP_TRY(hipMemcpyAsync(w.o + (size_t)offsets[active[i]] * H, p->hs_o + (size_t)xoff[i] * H,
+                           sizeof(float) * M[i] * H, hipMemcpyHostToDevice, s));
+  ly.host_computed += n;
+  (void)T;
+  return MOE_OK;
+}
+
 // The forward of moe_layer_forward on the workspace `w` (the plan's, or one carved
 // from the static scratch array for moe_layer_forward_noalloc).
 moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
@@ -834,6 +897,7 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   rt.wptr = ly.d_wptr;
   rt.hist = w.hist;
   rt.act_pos = w.act_pos;
+  rt.skip_host = ly.host_mode;
 
   // one-launch routing for small batches (its router walks the tokens one by one;
   // past a few bf16 tokens the MFMA router and the multi-block grouping are faster)
@@ -841,13 +905,17 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   // the grouped MFMA GEMMs and the fused down + combine kernels take 4-bit codes only;
   // 2- and 3-bit layers run every batch on the dequant-GEMVs
   const bool int4 = p->L.bits == 4;
-  const bool prefill = bf16 && int4 && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
+  // layers whose experts the host cores compute (some or all) run on the GEMVs with the
+  // down projection and the combine apart, so the combine can merge the host's rows
+  const int hmode = ly.host_mode;
+  const bool prefill =
+      bf16 && int4 && hmode == MOE_HOST_COMPUTE_NONE && c.gemm_min_tokens > 0 && T >= c.gemm_min_tokens && !decode;
   rt.work = prefill ? nullptr : w.work;
   // a few tokens: down projection and combine in one launch (K split over the free
   // waves), when its (H/64) x T workgroups still keep the CUs streaming; below that
   // the per-expert down GEMV spreads the same bytes over more workgroups
   const int down_splits = std::max(1, std::min(16 / k, (int)p->L.dn_groups));
-  const bool fuse_small = bf16 && int4 && decode && T <= kDownCombMaxTokens && k <= 16;
+  const bool fuse_small = bf16 && int4 && hmode == MOE_HOST_COMPUTE_NONE && decode && T <= kDownCombMaxTokens && k <= 16;
   const bool fuse_down = fuse_small && (H / 64) * T >= kDownCombMinGroups;
   // fewer 64-row tiles than that: the same fusion on 16-row tiles of H, with the
   // K chunks of each wave spread over its four 16-lane quarters
@@ -979,6 +1047,17 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
   }
 
+  if (hmode != MOE_HOST_COMPUTE_NONE) {  // the routing results and x for the host part
+    LAUNCH_USES("copies to the host", WB_NACTIVE | WB_ACTIVE | WB_OFFSETS | WB_SORTED, 0);
+    int32_t* hr = p->hs_route;
+    HIP_TRY(hipMemcpyAsync(hr, w.n_active, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(hr + 2, w.active, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(hr + 2 + E, w.offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(hr + 3 + 2 * E, w.sorted, sizeof(int32_t) * A, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(p->hs_x, x, p->act_size * T * H, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipEventRecord(p->ev_route, s));
+  }
+
   if (!prefill) {  // decode / small-batch path: dequant-GEMVs over the active experts
     const int max_act = std::min(E, A);
     GemvArgs ga{};
@@ -1046,6 +1125,10 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
         LAUNCH_USES("k_down", WB_WORK | WB_H | (bf16 ? WB_HPART : 0), WB_O);
         KernelTimer kt(p, MOE_K_DOWN);
         launch_down(da, bf16, std::min(T, 8), max_act * da.tiles, kt.tm, s);
+      }
+      if (hmode != MOE_HOST_COMPUTE_NONE) {
+        moe_status st = host_part(p, ly, T, w, s);
+        if (st != MOE_OK) return st;
       }
       CombineArgs ca{};
       ca.o = w.o;
@@ -1193,6 +1276,48 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
   return MOE_OK;
 }
 
+moe_status moe_plan_set_host_compute(moe_plan* p, int32_t layer, int32_t mode, int32_t threads) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (layer < -1 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (mode < MOE_HOST_COMPUTE_NONE || mode > MOE_HOST_COMPUTE_LAYER) return fail(MOE_E_INVALID, "bad mode");
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? p->cfg.num_layers : layer + 1;
+  if (mode != MOE_HOST_COMPUTE_NONE) {
+    if (p->L.bits != 4) return fail(MOE_E_UNSUPPORTED, "host computation takes 4-bit codes only");
+    if (!host_ffn_supported()) return fail(MOE_E_UNSUPPORTED, "host computation needs AVX-512 (F, BW, VL) and F16C");
+    if (!p->host_pool) {  // pinned staging and the worker pool, once per plan
+      const moe_config& c = p->cfg;
+      const size_t Tm = (size_t)c.max_tokens, A = Tm * c.top_k, E = c.num_experts;
+      void* v = nullptr;
+      moe_status st = host_alloc(p, &v, sizeof(int32_t) * (3 + 2 * E + A), 0);
+      if (st != MOE_OK) return st;
+      p->hs_route = static_cast<int32_t*>(v);
+      st = host_alloc(p, &p->hs_x, p->act_size * Tm * c.hidden, 0);
+      if (st != MOE_OK) return st;
+      st = host_alloc(p, &v, sizeof(float) * A * c.hidden, 0);
+      if (st != MOE_OK) return st;
+      p->hs_o = static_cast<float*>(v);
+      if (!p->ev_route && hipEventCreateWithFlags(&p->ev_route, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_E_HIP, "creating the routing event failed");
+      }
+      try {
+        p->hx.assign(A * c.hidden, 0.f);
+        p->hh.assign(A * c.inter, 0.f);
+      } catch (const std::bad_alloc&) {
+        return fail(MOE_E_HOST_NOMEM, "host scratch for the host computation");
+      }
+      int n = threads;
+      if (n <= 0) {
+        cpu_set_t set;
+        n = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : (int)std::thread::hardware_concurrency();
+      }
+      p->host_pool = new HostPool(std::max(1, n));
+    }
+  }
+  for (int l = l0; l < l1; ++l) p->layers[l].host_mode = mode;
+  return MOE_OK;
+}
+
 moe_status moe_plan_stats(moe_plan* p, int32_t layer, moe_stats* out) {
   if (!p || !out) return fail(MOE_E_INVALID, "null argument");
   if (layer < -1 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
@@ -1213,6 +1338,7 @@ moe_status moe_plan_stats(moe_plan* p, int32_t layer, moe_stats* out) {
     out->bytes_copied += ly.bytes_copied;
     out->promotions += ly.promotions;
     out->evictions += ly.evictions;
+    out->host_computed += ly.host_computed;
   }
   return MOE_OK;
 }
@@ -1223,7 +1349,7 @@ moe_status moe_plan_reset_stats(moe_plan* p) {
   HIP_TRY(hipDeviceSynchronize());
   for (Layer& ly : p->layers) {
     HIP_TRY(hipMemset(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT));
-    ly.bytes_copied = ly.promotions = ly.evictions = 0;
+    ly.bytes_copied = ly.promotions = ly.evictions = ly.host_computed = 0;
   }
   HIP_TRY(hipDeviceSynchronize());
   return MOE_OK;

@@ -254,7 +254,7 @@ __device__ __forceinline__ void align_one(const RouteArgs& a, DecodeShared& sh) 
     WorkDesc* d = a.work + ap;
     d->w = sh.wptr[e];
     d->p0 = off;
-    d->M = cnt;
+    d->M = skipped(a, host) ? 0 : cnt;
     const float inv_k = 1.f / (float)a.k;
     uint64_t mm = eq;
     for (int j = 0; mm && j < kDescTok; ++j) {
@@ -264,7 +264,8 @@ __device__ __forceinline__ void align_one(const RouteArgs& a, DecodeShared& sh) 
   }
   for (int sl = n_act + lane; sl < min(E, n); sl += 64) a.work[sl].M = 0;
   if (lane == 0) {
-    *a.n_active = n_act;
+    a.n_active[0] = n_act;
+    a.n_active[1] = n_host;
     unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
     atomicAdd(st + ST_FORWARDS, 1ull);
     atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
@@ -364,7 +365,7 @@ __device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh
     WorkDesc* d = a.work + ap;
     d->w = sh.wptr[e];
     d->p0 = sh.a_off[tid];
-    d->M = cnt;
+    d->M = skipped(a, host) ? 0 : cnt;
     const float inv_k = 1.f / (float)a.k;
     int j = 0;
     for (int c = 0; c < NC && j < kDescTok; ++c) {
@@ -380,7 +381,8 @@ __device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh
   // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
   for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
   if (tid == 0) {
-    *a.n_active = n_act;
+    a.n_active[0] = n_act;
+    a.n_active[1] = n_host;
     unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats);
     atomicAdd(st + ST_FORWARDS, 1ull);
     atomicAdd(st + ST_TOKENS, (unsigned long long)a.T);
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
     if (a.work) {
       a.work[pos].w = a.wptr[e];
       a.work[pos].p0 = sh.off[e];
-      a.work[pos].M = sh.cnt[e];
+      a.work[pos].M = skipped(a, i0 < E) ? 0 : sh.cnt[e];
     }
   }
   if (f1) {
@@ -606,12 +608,12 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
     if (a.work) {
       a.work[pos + f0].w = a.wptr[e];
       a.work[pos + f0].p0 = sh.off[e];
-      a.work[pos + f0].M = sh.cnt[e];
+      a.work[pos + f0].M = skipped(a, i1 < E) ? 0 : sh.cnt[e];
     }
   }
   if (a.work)  // unused GEMV slots up to min(E, T*k) (the GEMV grid) have no rows
     for (int sl = n_act + tid; sl < min(E, n); sl += blockDim.x) a.work[sl].M = 0;
-  if (tid == 0) *a.n_active = n_act;
+  if (tid == 0) a.n_active[0] = n_act;
   if (a.tiles) {  // prefill GEMM tiles of kGemmRows rows, expert by expert
     const int ntile = (tid < E) ? (c + kGemmRows - 1) / kGemmRows : 0;
     int n_all;
@@ -634,6 +636,7 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
     atomicAdd(st + ST_MISSES, (unsigned long long)sh.stat[1]);
     atomicAdd(st + ST_BYTES_HBM, (unsigned long long)((int64_t)sh.stat[2] * a.expert_bytes));
     atomicAdd(st + ST_BYTES_HOST, (unsigned long long)((int64_t)sh.stat[3] * a.expert_bytes));
+    a.n_active[1] = sh.stat[3];  // host-read experts, the first entries of the active list
   }
 }
 

@@ -55,7 +55,7 @@ struct RouteArgs {
   int32_t* sorted;          // [T*k]
   int32_t* inv;             // [T*k]
   int32_t* active;          // [E] experts with counts > 0: host-read ones first, then ascending id
-  int32_t* n_active;        // [1]
+  int32_t* n_active;        // [2]: active experts, of which host-read (the first entries of `active`)
   const int32_t* is_host;   // [E] 1 = expert read from host memory
   int64_t* counts_acc;      // [E] per-layer assignment counts since the last cache update
   int64_t* stats;           // [ST_COUNT]
@@ -68,6 +68,7 @@ struct RouteArgs {
   const uint8_t** aptr;     // [T*k] blob of each assignment's expert (decode), or null
   int32_t* hist;            // [ceil(T/16)][E] per-block counts, then bases (multi-block grouping)
   int32_t* act_pos;         // [E] active-list position of each expert (multi-block grouping)
+  int skip_host;            // GEMV descriptors with zero rows for: 0 none, 1 host-read experts, 2 all experts
 };
 
 struct GemvArgs {

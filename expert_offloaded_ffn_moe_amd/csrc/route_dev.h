@@ -13,6 +13,12 @@
 
 namespace moe {
 
+// Whether the GEMVs skip an active expert's rows (its FFN computed by the host
+// cores): skip_host 1 = the experts read from host memory, 2 = every expert.
+__device__ __forceinline__ bool skipped(const RouteArgs& a, bool host) {
+  return a.skip_host == 2 || (a.skip_host == 1 && host);
+}
+
 // ----------------------------------------------------------------------------- top-k
 
 // One wave chooses the k experts of one token, in k rounds. Lane l holds the

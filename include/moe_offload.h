@@ -130,7 +130,18 @@ typedef struct {
   int64_t bytes_copied;   /* host -> HBM bytes copied by cache updates */
   int64_t promotions;     /* experts moved into HBM slots by cache updates */
   int64_t evictions;      /* experts sent back to their host copy by cache updates */
+  int64_t host_computed;  /* unique experts whose FFN the host cores computed, per forward, summed
+                             (moe_plan_set_host_compute); their bytes are read from host memory by
+                             the CPU, not over the host link, though bytes_host still counts them
+                             when they are offloaded */
 } moe_stats;
+
+/* Where the experts of a layer are computed (moe_plan_set_host_compute). */
+typedef enum {
+  MOE_HOST_COMPUTE_NONE = 0,    /* the GPU computes every expert; offloaded ones read in place over the host link */
+  MOE_HOST_COMPUTE_MISSES = 1,  /* the host cores compute the experts read from host memory, the GPU the rest */
+  MOE_HOST_COMPUTE_LAYER = 2    /* the host cores compute every expert of the layer; the GPU routes and combines */
+} moe_host_compute;
 
 typedef struct {
   double decay;           /* score_e <- decay * score_e + count_e; default 0.9 */
@@ -276,6 +287,23 @@ moe_status moe_layer_forward_noalloc(moe_plan* plan, int32_t layer, int32_t T, c
  * Errors: MOE_E_INVALID, MOE_E_STATE (hbm_slots == 0), MOE_E_HIP. */
 moe_status moe_cache_update(moe_plan* plan, int32_t layer, const moe_cache_policy* policy,
                             moe_stream stream);
+
+/* Where a layer's experts are computed (one layer, or all for layer = -1), for plans
+ * with 4-bit codes on a host with AVX-512. [24K] section 二 computes the experts that
+ * are not in VRAM on the CPU; [125B] sections "先说结论" and "排除法" keep whole
+ * layers' experts on the CPU (ncmoe), where the serialisation between GPU and CPU
+ * was the measured cost. With a host mode, a forward on the layer enqueues the routing
+ * and copies the routing results and x to pinned host memory; the GPU's GEMVs skip the
+ * experts the host computes; the call then waits for the routing (the GPU meanwhile
+ * computes its experts), computes those experts on `threads` host threads (<= 0: the
+ * cores this process may use) from the host pool, copies their rows into the
+ * forward's workspace and enqueues the gate-weighted combine, which merges all rows in
+ * slot order. So the call returns after the host part is done. Host-computed rows are
+ * fp32 sums in another order than the GPU's: results match the oracle's tolerance,
+ * not the GPU path bit for bit. Batches of a host-mode layer run on the GEMV path.
+ * Errors: MOE_E_INVALID (layer, mode), MOE_E_UNSUPPORTED (codes other than 4-bit, no
+ * AVX-512), MOE_E_HOST_NOMEM (pinned staging), MOE_E_HIP. */
+moe_status moe_plan_set_host_compute(moe_plan* plan, int32_t layer, int32_t mode, int32_t threads);
 
 /* Counters of one layer, or summed over layers for layer = -1: hits and misses
  * per assignment and expert bytes per link, the quantities [763B] section

@@ -9,6 +9,9 @@
 //                                        answers: score, slot_of, promoted pairs, evicted
 //   setres E S decay                  -> then lines: counts, score, slot_of, want
 //   check H I E k G L act T S gmin stage bits -> "OK" or the reason
+//   ffn H I G M threads hbf16 blob_path x_path o_path -> the host expert FFN (host_ffn.cpp) of
+//                                     the canonical 4-bit blob on M fp32 token rows (h rounded to
+//                                     bf16 when hbf16 is 1), o rows written
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -18,6 +21,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "host_ffn.h"
 #include "host_logic.h"
 
 using namespace moe;
@@ -114,6 +118,27 @@ int main() {
           c.max_tokens >> c.hbm_slots >> c.gemm_min_tokens >> c.prefill_stage_slots >> c.weight_bits;
       const std::string why = check_config(c);
       std::printf("%s\n", why.empty() ? "OK" : why.c_str());
+    } else if (cmd == "ffn") {
+      int64_t H, I, G;
+      int M, threads, hbf16;
+      std::string bp, xp, op;
+      in >> H >> I >> G >> M >> threads >> hbf16 >> bp >> xp >> op;
+      const Layout L = make_layout(H, I, G, 4);
+      std::vector<uint8_t> canon((size_t)L.canonical_bytes), blob((size_t)L.bytes);
+      std::vector<float> x((size_t)M * H), h((size_t)M * I), o((size_t)M * H);
+      FILE* f = std::fopen(bp.c_str(), "rb");
+      if (!f || std::fread(canon.data(), 1, canon.size(), f) != canon.size()) return 4;
+      std::fclose(f);
+      f = std::fopen(xp.c_str(), "rb");
+      if (!f || std::fread(x.data(), sizeof(float), x.size(), f) != x.size()) return 5;
+      std::fclose(f);
+      repack_expert(L, canon.data(), blob.data());
+      HostPool pool(threads);
+      host_expert_ffn(L, blob.data(), x.data(), M, h.data(), o.data(), hbf16 != 0, pool);
+      f = std::fopen(op.c_str(), "wb");
+      if (!f || std::fwrite(o.data(), sizeof(float), o.size(), f) != o.size()) return 6;
+      std::fclose(f);
+      std::printf("done\n");
     } else if (cmd.empty()) {
       continue;
     } else {

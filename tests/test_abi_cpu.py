@@ -77,7 +77,7 @@ def test_binding_structs_match_header(cname, pyname):
     same size (ctypes lays fields out by the platform C ABI)."""
     fields = [n for _, n in _header_struct_fields(cname)]
     assert [n for n, _ in getattr(moe, pyname)._fields_] == fields, cname
-    sizes = {"moe_layer_weights": 24, "moe_routing": 56, "moe_stats": 72, "moe_cache_policy": 24,
+    sizes = {"moe_layer_weights": 24, "moe_routing": 56, "moe_stats": 80, "moe_cache_policy": 24,
              "moe_plan_info": 48, "moe_link_ceilings": 24, "moe_kernel_times": 128}
     assert ctypes.sizeof(getattr(moe, pyname)) == sizes[cname]
 

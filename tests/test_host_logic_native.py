@@ -47,8 +47,9 @@ def drv(tmp_path_factory):
         pytest.fail("g++ is required")
     exe = str(tmp_path_factory.mktemp("hl") / "host_logic_check")
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
-           "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "host_logic.cpp"), os.path.join(ROOT, "tests", "native", "host_logic_check.cpp"),
+           "-fno-sanitize-recover=all", "-mavx512f", "-mavx512bw", "-mavx512vl", "-mf16c", "-mfma", "-pthread",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "host_logic.cpp"),
+           os.path.join(CSRC, "host_ffn.cpp"), os.path.join(ROOT, "tests", "native", "host_logic_check.cpp"),
            "-o", exe]
     subprocess.check_call(cmd)
     d = Driver(exe)
@@ -249,3 +250,35 @@ def test_check_config_matches_stated_rules(drv):
     for c in cases:
         got = drv.ask(["check " + _ints(c)], 1)[0]
         assert (got == "OK") == _valid(*c), (c, got)
+
+
+def _avx512():
+    flags = open("/proc/cpuinfo").read()
+    return all(f in flags for f in ("avx512f", "avx512bw", "avx512vl", "f16c"))
+
+
+@pytest.mark.parametrize("H,I,G,M,threads,act", [(256, 128, 32, 1, 1, "bf16"), (512, 256, 128, 3, 4, "bf16"),
+                                                 (1024, 768, 256, 9, 3, "bf16"), (2048, 768, 128, 2, 8, "bf16"),
+                                                 (256, 128, 32, 5, 2, "f32"), (1024, 256, 64, 3, 4, "f32")])
+def test_host_expert_ffn_against_oracle(drv, tmp_path, H, I, G, M, threads, act):
+    """The host expert FFN (AVX-512, several worker threads, 8-token passes) on the library's
+    internal layout against the oracle's FFN of the canonical blob: codes covering every
+    value, bf16 activations, h rounded to bf16 on both sides; rel-L2 <= 1e-3, max-abs <= 2e-2."""
+    if not _avx512():
+        pytest.skip("host FFN needs AVX-512")
+    import layer_cases as LC
+    blob = LC.random_code_blobs(1, H, I, G, seed=H + M)[0]
+    rng = np.random.default_rng(M)
+    x = rng.standard_normal((M, H)).astype(np.float32)
+    if act == "bf16":
+        x = O.round_bf16(x.astype(np.float64)).astype(np.float32)
+    bp, xp, op = tmp_path / "b.bin", tmp_path / "x.bin", tmp_path / "o.bin"
+    blob.tofile(bp)
+    x.tofile(xp)
+    assert drv.ask(["ffn %d %d %d %d %d %d %s %s %s" % (H, I, G, M, threads, act == "bf16", bp, xp, op)],
+                   1) == ["done"]
+    o = np.fromfile(op, dtype=np.float32).reshape(M, H).astype(np.float64)
+    Wg, Wu, Wd = O.expert_weights(blob, H, I, G)
+    ref = np.stack([O.expert_ffn(x[m].astype(np.float64), Wg, Wu, Wd, act) for m in range(M)])
+    r, m = LC.rel_l2(o, ref), LC.max_abs(o, ref)
+    assert r <= (1e-3 if act == "bf16" else 1e-5) and m <= 2e-2, (r, m)
