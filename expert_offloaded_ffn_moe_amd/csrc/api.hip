@@ -158,11 +158,13 @@ struct moe_plan {
   // host computation of experts: worker pool, pinned staging of the routing results,
   // the activations and the host-computed o rows, and host scratch for packed rows
   HostPool* host_pool = nullptr;
-  int32_t* hs_route = nullptr;  // n_active[2] | active[E] | offsets[E+1] | sorted[Tmax*k]
-  void* hs_x = nullptr;         // [Tmax][H] act dtype
+  int32_t* hs_route = nullptr;  // n_active[2] | active[E] | offsets[E+1] | sorted[Tmax*k]; mapped, coherent
+  void* hs_x = nullptr;         // [Tmax][H] act dtype; mapped, coherent
+  int32_t* hs_route_dev = nullptr;  // device addresses of the two
+  void* hs_x_dev = nullptr;
   float* hs_o = nullptr;        // [Tmax*k][H]
   std::vector<float> hx, hh;    // packed x rows [Tmax*k][H], h rows [Tmax*k][I]
-  hipEvent_t ev_route = nullptr;
+  hipEvent_t ev_route = nullptr;  // the routing results and x are in the host staging
 };
 
 namespace {
@@ -1047,14 +1049,14 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     launch_topk_group(rt, w.route_cnt + 16, kt.tm, s);
   }
 
-  if (hmode != MOE_HOST_COMPUTE_NONE) {  // the routing results and x for the host part
-    LAUNCH_USES("copies to the host", WB_NACTIVE | WB_ACTIVE | WB_OFFSETS | WB_SORTED, 0);
-    int32_t* hr = p->hs_route;
-    HIP_TRY(hipMemcpyAsync(hr, w.n_active, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipMemcpyAsync(hr + 2, w.active, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipMemcpyAsync(hr + 2 + E, w.offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipMemcpyAsync(hr + 3 + 2 * E, w.sorted, sizeof(int32_t) * A, hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipMemcpyAsync(p->hs_x, x, p->act_size * T * H, hipMemcpyDeviceToHost, s));
+  if (hmode != MOE_HOST_COMPUTE_NONE) {
+    // the routing results and x for the host part, written by one small kernel into
+    // mapped, coherent pinned memory right after the routing (the GEMVs follow it);
+    // the host part waits for the event, and the call returns only after it has read
+    // the staging, so the next forward cannot overwrite it while it is read
+    LAUNCH_USES("k_export_route", WB_NACTIVE | WB_ACTIVE | WB_OFFSETS | WB_SORTED, 0);
+    launch_export_route(w.n_active, w.active, w.offsets, w.sorted, x, p->act_size * T * H, p->hs_route_dev,
+                        p->hs_x_dev, E, A, s);
     HIP_TRY(hipEventRecord(p->ev_route, s));
   }
 
@@ -1288,17 +1290,26 @@ moe_status moe_plan_set_host_compute(moe_plan* p, int32_t layer, int32_t mode, i
       const moe_config& c = p->cfg;
       const size_t Tm = (size_t)c.max_tokens, A = Tm * c.top_k, E = c.num_experts;
       void* v = nullptr;
-      moe_status st = host_alloc(p, &v, sizeof(int32_t) * (3 + 2 * E + A), 0);
+      const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
+      moe_status st = host_alloc(p, &v, sizeof(int32_t) * (3 + 2 * E + A), mapped);
       if (st != MOE_OK) return st;
       p->hs_route = static_cast<int32_t*>(v);
-      st = host_alloc(p, &p->hs_x, p->act_size * Tm * c.hidden, 0);
+      st = host_alloc(p, &p->hs_x, p->act_size * Tm * c.hidden, mapped);
       if (st != MOE_OK) return st;
+      void *d1 = nullptr, *d2 = nullptr;
+      if (hipHostGetDevicePointer(&d1, p->hs_route, 0) != hipSuccess ||
+          hipHostGetDevicePointer(&d2, p->hs_x, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_E_HIP, "hipHostGetDevicePointer of the host-part staging failed");
+      }
+      p->hs_route_dev = static_cast<int32_t*>(d1);
+      p->hs_x_dev = d2;
       st = host_alloc(p, &v, sizeof(float) * A * c.hidden, 0);
       if (st != MOE_OK) return st;
       p->hs_o = static_cast<float*>(v);
       if (!p->ev_route && hipEventCreateWithFlags(&p->ev_route, hipEventDisableTiming) != hipSuccess) {
         (void)hipGetLastError();
-        return fail(MOE_E_HIP, "creating the routing event failed");
+        return fail(MOE_E_HIP, "creating the host-part event failed");
       }
       try {
         p->hx.assign(A * c.hidden, 0.f);

@@ -41,6 +41,43 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ s
 
 int stream_read_blocks() { return 2048; }
 
+// The routing results and x of a forward into the pinned staging of its host part,
+// with plain stores through the staging's device address (one launch instead of a
+// DMA copy per buffer): dst = n_active[2] | active[E] | offsets[E+1] | sorted[A], x to
+// xdst (xwords 32-bit words).
+__global__ __launch_bounds__(256) void k_export_route(const int32_t* __restrict__ n_active,
+                                                      const int32_t* __restrict__ active,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ sorted, const uint32_t* __restrict__ x,
+                                                      int32_t* __restrict__ dst, uint32_t* __restrict__ xdst, int E, int A,
+                                                      int xwords) {
+  const int n_route = 3 + 2 * E + A;
+  const int stride = gridDim.x * blockDim.x;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_route + xwords; i += stride) {
+    if (i >= n_route) {
+      xdst[i - n_route] = x[i - n_route];
+    } else if (i < 2) {
+      dst[i] = n_active[i];
+    } else if (i < 2 + E) {
+      dst[i] = active[i - 2];
+    } else if (i < 3 + 2 * E) {
+      dst[i] = offsets[i - 2 - E];
+    } else {
+      dst[i] = sorted[i - 3 - 2 * E];
+    }
+  }
+}
+
+void launch_export_route(const int32_t* n_active, const int32_t* active, const int32_t* offsets,
+                         const int32_t* sorted, const void* x, size_t x_bytes, int32_t* dst, void* xdst, int E, int A,
+                         hipStream_t s) {
+  const int xwords = (int)(x_bytes / 4);
+  const int n = 3 + 2 * E + A + xwords;
+  const int blocks = std::min(64, (n + 255) / 256);
+  hipLaunchKernelGGL(k_export_route, dim3(blocks), dim3(256), 0, s, n_active, active, offsets, sorted,
+                     static_cast<const uint32_t*>(x), dst, static_cast<uint32_t*>(xdst), E, A, xwords);
+}
+
 void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
   hipLaunchKernelGGL(k_stream_read, dim3(stream_read_blocks()), dim3(256), 0, s, static_cast<const u32x4*>(src),
                      bytes / 16, sink);

@@ -173,6 +173,10 @@ constexpr int kGemmMinTokensDefault = 6;
 void launch_fill32(void* p, uint32_t v, size_t n_words, hipStream_t s);
 int stream_read_blocks();  // workgroups of launch_stream_read (one sink word each)
 void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);  // bytes % 16 == 0
+// routing results and x (x_bytes % 4 == 0) into host staging reached through its device address
+void launch_export_route(const int32_t* n_active, const int32_t* active, const int32_t* offsets,
+                         const int32_t* sorted, const void* x, size_t x_bytes, int32_t* dst, void* xdst, int E, int A,
+                         hipStream_t s);
 
 
 }  // namespace moe
