@@ -79,6 +79,9 @@ def parse_args():
     ap.add_argument("--cache-steps", type=int, default=256)
     ap.add_argument("--max-promotions", type=int, default=8, help="cache run: promotions per layer per update")
     ap.add_argument("--decay", type=float, default=0.9, help="cache run: score decay per update")
+    ap.add_argument("--prefetch-slots", type=int, default=8, help="cache run: prefetch slots per layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="cache run: replay each step's 48 layers as one captured HIP graph instead of enqueueing them")
     ap.add_argument("--cpu-seconds", type=float, default=3.0, help="CPU oracle time budget per configuration")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
@@ -450,11 +453,16 @@ def run_prefill(args, out):
 
 
 def run_cache(args, out):
-    """Expert-cache decode run over the stacked layers: the static coldest-on-host plan
-    (warm-up steps, then the timed steps, no updates), then the cached plan from its cold
-    start (slots hold experts 0..89) with a pipelined cache update after every step. One
-    step = one token through every layer; each (step, layer) takes its own seeded
-    activations (the bench's inputs, also checked against the oracle by the GPU tests)."""
+    """Expert-cache decode run over the stacked layers. One step = one token through
+    every layer along a residual stream: x_0 is the step's seeded token activation,
+    x_{l+1} = bf16(x_l + y_l). Plans, each on the same inputs:
+      static   - the coldest-on-host residency (warm-up steps first), no updates;
+      cache    - cold start (slots hold experts 0..S-1), pipelined update after every step;
+      prefetch - as cache, plus P prefetch slots per layer: before the forward of layer l,
+                 the experts of layer l+1 that its router picks for x_l are copied in;
+      cache_more_slots - as cache with S+P slots (the same HBM as the prefetch plan);
+    and, for comparison with runs that fed every (step, layer) its own activations,
+      cache_independent_inputs - as cache on such inputs."""
     import numpy as np
     import torch
     import expert_offloaded_ffn_moe_amd as moe
@@ -462,24 +470,60 @@ def run_cache(args, out):
     d = DIMS["cache"]
     H, I, E, k, G = d["H"], d["I"], d["E"], d["k"], d["G"]
     L, B, steps, warmup = 48, 1, args.cache_steps, args.warmup
-    S = int(round(0.7 * E))
+    S, P = int(round(0.7 * E)), args.prefetch_slots
     layers = gen_layers("cache", L)
+    x0b = synth.activations(d["seed"], 7100, (warmup + steps) * B, H, "bf16")
+    x0 = torch.from_numpy(x0b.view(np.int16).copy()).view(torch.bfloat16).cuda().view(warmup + steps, B, H)
     n_x = (warmup + steps) * L
-    xb = synth.activations(d["seed"], 7000, n_x * B, H, "bf16")
-    xs = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).cuda().view(n_x, B, H)
+    xib = synth.activations(d["seed"], 7000, n_x * B, H, "bf16")
+    xind = torch.from_numpy(xib.view(np.int16).copy()).view(torch.bfloat16).cuda().view(n_x, B, H)
+    xl = torch.empty((L + 1, B, H), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((B, H), device="cuda")
+    stream = torch.cuda.current_stream()
     modes = {}
-    for mode in ("static", "cache"):
-        cfg = moe.make_config(H, I, E, k, G, "bf16", num_layers=L, max_tokens=B, hbm_slots=S)
-        init = (np.stack([synth.coldest_host_plan(d["seed"], l, E, S / E) for l in range(L)]) if mode == "static"
+    runs = [("static", S, 0, False, True), ("cache", S, 0, True, True), ("prefetch", S, P, True, True),
+            ("cache_more_slots", S + P, 0, True, True), ("cache_independent_inputs", S, 0, True, False)]
+    for mode, slots, pf, update, chained in runs:
+        cfg = moe.make_config(H, I, E, k, G, "bf16", num_layers=L, max_tokens=B, hbm_slots=slots, prefetch_slots=pf)
+        init = (np.stack([synth.coldest_host_plan(d["seed"], l, E, slots / E) for l in range(L)]) if not update
                 else None)
         plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in layers], initial_hbm=init)
         torch.cuda.synchronize()
+
+        def layers_pass(i, st):
+            for l in range(L):
+                x = xl[l] if chained else xind[i * L + l]
+                if pf and l + 1 < L:
+                    plan.prefetch(l + 1, x=x, stream=st)
+                if chained:  # y and x_l+1 = bf16(x_l + y) from the same kernel
+                    plan.forward_residual(l, x, y, xl[l + 1], stream=st)
+                else:
+                    plan.forward(l, x, y, stream=st)
+
+        graph = None
+        if chained and args.graph:  # the 48 layers of a step as one HIP graph
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                layers_pass(0, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+
+        def one_step(i, eager=False):
+            if chained:
+                xl[0].copy_(x0[i])
+            if graph is not None and not eager:
+                graph.replay()
+            else:
+                layers_pass(i, stream)
+            if update:
+                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True,
+                                  stream=stream)
+
         first = 0
-        if mode == "static":
+        if not update:
             for i in range(warmup):
-                for l in range(L):
-                    plan.forward(l, xs[i * L + l], y)
+                one_step(i)
             torch.cuda.synchronize()
             plan.reset_stats()
             first = warmup
@@ -487,26 +531,22 @@ def run_cache(args, out):
         t_all = time.perf_counter()
         for i in range(first, first + steps):
             t0 = time.perf_counter()
-            for l in range(L):
-                plan.forward(l, xs[i * L + l], y)
-            if mode == "cache":
-                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
-            else:
+            one_step(i)
+            if not update:
                 torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_all
         st = plan.stats(-1)
-        log("cache run, %s plan: %d steps x %d layers in %.3fs, hit rate %.4f" % (
-            mode, steps, L, elapsed, st["hits"] / max(st["hits"] + st["misses"], 1)))
-        plan.profile(True)  # per-kernel times over a further 16 steps in the same mode
+        log("cache run, %s: %d steps x %d layers in %.3fs, hit rate %.4f, prefetched %d" % (
+            mode, steps, L, elapsed, st["hits"] / max(st["hits"] + st["misses"], 1), st["prefetched"]))
+        plan.profile(True)  # per-kernel times over a further 16 steps in the same mode, enqueued eagerly
         for i in range(first, first + min(16, steps)):
-            for l in range(L):
-                plan.forward(l, xs[i * L + l], y)
-            if mode == "cache":
-                plan.cache_update(-1, decay=args.decay, max_promotions=args.max_promotions, overlap=True)
+            one_step(i, eager=True)
         kt = plan.kernel_times()
         plan.profile(False)
+        launch = "one HIP graph per step" if graph is not None else "eager"
+        del graph
         plan.destroy()
         t = np.sort(np.array(times))
         fwd = max(st["forwards"], 1)
@@ -514,23 +554,26 @@ def run_cache(args, out):
         modes[mode] = dict(
             tokens_per_s=round(B * steps / elapsed, 2), step_ms_median=round(float(np.median(t)) * 1e3, 4),
             step_ms_p95=round(float(np.percentile(t, 95)) * 1e3, 4),
-            tokens_per_s_median=round(B / float(np.median(t)), 2),
-            tokens_per_s_p5=round(B / float(np.percentile(t, 95)), 2),
+            hbm_slots=slots, prefetch_slots=pf, inputs="residual stream" if chained else "independent per layer",
+            launch=launch,
             hit_rate=round(st["hits"] / max(st["hits"] + st["misses"], 1), 5), hits=st["hits"], misses=st["misses"],
+            prefetched=st["prefetched"],
             bytes_hbm_per_layer_step=int(st["bytes_hbm"] / fwd), bytes_host_per_layer_step=int(st["bytes_host"] / fwd),
             bytes_copied=st["bytes_copied"], promotions=st["promotions"], evictions=st["evictions"],
             roofline=roofline(pk, st["bytes_hbm"] / fwd, st["bytes_host"] / fwd, B * k, H, I, "cache_48_layers"))
     c = modes["cache"]
     r = {"value": c["tokens_per_s"], "unit": "tokens/s", "steps": steps, "warmup": 0,
          "ms_per_step": round(1e3 * B / c["tokens_per_s"], 5),
-         "workload": "%s: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d int4 G%d, %d HBM slots per layer "
-                     "(rest host-mapped), batch %d, %d steps, cold start, pipelined cache update after every step "
-                     "(max %d promotions per layer, score decay %g)" % (
+         "workload": "%s: %d stacked Qwen3-30B-A3B-shaped layers H%d I%d E%d k%d int4 G%d on a residual stream "
+                     "(x_l+1 = bf16(x_l + y_l), fused into each layer's combine), %d HBM slots per layer (rest "
+                     "host-mapped), batch %d, %d steps, cold start, pipelined cache update after every step (max %d "
+                     "promotions per layer, score decay %g)" % (
                          NAMES["cache"], L, H, I, E, k, G, S, B, steps, args.max_promotions, args.decay),
-         "roofline": c.pop("roofline"), "cache_run": c, "static_plan": modes["static"]}
+         "roofline": c.pop("roofline"), "cache_run": c,
+         "other_plans": {m: v for m, v in modes.items() if m != "cache"}}
     if not args.no_cpu:
         # 2 steps x 48 layers of the same inputs, extrapolated to full steps
-        cb = cpu_baseline("cache", layers[:2], [xb[(i * L) * B:(i * L + 1) * B] for i in range(4)], args.cpu_seconds,
+        cb = cpu_baseline("cache", layers[:2], [xib[(i * L) * B:(i * L + 1) * B] for i in range(4)], args.cpu_seconds,
                           per_step_forwards=L, label="extrapolated from forwards of single layers")
         r["cpu_baseline"] = cb
     out["cache_48_layers"] = r
@@ -615,6 +658,9 @@ def main():
         "layer": head.get("layer"),
         "configs": {k: v for k, v in configs.items() if k != head_key},
     }
+    for key, v in head.items():  # the head workload's own extra fields (comparison runs and the like)
+        if key not in line and key not in ("workload", "unit", "value", "steps", "warmup", "ms_per_step"):
+            line[key] = v
     line.update(extra)
     print(json.dumps(line), flush=True)
 

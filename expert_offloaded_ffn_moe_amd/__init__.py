@@ -24,7 +24,7 @@ class Config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32), ("num_layers", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("hbm_slots", ctypes.c_int32),
                 ("gemm_min_tokens", ctypes.c_int32), ("prefill_stage_slots", ctypes.c_int32),
-                ("weight_bits", ctypes.c_int32)]
+                ("weight_bits", ctypes.c_int32), ("prefetch_slots", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -39,7 +39,8 @@ class Routing(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("forwards", "tokens", "hits", "misses", "bytes_hbm", "bytes_host",
-                                              "bytes_copied", "promotions", "evictions", "host_computed")]
+                                              "bytes_copied", "promotions", "evictions", "host_computed",
+                                              "prefetched")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -106,9 +107,12 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_measure_link_ceilings.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i32, vp, ctypes.POINTER(LinkCeilings)]
     lib.moe_debug_fail_alloc.argtypes = [i32, i32]
     lib.moe_plan_set_host_compute.argtypes = [vp, i32, i32, i32]
+    lib.moe_prefetch.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp]
+    lib.moe_plan_prefetch_slots.argtypes = [vp, i32, vp]
     lib.moe_debug_live_allocs.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
     lib.moe_layer_forward_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(Routing), vp]
+    lib.moe_layer_forward_residual.argtypes = [vp, i32, i32, vp, vp, vp, vp, ctypes.POINTER(Routing), vp]
     lib.moe_cache_update.argtypes = [vp, i32, ctypes.POINTER(CachePolicy), vp]
     lib.moe_plan_stats.argtypes = [vp, i32, ctypes.POINTER(Stats)]
     lib.moe_plan_reset_stats.argtypes = [vp]
@@ -121,10 +125,11 @@ def load_library(path: str = LIB_PATH, with_torch: bool = True):
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_last_error.restype = ctypes.c_char_p
     for fn in ("moe_expert_bytes", "moe_plan_create", "moe_plan_load_layer", "moe_layer_forward",
-               "moe_layer_forward_noalloc",
+               "moe_layer_forward_noalloc", "moe_layer_forward_residual",
                "moe_cache_update", "moe_plan_stats", "moe_plan_reset_stats", "moe_plan_residency",
                "moe_plan_profile", "moe_plan_kernel_times", "moe_plan_get_info", "moe_measure_link_ceilings",
-               "moe_debug_fail_alloc", "moe_debug_live_allocs", "moe_plan_set_host_compute"):
+               "moe_debug_fail_alloc", "moe_debug_live_allocs", "moe_plan_set_host_compute",
+               "moe_prefetch", "moe_plan_prefetch_slots"):
         getattr(lib, fn).restype = st
     _lib = lib
     return lib
@@ -178,9 +183,10 @@ def debug_live_allocs():
 
 
 def make_config(H, I, E, k, G, act="bf16", num_layers=1, max_tokens=16, hbm_slots=None, gemm_min_tokens=0,
-                prefill_stage_slots=0, weight_bits=4):
+                prefill_stage_slots=0, weight_bits=4, prefetch_slots=0):
     return Config(H, I, E, k, G, num_layers, ACT_BF16 if act == "bf16" else ACT_F32, max_tokens,
-                  E if hbm_slots is None else hbm_slots, gemm_min_tokens, prefill_stage_slots, weight_bits)
+                  E if hbm_slots is None else hbm_slots, gemm_min_tokens, prefill_stage_slots, weight_bits,
+                  prefetch_slots)
 
 
 def expert_bytes(cfg: Config) -> int:
@@ -244,6 +250,18 @@ class Plan:
                "moe_layer_forward")
         return y
 
+    def forward_residual(self, layer, x, y, x_out, logits_in=None, route=None, stream=None):
+        """forward() that also writes x_out = x + y in x's dtype (the residual stream's
+        next value), from the kernel that writes y."""
+        T = int(x.shape[0])
+        r = None
+        if route is not None:
+            r = Routing(*[_ptr(route.get(n)) for n, _ in Routing._fields_])
+        _check(self.lib.moe_layer_forward_residual(self.handle, layer, T, _ptr(x), _ptr(logits_in), _ptr(y),
+                                                   _ptr(x_out), ctypes.byref(r) if r is not None else None,
+                                                   _stream(stream)), "moe_layer_forward_residual")
+        return y
+
     def forward_noalloc(self, layer, x, y, logits_in=None, route=None, stream=None):
         """forward() through moe_layer_forward_noalloc: the workspace comes from the
         library's static per-device array, and the call allocates nothing."""
@@ -265,6 +283,22 @@ class Plan:
         pol = CachePolicy(decay, max_promotions, 1 if overlap else 0, _ptr(want))
         _check(self.lib.moe_cache_update(self.handle, layer, ctypes.byref(pol), _stream(stream)),
                "moe_cache_update")
+
+    def prefetch(self, layer, x=None, logits_in=None, candidates=0, predicted_out=None, stream=None):
+        """Predict the layer's experts from x (cuda [T, H], the layer's router applied to
+        it) or logits_in (cuda float32 [T, E]) and copy the host-read ones among them
+        into the layer's prefetch slots, on the plan's prefetch stream, after the work
+        enqueued on `stream` so far. predicted_out: optional cuda int32 [prefetch_slots]."""
+        src = logits_in if logits_in is not None else x
+        T = int(src.shape[0])
+        _check(self.lib.moe_prefetch(self.handle, layer, T, _ptr(x), _ptr(logits_in), candidates,
+                                     _ptr(predicted_out), _stream(stream)), "moe_prefetch")
+
+    def prefetch_slots(self, layer) -> np.ndarray:
+        """Expert held by each prefetch slot of the layer (-1 none); waits for its prefetch."""
+        out = np.empty(self.cfg.prefetch_slots, dtype=np.int32)
+        _check(self.lib.moe_plan_prefetch_slots(self.handle, layer, out.ctypes.data), "moe_plan_prefetch_slots")
+        return out
 
     def set_host_compute(self, layer=-1, mode=HOST_COMPUTE_MISSES, threads=0):
         """Where the layer's experts are computed: HOST_COMPUTE_NONE (the GPU, offloaded ones

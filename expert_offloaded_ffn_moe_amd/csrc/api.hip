@@ -92,6 +92,13 @@ struct Layer {
   int64_t bytes_copied = 0, promotions = 0, evictions = 0;
   int host_mode = MOE_HOST_COMPUTE_NONE;  // moe_plan_set_host_compute
   int64_t host_computed = 0;             // unique experts computed by the host cores, summed over forwards
+  // predictive prefetch (moe_prefetch): slots, their occupants and the copy list on
+  // the device; the prefetch's completion as an event
+  uint8_t* pf_slots = nullptr;   // [prefetch_slots][L.bytes]
+  int32_t* d_pf_occ = nullptr;   // [prefetch_slots] expert per slot, -1 none
+  int32_t* d_pf_list = nullptr;  // [prefetch_slots + 1] slots to fill, then their count
+  hipEvent_t ev_prefetch = nullptr;
+  bool pf_pending = false;
 };
 
 struct Workspace {
@@ -165,6 +172,12 @@ struct moe_plan {
   float* hs_o = nullptr;        // [Tmax*k][H]
   std::vector<float> hx, hh;    // packed x rows [Tmax*k][H], h rows [Tmax*k][I]
   hipEvent_t ev_route = nullptr;  // the routing results and x are in the host staging
+  // predictive prefetch: its stream, router logits and arrival counter (prefetches of
+  // all layers run in order on the one stream), and the caller's point it starts after
+  hipStream_t pf_stream = nullptr;
+  float* pf_logits = nullptr;       // [Tmax][E]
+  unsigned* pf_counter = nullptr;   // [1]
+  hipEvent_t ev_caller = nullptr;
 };
 
 namespace {
@@ -265,6 +278,10 @@ void free_plan(moe_plan* p) {
     if (e) (void)hipEventDestroy(e);
   if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
   if (p->ev_route) (void)hipEventDestroy(p->ev_route);
+  if (p->pf_stream) (void)hipStreamDestroy(p->pf_stream);
+  if (p->ev_caller) (void)hipEventDestroy(p->ev_caller);
+  for (Layer& ly : p->layers)
+    if (ly.ev_prefetch) (void)hipEventDestroy(ly.ev_prefetch);
   delete p->host_pool;
   for (void* q : p->dev_allocs) (void)hipFree(q);
   for (void* q : p->host_allocs) (void)hipHostFree(q);
@@ -325,6 +342,17 @@ moe_status push_tables(moe_plan* p, Layer& ly, hipStream_t s) {
   return MOE_OK;
 }
 
+// Work on `s` that reads or rewrites a layer's table, or its prefetch slots, waits
+// on the device for the layer's pending prefetch.
+moe_status wait_prefetch(moe_plan* p, Layer& ly, hipStream_t s) {
+  if (ly.pf_pending) {
+    HIP_TRY(hipStreamWaitEvent(s, ly.ev_prefetch, 0));
+    ly.pf_pending = false;
+  }
+  (void)p;
+  return MOE_OK;
+}
+
 // Wait for the promotion copies of a pipelined update and drop what it staged
 // for layers [l0, l1): afterwards slot_of is exactly what push_tables uploads.
 moe_status settle_pipelined(moe_plan* p, int l0, int l1) {
@@ -345,6 +373,10 @@ moe_status cache_update_pipelined(moe_plan* p, int l0, int l1, double decay, int
   const int cur = (int)(p->update_seq & 1u), prev = cur ^ 1;
   ++p->update_seq;
   const size_t off = (size_t)l0 * E, n = (size_t)(l1 - l0) * E;
+  for (int l = l0; l < l1; ++l) {
+    moe_status st = wait_prefetch(p, p->layers[l], s);
+    if (st != MOE_OK) return st;
+  }
   // (a) the previous update's promotions: forwards after this table upload read
   // them from HBM, so the upload waits for their copies (a device-side wait)
   if (p->copy_pending) {
@@ -520,6 +552,8 @@ moe_status load_layer_impl(moe_plan* p, int layer, const moe_layer_weights* w, c
     if (initial_hbm ? (initial_hbm[e] != 0) : (e < S)) slot_of[e] = used++;
   HIP_TRY(hipSetDevice(p->device));
   HIP_TRY(hipStreamSynchronize(s));  // no queued work may still read this layer
+  if (p->pf_stream) HIP_TRY(hipStreamSynchronize(p->pf_stream));  // nor a prefetch copy from it
+  ly.pf_pending = false;
   {
     moe_status st = settle_pipelined(p, layer, layer + 1);  // nor copy into it
     if (st != MOE_OK) return st;
@@ -555,6 +589,7 @@ moe_status load_layer_impl(moe_plan* p, int layer, const moe_layer_weights* w, c
     HIP_TRY(hipMemsetAsync(ly.d_router_b, 0, sizeof(float) * E, s));
   HIP_TRY(hipMemsetAsync(ly.d_counts_acc, 0, sizeof(int64_t) * E, s));
   HIP_TRY(hipMemsetAsync(ly.d_stats, 0, sizeof(int64_t) * ST_COUNT, s));
+  if (ly.d_pf_occ) launch_fill32(ly.d_pf_occ, 0xFFFFFFFFu, (size_t)p->cfg.prefetch_slots, s);
   HIP_TRY(hipStreamSynchronize(s));
   ly.bytes_copied = ly.promotions = ly.evictions = 0;
   ly.loaded = true;
@@ -722,6 +757,28 @@ moe_status moe_plan_create(const moe_config* cfg, const moe_layer_weights* layer
     ly.h_counts_stage = static_cast<int64_t*>(v);
     ly.slot_of.assign(E, -1);
     ly.score.assign(E, 0.0);
+    if (cfg->prefetch_slots > 0) {
+      TRY(dev_alloc(p, &v, (size_t)cfg->prefetch_slots * p->L.bytes));
+      ly.pf_slots = static_cast<uint8_t*>(v);
+      p->hbm_slot_bytes += (int64_t)cfg->prefetch_slots * p->L.bytes;
+      TRY(alloc_as(p, &ly.d_pf_occ, (size_t)cfg->prefetch_slots));
+      TRY(alloc_as(p, &ly.d_pf_list, (size_t)cfg->prefetch_slots + 1));
+      launch_fill32(ly.d_pf_occ, 0xFFFFFFFFu, (size_t)cfg->prefetch_slots, nullptr);
+      if (hipEventCreateWithFlags(&ly.ev_prefetch, hipEventDisableTiming) != hipSuccess) {
+        free_plan(p);
+        return fail(MOE_E_HIP, "creating prefetch events failed");
+      }
+    }
+  }
+  if (cfg->prefetch_slots > 0) {
+    TRY(alloc_as(p, &p->pf_logits, Tm * E));
+    TRY(alloc_as(p, &p->pf_counter, 64));
+    if (hipMemset(p->pf_counter, 0, 64 * sizeof(unsigned)) != hipSuccess ||
+        hipStreamCreateWithFlags(&p->pf_stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&p->ev_caller, hipEventDisableTiming) != hipSuccess) {
+      free_plan(p);
+      return fail(MOE_E_HIP, "setting up the prefetch stream failed");
+    }
   }
   Workspace& w = p->ws;
   const int64_t dev_before_ws = p->dev_bytes;
@@ -856,7 +913,7 @@ moe_status host_part(moe_plan* p, Layer& ly, int T, Workspace& w, hipStream_t s)
 // The forward of moe_layer_forward on the workspace `w` (the plan's, or one carved
 // from the static scratch array for moe_layer_forward_noalloc).
 moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in, float* y,
-                        const moe_routing* ro, hipStream_t s, Workspace& w, bool own_ws) {
+                        void* x_out, const moe_routing* ro, hipStream_t s, Workspace& w, bool own_ws) {
   Layer& ly = p->layers[layer];
   const moe_config& c = p->cfg;
   const int E = c.num_experts, H = c.hidden, I = c.inter, k = c.top_k, G = c.group_size;
@@ -1016,6 +1073,9 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     ca.T = T;
     ca.H = H;
     ca.k = k;
+    ca.xres = x_out ? x : nullptr;
+    ca.xout = x_out;
+    ca.act_bf16 = bf16;
     {
       LAUNCH_USES("k_combine", WB_O | WB_WTS | WB_INV, 0);
       KernelTimer kt(p, MOE_K_COMBINE);
@@ -1116,6 +1176,8 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
       dc.k = k;
       dc.T = T;
       dc.splits = fuse_down ? down_splits : narrow_splits;
+      dc.xres = x_out ? static_cast<const uint16_t*>(x) : nullptr;
+      dc.xout = static_cast<uint16_t*>(x_out);
       LAUNCH_USES(fuse_down ? "k_down_comb" : "k_down_comb16", WB_APTR | WB_INV | WB_WTS | WB_H | WB_HPART, 0);
       KernelTimer kt(p, MOE_K_DOWN);
       if (fuse_down)
@@ -1140,6 +1202,9 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
       ca.T = T;
       ca.H = H;
       ca.k = k;
+    ca.xres = x_out ? x : nullptr;
+    ca.xout = x_out;
+    ca.act_bf16 = bf16;
       LAUNCH_USES("k_combine", WB_O | WB_WTS | WB_INV, 0);
       KernelTimer kt(p, MOE_K_COMBINE);
       launch_combine(ca, kt.tm, s);
@@ -1160,6 +1225,9 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   }
   return MOE_OK;
 }
+
+moe_status cache_update_sync(moe_plan* p, int l0, int l1, double decay, int maxp, const int32_t* want,
+                             hipStream_t s);
 
 // Arguments shared by both forward entry points.
 moe_status check_forward_args(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
@@ -1183,7 +1251,27 @@ moe_status moe_layer_forward(moe_plan* p, int32_t layer, int32_t T, const void* 
                              const moe_routing* ro, moe_stream stream) {
   moe_status st = check_forward_args(p, layer, T, x, logits_in, y);
   if (st != MOE_OK || T == 0) return st;
-  return forward_impl(p, layer, T, x, logits_in, y, ro, static_cast<hipStream_t>(stream), p->ws, true);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = wait_prefetch(p, p->layers[layer], s);
+  if (st == MOE_OK) st = forward_impl(p, layer, T, x, logits_in, y, nullptr, ro, s, p->ws, true);
+  return st;
+}
+
+moe_status moe_layer_forward_residual(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
+                                      float* y, void* x_out, const moe_routing* ro, moe_stream stream) {
+  moe_status st = check_forward_args(p, layer, T, x, logits_in, y);
+  if (st != MOE_OK || T == 0) return st;
+  if (!x_out || !aligned16(x_out)) return fail(MOE_E_INVALID, "x_out is required and must be 16-byte aligned");
+  const size_t xb = (size_t)T * p->cfg.hidden * p->act_size;
+  const char *xa = static_cast<const char*>(x), *oa = static_cast<const char*>(x_out);
+  if (oa < xa + xb && xa < oa + xb) return fail(MOE_E_INVALID, "x_out overlaps x");
+  const char* ya = reinterpret_cast<const char*>(y);
+  const size_t yb = (size_t)T * p->cfg.hidden * sizeof(float);
+  if (oa < ya + yb && ya < oa + xb) return fail(MOE_E_INVALID, "x_out overlaps y");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = wait_prefetch(p, p->layers[layer], s);
+  if (st == MOE_OK) st = forward_impl(p, layer, T, x, logits_in, y, x_out, ro, s, p->ws, true);
+  return st;
 }
 
 moe_status moe_layer_forward_noalloc(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
@@ -1199,7 +1287,10 @@ moe_status moe_layer_forward_noalloc(moe_plan* p, int32_t layer, int32_t T, cons
   uint8_t* base = scratch_on(p->device, &why);  // set up by moe_plan_create on this device
   if (!base) return fail(MOE_E_HIP, why);
   carve_workspace(p, T, base, &w);
-  return forward_impl(p, layer, T, x, logits_in, y, ro, static_cast<hipStream_t>(stream), w, false);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = wait_prefetch(p, p->layers[layer], s);
+  if (st == MOE_OK) st = forward_impl(p, layer, T, x, logits_in, y, nullptr, ro, s, w, false);
+  return st;
 }
 
 moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* pol, moe_stream stream) {
@@ -1222,7 +1313,84 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
     }
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(p->device));
-  if (pol && pol->overlap && !want) return cache_update_pipelined(p, l0, l1, decay, maxp, s);
+  return pol && pol->overlap && !want ? cache_update_pipelined(p, l0, l1, decay, maxp, s)
+                                      : cache_update_sync(p, l0, l1, decay, maxp, want, s);
+}
+
+moe_status moe_prefetch(moe_plan* p, int32_t layer, int32_t T, const void* x, const float* logits_in,
+                        int32_t candidates, int32_t* predicted_out, moe_stream stream) {
+  if (!p) return fail(MOE_E_INVALID, "plan is null");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (p->cfg.prefetch_slots == 0) return fail(MOE_E_STATE, "plan has no prefetch slots");
+  const int E = p->cfg.num_experts;
+  if (T < 1 || T > p->cfg.max_tokens) return fail(MOE_E_INVALID, "T out of range 1..max_tokens");
+  const int kp = candidates == 0 ? p->cfg.top_k : candidates;
+  if (kp < 1 || kp > 64 || kp > E) return fail(MOE_E_INVALID, "candidates must be in 0..min(64, num_experts)");
+  if ((int64_t)T * kp > kPrefetchMaxCand) return fail(MOE_E_INVALID, "T * candidates must be <= 2048");
+  if (!logits_in && !x) return fail(MOE_E_INVALID, "x or logits_in is required");
+  if ((x && !logits_in && !aligned16(x)) || (logits_in && !aligned16(logits_in)))
+    return fail(MOE_E_INVALID, "x and logits_in must be 16-byte aligned");
+  Layer& ly = p->layers[layer];
+  if (!ly.loaded) return fail(MOE_E_INVALID, "layer not loaded");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipEventRecord(p->ev_caller, s));
+  HIP_TRY(hipStreamWaitEvent(p->pf_stream, p->ev_caller, 0));
+  RouterArgs r{};
+  r.x = x;
+  r.w = ly.d_router_w;
+  r.b = ly.d_router_b;
+  r.logits = p->pf_logits;
+  r.T = T;
+  r.H = p->cfg.hidden;
+  r.E = E;
+  r.G = p->cfg.group_size;
+  r.router_blocks = logits_in ? 0 : (E + 7) / 8;
+  PrefetchArgs a{};
+  a.wptr = ly.d_wptr;
+  a.is_host = ly.d_is_host;
+  a.host_pool = ly.host_pool_dev;
+  a.slots = ly.pf_slots;
+  a.occ = ly.d_pf_occ;
+  a.list = ly.d_pf_list;
+  a.predicted_out = predicted_out;
+  a.stats = ly.d_stats;
+  a.logits = logits_in ? logits_in : p->pf_logits;
+  a.bytes = p->L.bytes;
+  a.E = E;
+  a.P = p->cfg.prefetch_slots;
+  a.kp = kp;
+  a.T = T;
+  launch_prefetch(a, r, p->cfg.act_dtype == MOE_ACT_BF16, p->pf_counter, p->pf_stream);
+  HIP_TRY(hipGetLastError());
+  HIP_TRY(hipEventRecord(ly.ev_prefetch, p->pf_stream));
+  ly.pf_pending = true;
+  return MOE_OK;
+}
+
+moe_status moe_plan_prefetch_slots(moe_plan* p, int32_t layer, int32_t* slot_expert) {
+  if (!p || !slot_expert) return fail(MOE_E_INVALID, "null argument");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(MOE_E_INVALID, "layer out of range");
+  if (p->cfg.prefetch_slots == 0) return fail(MOE_E_STATE, "plan has no prefetch slots");
+  HIP_TRY(hipSetDevice(p->device));
+  HIP_TRY(hipStreamSynchronize(p->pf_stream));
+  HIP_TRY(hipMemcpy(slot_expert, p->layers[layer].d_pf_occ, sizeof(int32_t) * p->cfg.prefetch_slots,
+                    hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Synchronous cache update of layers [l0, l1) (see moe_cache_update).
+moe_status cache_update_sync(moe_plan* p, int l0, int l1, double decay, int maxp, const int32_t* want,
+                             hipStream_t s) {
+  const int E = p->cfg.num_experts;
+  for (int l = l0; l < l1; ++l) {
+    moe_status st = wait_prefetch(p, p->layers[l], s);
+    if (st != MOE_OK) return st;
+  }
   for (int l = l0; l < l1; ++l) {
     Layer& ly = p->layers[l];
     HIP_TRY(hipMemcpyAsync(ly.h_counts_stage, ly.d_counts_acc, sizeof(int64_t) * E, hipMemcpyDeviceToHost, s));
@@ -1277,6 +1445,10 @@ moe_status moe_cache_update(moe_plan* p, int32_t layer, const moe_cache_policy* 
   }
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 moe_status moe_plan_set_host_compute(moe_plan* p, int32_t layer, int32_t mode, int32_t threads) {
   if (!p) return fail(MOE_E_INVALID, "plan is null");
@@ -1350,6 +1522,7 @@ moe_status moe_plan_stats(moe_plan* p, int32_t layer, moe_stats* out) {
     out->promotions += ly.promotions;
     out->evictions += ly.evictions;
     out->host_computed += ly.host_computed;
+    out->prefetched += st[ST_PREFETCHED];
   }
   return MOE_OK;
 }

@@ -57,6 +57,8 @@ std::string check_config(const moe_config& c) {
   if (c.hbm_slots < 0 || c.hbm_slots > c.num_experts) return "hbm_slots must be in 0..num_experts";
   if (c.prefill_stage_slots < 0 || c.prefill_stage_slots > c.num_experts)
     return "prefill_stage_slots must be in 0..num_experts";
+  if (c.prefetch_slots < 0 || c.prefetch_slots > c.num_experts || c.prefetch_slots > 64)
+    return "prefetch_slots must be in 0..min(num_experts, 64)";
   if (c.hidden > 65536 || c.inter > 65536) return "hidden and inter must be <= 65536";
   const int bits = c.weight_bits == 0 ? 4 : c.weight_bits;
   if (bits != 2 && bits != 3 && bits != 4) return "weight_bits must be 0 (4), 2, 3 or 4";

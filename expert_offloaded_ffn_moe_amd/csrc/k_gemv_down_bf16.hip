@@ -17,7 +17,8 @@ template <int CPG>
 __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __restrict__ aptr,
                                                     const int32_t* __restrict__ inv, const float* __restrict__ wts,
                                                     const void* __restrict__ h, const float* __restrict__ hpart,
-                                                    float* __restrict__ y, int64_t off_codes, int64_t off_scales,
+                                                    float* __restrict__ y, const uint16_t* __restrict__ xres,
+                                                    uint16_t* __restrict__ xout, int64_t off_codes, int64_t off_scales,
                                                     int chunks, int groups, int H, int I, int k, int splits) {
   __shared__ float part[kMaxW][64];
   const int lane = threadIdx.x & 63;
@@ -44,7 +45,9 @@ __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __rest
       for (int s2 = 0; s2 < splits; ++s2) o += part[jj * splits + s2][lane];
       yv = fmaf(wts[t * k + jj], o, yv);
     }
-    y[(size_t)t * H + tile * 64 + lane] = yv;
+    const size_t i = (size_t)t * H + tile * 64 + lane;
+    y[i] = yv;
+    if (xout) xout[i] = residual_bf16(xres[i], yv);
   }
 }
 
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ wts, const void* __restrict__ h,
                                                       const float* __restrict__ hpart, float* __restrict__ y,
+                                                      const uint16_t* __restrict__ xres, uint16_t* __restrict__ xout,
                                                       int64_t off_codes, int64_t off_scales, int chunks, int groups,
                                                       int H, int I, int k, int splits) {
   __shared__ float part[kMaxW][16];
@@ -169,7 +173,9 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
       for (int s2 = 0; s2 < splits; ++s2) o += part[jj * splits + s2][lane];
       yv = fmaf(wts[t * k + jj], o, yv);
     }
-    y[(size_t)t * H + tile * 16 + lane] = yv;
+    const size_t i = (size_t)t * H + tile * 16 + lane;
+    y[i] = yv;
+    if (xout) xout[i] = residual_bf16(xres[i], yv);
   }
 }
 
@@ -181,10 +187,10 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
   const size_t lds = stage ? down_combine16_lds(a.k, a.I) : 0;
 #define DOWN_COMB16(C)                                                                                               \
   if (stage)                                                                                                         \
-    launch_timed(k_down_comb16<C, true>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,          \
+    launch_timed(k_down_comb16<C, true>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, a.xout, \
                  a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);                            \
   else                                                                                                               \
-    launch_timed(k_down_comb16<C, false>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y,         \
+    launch_timed(k_down_comb16<C, false>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, a.xout, \
                  a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);
   switch (a.G / 32) {
     case 1: DOWN_COMB16(1); break;
@@ -198,7 +204,7 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
 void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s) {
   const dim3 grid(a.H / 64, a.T), block(64 * a.k * a.splits);
 #define DOWN_COMB(C)                                                                                           \
-  launch_timed(k_down_comb<C>, grid, block, 0, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.off_codes,       \
+  launch_timed(k_down_comb<C>, grid, block, 0, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, a.xout, a.off_codes, \
                a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits)
   switch (a.G / 32) {
     case 1: DOWN_COMB(1); break;

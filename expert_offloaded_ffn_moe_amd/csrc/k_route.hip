@@ -16,6 +16,7 @@
 #include <cfloat>
 #include <climits>
 
+#include "copy_dev.h"
 #include "kernels.h"
 #include "route_dev.h"
 #include "wave.h"
@@ -478,6 +479,143 @@ void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, 
 }
 
 
+// ----------------------------------------------------------------------------- predictive prefetch
+
+// Prediction of a prefetch. Blocks [0, router_blocks): router rows, 8 per block, into
+// a.logits (none when the logits are given); every block arrives on the counter,
+// and the last one picks each token's kp best experts (the routing's order: logit
+// descending, id ascending). The predicted set is the first P distinct candidates,
+// in token order then candidate order, whose weights are read from host memory
+// without the prefetch (their host copy, or a prefetch slot of this layer). A slot
+// whose expert is predicted again keeps it; every other slot gives its expert back
+// to its host copy (where the table still points at the slot: a cache update may
+// have rewritten the entry) and is free; each predicted expert not yet in a slot
+// takes the lowest free slot and goes on the copy list.
+template <int BF16, int NCH>
+__global__ __launch_bounds__(512) void k_predict(PrefetchArgs a, RouterArgs r, unsigned* counter) {
+  __shared__ int32_t ids[kPrefetchMaxCand];
+  __shared__ float wts[kPrefetchMaxCand];
+  __shared__ int16_t in_slot[kPrefetchMaxE];  // slot + 1 of an expert the table reads from a slot, else 0
+  __shared__ uint8_t chosen[kPrefetchMaxE];
+  __shared__ int last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if ((int)blockIdx.x < r.router_blocks) {
+    const int e = blockIdx.x * 8 + wave;
+    if (e < r.E) {
+      if (NCH > 0)
+        router_row<BF16, (NCH > 0 ? NCH : 1)>(r, e, lane);
+      else
+        router_row_long<BF16>(r, e, lane);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned prev = atomicAdd(counter, 1u);
+    last = (prev == gridDim.x - 1) ? 1 : 0;
+    if (last) __threadfence();
+  }
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) *counter = 0u;  // ready for the next launch
+  for (int e = threadIdx.x; e < a.E; e += 512) {
+    in_slot[e] = 0;
+    chosen[e] = 0;
+  }
+  for (int t = wave; t < a.T; t += 8)
+    topk_wave(a.logits + (size_t)t * a.E, a.E, a.kp, lane, ids + t * a.kp, wts + t * a.kp, nullptr);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int i = 0; i < a.P; ++i) {
+    const int e = a.occ[i];
+    if (e >= 0 && a.wptr[e] == a.slots + (size_t)i * a.bytes) in_slot[e] = (int16_t)(i + 1);
+  }
+  int n = 0;
+  for (int c = 0; c < a.T * a.kp && n < a.P; ++c) {
+    const int e = ids[c];
+    if (chosen[e] || !(a.is_host[e] != 0 || in_slot[e] != 0)) continue;
+    chosen[e] = 1;
+    if (a.predicted_out) a.predicted_out[n] = e;
+    ++n;
+  }
+  if (a.predicted_out)
+    for (int i = n; i < a.P; ++i) a.predicted_out[i] = -1;
+  for (int i = 0; i < a.P; ++i) {  // slots kept, and slots given back
+    const int e = a.occ[i];
+    if (e < 0) continue;
+    if (in_slot[e] == i + 1) {
+      if (chosen[e]) {
+        chosen[e] = 2;  // stays in slot i
+        continue;
+      }
+      a.wptr[e] = a.host_pool + (size_t)e * a.bytes;
+      a.is_host[e] = 1;
+    }
+    a.occ[i] = -1;
+  }
+  int m = 0, free_slot = 0;
+  for (int c = 0; c < a.T * a.kp; ++c) {  // the new ones, in prediction order
+    const int e = ids[c];
+    if (chosen[e] != 1) continue;
+    chosen[e] = 2;
+    while (a.occ[free_slot] >= 0) ++free_slot;  // a free slot exists: at most P are chosen
+    a.occ[free_slot] = e;
+    a.list[m++] = free_slot;
+  }
+  a.list[a.P] = m;
+  atomicAdd(reinterpret_cast<unsigned long long*>(a.stats + ST_PREFETCHED), (unsigned long long)m);
+}
+
+// The copies: block (j, part) copies part `part` of the expert going into slot
+// list[j] from its host copy; block 0 points the table at the new slots. Forwards
+// of the layer start only after this kernel has finished, so the order of the two
+// inside it does not matter.
+__global__ __launch_bounds__(kCopyThreads) void k_prefetch_copy(PrefetchArgs a) {
+  const int m = a.list[a.P];
+  if (blockIdx.x == 0 && (int)threadIdx.x < m) {
+    const int slot = a.list[threadIdx.x];
+    const int e = a.occ[slot];
+    a.wptr[e] = a.slots + (size_t)slot * a.bytes;
+    a.is_host[e] = 0;
+  }
+  const int j = blockIdx.x / a.blocks_per_expert, part = blockIdx.x % a.blocks_per_expert;
+  if (j >= m) return;
+  const int slot = a.list[j];
+  const int e = a.occ[slot];
+  const int64_t n16 = a.bytes / 16;
+  const int64_t u0 = (int64_t)part * kCopyUnits, u1 = u0 + kCopyUnits < n16 ? u0 + kCopyUnits : n16;
+  copy_units(a.host_pool + (size_t)e * a.bytes, a.slots + (size_t)slot * a.bytes, u0, u1);
+}
+
+void launch_prefetch(PrefetchArgs a, const RouterArgs& r, int act_bf16, unsigned* counter, hipStream_t s) {
+  a.blocks_per_expert = (int)((a.bytes / 16 + kCopyUnits - 1) / kCopyUnits);
+  const int grid = std::max(1, r.router_blocks);
+  const int nch = (r.H * (act_bf16 ? 2 : 4) / 16 + 63) / 64;
+#define PREDICT(B, N) hipLaunchKernelGGL((k_predict<B, N>), dim3(grid), dim3(512), 0, s, a, r, counter)
+#define PREDICT_NCH(B)  \
+  if (nch <= 1)         \
+    PREDICT(B, 1);      \
+  else if (nch <= 2)    \
+    PREDICT(B, 2);      \
+  else if (nch <= 4)    \
+    PREDICT(B, 4);      \
+  else if (nch <= 8)    \
+    PREDICT(B, 8);      \
+  else if (nch <= 16)   \
+    PREDICT(B, 16);     \
+  else                  \
+    PREDICT(B, 0);
+  if (act_bf16) {
+    PREDICT_NCH(1)
+  } else {
+    PREDICT_NCH(0)
+  }
+#undef PREDICT_NCH
+#undef PREDICT
+  hipLaunchKernelGGL(k_prefetch_copy, dim3(a.P * a.blocks_per_expert), dim3(kCopyThreads), 0, s, a);
+}
+
 // ----------------------------------------------------------------------------- multi-block grouping
 
 // Top-k and grouping for any number of assignments, over blocks of kGroupTokens
@@ -712,6 +850,21 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     acc.w = fmaf(w, v.w, acc.w);
   }
   reinterpret_cast<float4*>(a.y + (size_t)t * a.H)[n4] = acc;
+  if (a.xout) {
+    const size_t i4 = (size_t)t * a.H / 4 + n4;
+    if (a.act_bf16) {
+      const ushort4 xv = static_cast<const ushort4*>(a.xres)[i4];
+      ushort4 r;
+      r.x = residual_bf16(xv.x, acc.x);
+      r.y = residual_bf16(xv.y, acc.y);
+      r.z = residual_bf16(xv.z, acc.z);
+      r.w = residual_bf16(xv.w, acc.w);
+      static_cast<ushort4*>(a.xout)[i4] = r;
+    } else {
+      const float4 xv = static_cast<const float4*>(a.xres)[i4];
+      static_cast<float4*>(a.xout)[i4] = make_float4(xv.x + acc.x, xv.y + acc.y, xv.z + acc.z, xv.w + acc.w);
+    }
+  }
 }
 
 void launch_combine(const CombineArgs& a, const Timing& tm, hipStream_t s) {

@@ -12,23 +12,20 @@
 // repeat per row tile.
 #include <hip/hip_runtime.h>
 
+#include "copy_dev.h"
 #include "kernels.h"
 
 namespace moe {
-
-constexpr int kStageThreads = 256;
-constexpr int kStageUnroll = 8;                                      // 16-byte loads in flight per thread
-constexpr int64_t kStageUnits = (int64_t)kStageThreads * kStageUnroll * 2;  // 16-byte units per block (64 KiB)
 
 // Blocks [0, table_blocks): the blob table, one thread per expert. Then
 // n_slots * blocks_per_expert copy blocks: block (s, part) copies part `part`
 // of the expert at active-list position s, if that expert is read from host
 // memory (host-read experts lead the active list, so positions below n_slots
 // that hold one are exactly the staged experts).
-__global__ __launch_bounds__(kStageThreads) void k_stage(StageArgs a) {
+__global__ __launch_bounds__(kCopyThreads) void k_stage(StageArgs a) {
   const int tb = a.table_blocks;
   if ((int)blockIdx.x < tb) {
-    const int e = blockIdx.x * kStageThreads + threadIdx.x;
+    const int e = blockIdx.x * kCopyThreads + threadIdx.x;
     if (e < a.E) {
       const int pos = a.act_pos[e];
       const bool staged = a.counts[e] > 0 && a.is_host[e] != 0 && pos >= 0 && pos < a.n_slots;
@@ -41,30 +38,16 @@ __global__ __launch_bounds__(kStageThreads) void k_stage(StageArgs a) {
   if (s >= *a.n_active) return;
   const int e = a.active[s];
   if (a.is_host[e] == 0) return;
-  const uint4* src = reinterpret_cast<const uint4*>(a.wptr[e]);
-  uint4* dst = reinterpret_cast<uint4*>(a.stage + (size_t)s * a.bytes);
   const int64_t n16 = a.bytes / 16;
-  const int64_t u0 = (int64_t)part * kStageUnits, u1 = u0 + kStageUnits < n16 ? u0 + kStageUnits : n16;
-  for (int64_t u = u0 + threadIdx.x; u < u1; u += (int64_t)kStageThreads * kStageUnroll) {
-    uint4 v[kStageUnroll];
-#pragma unroll
-    for (int i = 0; i < kStageUnroll; ++i) {
-      const int64_t q = u + (int64_t)i * kStageThreads;
-      if (q < u1) v[i] = src[q];
-    }
-#pragma unroll
-    for (int i = 0; i < kStageUnroll; ++i) {
-      const int64_t q = u + (int64_t)i * kStageThreads;
-      if (q < u1) dst[q] = v[i];
-    }
-  }
+  const int64_t u0 = (int64_t)part * kCopyUnits, u1 = u0 + kCopyUnits < n16 ? u0 + kCopyUnits : n16;
+  copy_units(a.wptr[e], a.stage + (size_t)s * a.bytes, u0, u1);
 }
 
 void launch_stage(StageArgs a, const Timing& tm, hipStream_t s) {
-  a.table_blocks = (a.E + kStageThreads - 1) / kStageThreads;
-  a.blocks_per_expert = (int)((a.bytes / 16 + kStageUnits - 1) / kStageUnits);
+  a.table_blocks = (a.E + kCopyThreads - 1) / kCopyThreads;
+  a.blocks_per_expert = (int)((a.bytes / 16 + kCopyUnits - 1) / kCopyUnits);
   const int grid = a.table_blocks + a.n_slots * a.blocks_per_expert;
-  launch_timed(k_stage, dim3(grid), dim3(kStageThreads), 0, s, tm, a);
+  launch_timed(k_stage, dim3(grid), dim3(kCopyThreads), 0, s, tm, a);
 }
 
 }  // namespace moe

@@ -10,7 +10,7 @@
 namespace moe {
 
 // Device counters per layer, int64 each.
-enum StatIndex { ST_FORWARDS = 0, ST_TOKENS, ST_HITS, ST_MISSES, ST_BYTES_HBM, ST_BYTES_HOST, ST_COUNT };
+enum StatIndex { ST_FORWARDS = 0, ST_TOKENS, ST_HITS, ST_MISSES, ST_BYTES_HBM, ST_BYTES_HOST, ST_PREFETCHED, ST_COUNT };
 
 // Optional events stamped by the dispatch itself at kernel start and end.
 struct Timing {
@@ -109,6 +109,8 @@ struct DownCombArgs {
   const void* h;               // [T*k][I] bf16 by sorted position
   const float* hpart;          // [T*k][I/32]
   float* y;                    // [T][H]
+  const uint16_t* xres;        // [T][H] bf16 x, with xout: xout = bf16(x + y), or null
+  uint16_t* xout;
   int64_t off_codes, off_scales;
   int chunks, groups, G, H, I, k, T;
   int splits;                  // waves per slot (K split)
@@ -129,13 +131,41 @@ struct StageArgs {
   int table_blocks, blocks_per_expert;  // set by launch_stage
 };
 
+// Predictive prefetch of one layer's experts into its prefetch slots (k_route.hip).
+struct PrefetchArgs {
+  const uint8_t** wptr;        // [E] the layer's blob table (read and written)
+  int32_t* is_host;            // [E]
+  const uint8_t* host_pool;    // device address of the layer's host copies (expert e at e * bytes)
+  uint8_t* slots;              // [P][bytes] the layer's prefetch slots
+  int32_t* occ;                // [P] expert each slot holds, -1 none
+  int32_t* list;               // [P] slots to fill this time, then [P] their count
+  int32_t* predicted_out;      // [P] or null: the predicted experts in order, -1 past their count
+  int64_t* stats;              // [ST_COUNT] the layer's counters (ST_PREFETCHED)
+  const float* logits;         // [T][E] logits the prediction takes (the router's, or given)
+  int64_t bytes;               // internal blob bytes (multiple of 16)
+  int E, P, kp, T;             // kp: candidates per token
+  int blocks_per_expert;       // set by launch_prefetch
+};
+
 struct CombineArgs {
   const float* o;       // [T*k][H]
   const float* wts;     // [T*k]
   const int32_t* inv;   // [T*k]
   float* y;             // [T][H]
-  int T, H, k;
+  const void* xres;     // [T][H] x in the act dtype, with xout: xout = act(x + y), or null
+  void* xout;
+  int T, H, k, act_bf16;
 };
+
+// The residual epilogue of the combines: act(x + y), the sum formed in fp32 and
+// rounded to bf16 (nearest, ties to even) for bf16 activations.
+__device__ __forceinline__ uint16_t residual_bf16(uint16_t x, float y) {
+  const float r = __uint_as_float((uint32_t)x << 16) + y;
+  uint32_t u = __float_as_uint(r);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x0040u);  // NaN stays NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
 
 constexpr int kRouteSmallMaxAssign = 256;   // T*k handled by launch_route_decode
 constexpr int kRouteSmallMaxTokens = 64;
@@ -159,6 +189,11 @@ size_t down_combine16_lds(int k, int I);  // dynamic LDS bytes of launch_down_co
 constexpr size_t kDownComb16MaxLds = 48 * 1024;
 constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count
 void launch_stage(StageArgs a, const Timing& tm, hipStream_t s);
+// router (unless r.router_blocks == 0) + prediction, then the copies and the table entries
+void launch_prefetch(PrefetchArgs a, const RouterArgs& r, int act_bf16, unsigned* counter, hipStream_t s);
+constexpr int kPrefetchMaxCand = 2048;  // T * kp of one prediction
+constexpr int kPrefetchMaxE = 1024;     // experts per layer
+constexpr int kPrefetchMaxSlots = 64;   // prefetch slots per layer
 void launch_router_mfma(const RouterArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_gateup(const GemmArgs& a, const Timing& tm, hipStream_t s);
 void launch_gemm_down(const GemmArgs& a, const Timing& tm, hipStream_t s);

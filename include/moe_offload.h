@@ -102,6 +102,8 @@ typedef struct {
                               the canonical blob below). 2 and 3 bits need bf16 activations,
                               group_size >= 64 and inter a multiple of 64; their forwards run
                               on the dequant-GEMVs for every batch size (no MFMA path) */
+  int32_t prefetch_slots;  /* 0..min(E, 64) extra HBM slots per layer that moe_prefetch fills with
+                              the experts it predicts; 0 = no prefetch */
 } moe_config;
 
 typedef struct {
@@ -134,6 +136,7 @@ typedef struct {
                              (moe_plan_set_host_compute); their bytes are read from host memory by
                              the CPU, not over the host link, though bytes_host still counts them
                              when they are offloaded */
+  int64_t prefetched;     /* experts copied host -> prefetch slot by moe_prefetch */
 } moe_stats;
 
 /* Where the experts of a layer are computed (moe_plan_set_host_compute). */
@@ -242,6 +245,17 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
                              const float* logits_in, float* y, const moe_routing* route_out,
                              moe_stream stream);
 
+/* The forward, and the residual stream's next value with it: y as moe_layer_forward,
+ * and x_out[t][h] = act(x[t][h] + y[t][h]) (the sum formed in fp32, rounded to bf16,
+ * nearest even, for bf16 activations), written by the same kernel that writes y. The
+ * pages place the MoE FFN inside a transformer's layers ([125B] and [24K]: the
+ * experts of each layer), whose output adds to the residual stream; fusing that add
+ * saves a launch and a round trip of y per layer. x_out: device [T][H] act dtype,
+ * 16-byte aligned, overlapping neither x nor y. Errors: as moe_layer_forward. */
+moe_status moe_layer_forward_residual(moe_plan* plan, int32_t layer, int32_t T, const void* x,
+                                      const float* logits_in, float* y, void* x_out,
+                                      const moe_routing* route_out, moe_stream stream);
+
 /* moe_layer_forward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation. The
  * same kernels and results (bitwise), with the forward's workspace (logits,
@@ -258,6 +272,43 @@ moe_status moe_layer_forward(moe_plan* plan, int32_t layer, int32_t T, const voi
 moe_status moe_layer_forward_noalloc(moe_plan* plan, int32_t layer, int32_t T, const void* x,
                                      const float* logits_in, float* y, const moe_routing* route_out,
                                      moe_stream stream);
+
+/* Predictive prefetch of one layer ([24K] section 二: while the current layer is
+ * computed, the next layer's experts are already streaming over the link into
+ * VRAM). The pages do not say how the experts are chosen; the plain reading taken
+ * is the layer's own router applied to the activations at hand, normally the
+ * current layer's input x (or the given logits_in [T][E] fp32), since the residual
+ * stream changes little from one layer to the next:
+ *   candidates = each token's `candidates` best experts (0 = top_k; at most 64 and
+ *                E), in the routing's order, tokens in order, T * candidates <= 2048;
+ *   predicted  = the first prefetch_slots distinct candidates whose weights are read
+ *                from host memory without a prefetch (their host copy, or a prefetch
+ *                slot of this layer);
+ *   the layer's prefetch slots: a slot whose expert is predicted again keeps it;
+ *                every other slot gives its expert back to its host copy; each
+ *                predicted expert not in a slot is copied into the lowest free slot.
+ * Until the next moe_prefetch of the layer, forwards read the slotted experts from
+ * HBM (hits). The work (router rows, prediction, copies) runs on a stream of the
+ * plan, after the work enqueued on `stream` before this call: x must be ready there,
+ * and the layer's earlier forwards and the plan's cache updates must be ordered
+ * before that point (enqueued on `stream`, or joined to it by the caller's events).
+ * The layer's next forward, cache update or load waits for the prefetch on the
+ * device, on whatever stream it runs. So a prefetch of layer l+1 issued just before
+ * the forward of layer l overlaps that forward. Both calls may be captured into a
+ * HIP graph (the prefetch stream forks from and joins the capturing stream).
+ * x [T][H] act dtype device (unused when logits_in is given); predicted_out: device
+ * int32 [prefetch_slots] or NULL, the predicted experts in order, -1 after the last.
+ * Cache updates rewrite whole tables and so give prefetched experts back to their
+ * host copies (or HBM slots). Errors: MOE_E_INVALID (arguments, T out of
+ * 1..max_tokens, layer not loaded), MOE_E_STATE (prefetch_slots == 0), MOE_E_HIP. */
+moe_status moe_prefetch(moe_plan* plan, int32_t layer, int32_t T, const void* x, const float* logits_in,
+                        int32_t candidates, int32_t* predicted_out, moe_stream stream);
+
+/* Host [prefetch_slots] slot table of a layer's prefetch: slot_expert[i] = the
+ * expert prefetch slot i holds, -1 none (a slot whose table entry a cache update
+ * has since rewritten still lists its expert until the next prefetch frees it).
+ * Waits for the layer's prefetch work. Errors: MOE_E_INVALID, MOE_E_STATE, MOE_E_HIP. */
+moe_status moe_plan_prefetch_slots(moe_plan* plan, int32_t layer, int32_t* slot_expert);
 
 /* Expert-cache update of one layer (or all, layer = -1). [24K] section 二: free
  * VRAM holds the most used experts, and the cache adapts the longer it runs; the

@@ -385,3 +385,54 @@ def cache_set_resident(score: np.ndarray, counts: np.ndarray, slot_of: np.ndarra
             slot_of[e] = s
             promoted.append((e, s))
     return score, slot_of, promoted, evicted
+
+
+def prefetch_step(logits: np.ndarray, candidates: int, n_slots: int, host_read: np.ndarray,
+                  slot_expert: np.ndarray, slot_valid: np.ndarray):
+    """One predictive prefetch of a layer (page "我在 32GB 单卡上跑两万四千专家的 MoE…",
+    section "二、跑起来靠的是分层,不是激活": the next layer's experts stream into VRAM
+    while the current layer is computed). The page does not say how the experts are
+    chosen; the reading taken: the layer's router logits of the activations at hand.
+
+    logits [T, E] float32; host_read[e] = the expert's weights are read from host memory
+    when no prefetch holds it; slot_expert [n_slots] = the expert each prefetch slot holds
+    (-1 none); slot_valid[i] = slot i still serves its expert (no cache update has since
+    pointed that expert elsewhere).
+    Candidates: each token's `candidates` best experts (logit descending, id ascending),
+    token by token. Predicted: the first n_slots distinct candidates that are host_read or
+    held by a valid slot. A valid slot whose expert is predicted keeps it; every other
+    slot is freed; each predicted expert not kept takes the lowest free slot, in
+    prediction order, and is copied.
+    Returns (predicted list, new slot_expert [n_slots], [(slot, expert) copied]).
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    held = {int(slot_expert[i]): i for i in range(n_slots) if slot_expert[i] >= 0 and slot_valid[i]}
+    predicted = []
+    for t in range(logits.shape[0]):
+        for e in topk_ids(logits[t], candidates):
+            e = int(e)
+            if len(predicted) < n_slots and e not in predicted and (host_read[e] or e in held):
+                predicted.append(e)
+    new = np.full(n_slots, -1, dtype=np.int64)
+    for e, i in held.items():
+        if e in predicted:
+            new[i] = e
+    copied = []
+    for e in predicted:
+        if e in held:
+            continue
+        i = int(np.flatnonzero(new < 0)[0])
+        new[i] = e
+        copied.append((i, e))
+    return predicted, new, copied
+
+
+def residual_next(x: np.ndarray, y: np.ndarray, act: str) -> np.ndarray:
+    """The residual stream's next value after a MoE FFN layer: act(x + y), the sum formed
+    in float32 (x in the activation dtype, y the layer's float32 output) and then
+    rounded to the activation dtype (nearest, ties to even). The pages place the expert
+    FFN inside transformer layers whose outputs add to the residual stream; they do not
+    fix the precision of the add, and this is the plain reading for a float32 y.
+    Returns float64 values."""
+    s = np.asarray(x, dtype=np.float64).astype(np.float32) + np.asarray(y, dtype=np.float32)
+    return round_act(s.astype(np.float64), act)

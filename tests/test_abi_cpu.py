@@ -43,7 +43,10 @@ def test_expert_bytes_and_validation(lib):
            moe.make_config(256, 128, 8, 2, 48), moe.make_config(256, 128, 2000, 2, 32),
            moe.make_config(256, 100, 8, 2, 32), moe.make_config(256, 128, 8, 2, 32, max_tokens=0),
            moe.make_config(256, 128, 8, 2, 32, hbm_slots=9), moe.make_config(256, 128, 8, 2, 32, prefill_stage_slots=9),
-           moe.make_config(256, 128, 8, 2, 32, prefill_stage_slots=-1)]
+           moe.make_config(256, 128, 8, 2, 32, prefill_stage_slots=-1),
+           moe.make_config(256, 128, 8, 2, 32, prefetch_slots=9),
+           moe.make_config(256, 128, 128, 2, 32, prefetch_slots=65),
+           moe.make_config(256, 128, 8, 2, 32, prefetch_slots=-1)]
     for cfg in bad:
         out = ctypes.c_size_t()
         assert lib.moe_expert_bytes(ctypes.byref(cfg), ctypes.byref(out)) == moe.MOE_E_INVALID
@@ -58,6 +61,8 @@ def test_status_strings_and_null_args(lib):
     assert lib.moe_status_str(4) == b"MOE_E_HIP"
     assert lib.moe_layer_forward(None, 0, 1, None, None, None, None, None) == moe.MOE_E_INVALID
     assert lib.moe_cache_update(None, 0, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_prefetch(None, 0, 1, None, None, 0, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_plan_prefetch_slots(None, 0, None) == moe.MOE_E_INVALID
     lib.moe_plan_destroy(None)
 
 
@@ -77,7 +82,7 @@ def test_binding_structs_match_header(cname, pyname):
     same size (ctypes lays fields out by the platform C ABI)."""
     fields = [n for _, n in _header_struct_fields(cname)]
     assert [n for n, _ in getattr(moe, pyname)._fields_] == fields, cname
-    sizes = {"moe_layer_weights": 24, "moe_routing": 56, "moe_stats": 80, "moe_cache_policy": 24,
+    sizes = {"moe_layer_weights": 24, "moe_routing": 56, "moe_stats": 88, "moe_cache_policy": 24,
              "moe_plan_info": 48, "moe_link_ceilings": 24, "moe_kernel_times": 128}
     assert ctypes.sizeof(getattr(moe, pyname)) == sizes[cname]
 

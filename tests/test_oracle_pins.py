@@ -543,6 +543,86 @@ def test_cache_set_resident_reaches_the_wanted_set():
         assert [e for e, _ in done] == sorted(np.nonzero((slot_of < 0) & want.astype(bool))[0].tolist())
 
 
+def test_prefetch_step_hand_cases():
+    lg = np.array([[5, 4, 3, 2, 1, 0], [0, 1, 2, 3, 4, 5]], np.float32)
+    host = np.array([1, 0, 1, 1, 1, 1])
+    # empty slots: token 0's top 3 are 0, 1, 2 (1 is in HBM, skipped), token 1's first is 5
+    pred, new, cp = O.prefetch_step(lg, 3, 3, host, np.full(3, -1), np.ones(3, bool))
+    assert pred == [0, 2, 5] and new.tolist() == [0, 2, 5] and cp == [(0, 0), (1, 2), (2, 5)]
+    # slot 1 holds 5, predicted again: kept; slot 2's 3 is not predicted: freed; 0 and 2
+    # then take the lowest free slots 0 and 2
+    pred, new, cp = O.prefetch_step(lg, 3, 3, host, np.array([-1, 5, 3]), np.ones(3, bool))
+    assert pred == [0, 2, 5] and new.tolist() == [0, 5, 2] and cp == [(0, 0), (2, 2)]
+    # a slot whose table entry was rewritten serves nothing: its expert is copied again
+    pred, new, cp = O.prefetch_step(lg, 3, 3, host, np.array([2, -1, -1]), np.array([False, True, True]))
+    assert pred == [0, 2, 5] and cp == [(0, 0), (1, 2), (2, 5)]
+    # an HBM-resident expert held by a stale slot is not predicted
+    host2 = np.array([1, 0, 0, 1, 1, 1])
+    pred, new, cp = O.prefetch_step(lg, 3, 3, host2, np.array([2, -1, -1]), np.array([False, True, True]))
+    assert pred == [0, 5, 4] and new.tolist() == [0, 5, 4]
+    # ties go to the lower id (-0.0 ties +0.0); tokens repeating experts add nothing
+    lt = np.array([[1, 1, 1, 1], [0.0, -0.0, 2, -1], [1, 1, 1, 1]], np.float32)
+    pred, new, cp = O.prefetch_step(lt, 2, 4, np.ones(4, int), np.full(4, -1), np.ones(4, bool))
+    assert pred == [0, 1, 2] and new.tolist() == [0, 1, 2, -1]
+    # every candidate in HBM: nothing predicted, held slots freed
+    pred, new, cp = O.prefetch_step(lg, 2, 2, np.zeros(6, int), np.array([3, -1]), np.ones(2, bool))
+    assert pred == [] and new.tolist() == [-1, -1] and cp == []
+
+
+def test_prefetch_step_invariants():
+    """Random cases: the predicted experts are distinct host-read candidates taken in
+    candidate order (none skipped while slots remain), the slots end up holding exactly
+    them, a kept expert stays in its slot, and only the others are copied."""
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        E = int(rng.integers(1, 30))
+        T, kp, P = int(rng.integers(1, 5)), int(rng.integers(1, E + 1)), int(rng.integers(1, E + 1))
+        lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+        host = rng.integers(0, 2, size=E)
+        occ = np.full(P, -1)
+        held_e = rng.choice(E, size=int(rng.integers(0, min(P, E) + 1)), replace=False)
+        occ[rng.choice(P, size=held_e.size, replace=False)] = held_e
+        valid = rng.integers(0, 2, size=P).astype(bool)
+        host_eff = host.copy()
+        for i in range(P):
+            if occ[i] >= 0 and valid[i]:
+                host_eff[occ[i]] = 1
+        pred, new, cp = O.prefetch_step(lg, kp, P, host, occ, valid)
+        cand = [int(e) for t in range(T) for e in O.topk_ids(lg[t], kp)]
+        want = []
+        for e in cand:
+            if host_eff[e] and e not in want:
+                want.append(e)
+        assert pred == want[:P]
+        assert sorted(new[new >= 0].tolist()) == sorted(pred)
+        for i in range(P):
+            if occ[i] >= 0 and valid[i] and occ[i] in pred:
+                assert new[i] == occ[i]
+        assert sorted(e for _, e in cp) == sorted(e for e in pred
+                                                  if not any(occ[i] == e and valid[i] for i in range(P)))
+        assert all(new[i] == e for i, e in cp)
+
+
+def test_residual_next_rounding():
+    # 1 + 2^-8 is halfway between the bf16 neighbours 1 and 1 + 2^-7: ties to even
+    assert O.residual_next(np.array([1.0]), np.array([2.0 ** -8]), "bf16")[0] == 1.0
+    assert O.residual_next(np.array([1.0]), np.array([3 * 2.0 ** -9]), "bf16")[0] == 1.0 + 2.0 ** -7
+    assert O.residual_next(np.array([1.0 + 2.0 ** -7]), np.array([2.0 ** -8]), "bf16")[0] == 1.0 + 2.0 ** -6
+    # the sum is a float32 one first: 2^-30 is lost there, so the halfway case stays a tie
+    # (the exact sum would round up)
+    assert O.residual_next(np.array([1.0]), np.array([2.0 ** -8 + 2.0 ** -30]), "bf16")[0] == 1.0
+    # float32 activations: the float32 sum itself; negatives and cancellation
+    assert O.residual_next(np.array([1.0]), np.array([2.0 ** -30]), "f32")[0] == 1.0
+    assert O.residual_next(np.array([-3.0, 0.5]), np.array([3.0, -0.25]), "bf16").tolist() == [0.0, 0.25]
+    # against torch's own float32 add and bfloat16 conversion on random values
+    import torch
+    rng = np.random.default_rng(3)
+    xb = O.round_bf16(rng.normal(size=4096))
+    y = rng.normal(scale=0.1, size=4096).astype(np.float32)
+    ref = (torch.tensor(xb, dtype=torch.float32) + torch.tensor(y)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.residual_next(xb, y, "bf16"), ref)
+
+
 # ----------------------------------------------------------------------------- page structural figures
 
 
