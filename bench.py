@@ -636,6 +636,8 @@ def main():
             extra.update(r)
     head_key = {"deepseek": "deepseek_mixed_b1", "qwen3": "qwen3_hbm_b1", "prefill": "prefill_t2048",
                 "cache": "cache_48_layers"}[order[0]]
+    if head_key not in configs:  # a subset of runs: the first one measured heads the line
+        head_key = next(iter(configs))
     head = configs[head_key]
     line = {
         "metric": METRIC,

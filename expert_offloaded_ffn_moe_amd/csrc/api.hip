@@ -934,6 +934,7 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   ra.H = H;
   ra.E = E;
   ra.G = G;
+  ra.rw = router_split(H, bf16, E);
   const float* logits = logits_in ? logits_in : w.logits;
 
   RouteArgs rt{};
@@ -1083,8 +1084,8 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
     }
     HIP_TRY(hipGetLastError());
   } else if (decode) {
-    // router + group sums + top-k + grouping in one launch (8 expert rows per block)
-    ra.router_blocks = logits_in ? 0 : (E + 7) / 8;
+    // router + group sums + top-k + grouping in one launch
+    ra.router_blocks = logits_in ? 0 : router_blocks_for(H, bf16, E);
     LAUNCH_USES("k_route_decode", 0,
                 (logits_in ? 0 : WB_LOGITS) | (bf16 ? WB_XSUM : 0) | WB_IDS | WB_WTS | WB_COUNTS | WB_OFFSETS |
                     WB_SORTED | WB_INV | WB_ACTIVE | WB_NACTIVE | WB_WORK | (rt.aptr ? WB_APTR : 0));
@@ -1098,7 +1099,7 @@ moe_status forward_impl(moe_plan* p, int32_t layer, int32_t T, const void* x, co
         ra.router_blocks = logits_in ? 0 : 1;
         launch_router_mfma(ra, kt.tm, s);
       } else {
-        ra.router_blocks = logits_in ? 0 : (E + 3) / 4;
+        ra.router_blocks = logits_in ? 0 : router_blocks_for(H, bf16, E);
         launch_router(ra, bf16, kt.tm, s);
       }
     }
@@ -1345,7 +1346,8 @@ moe_status moe_prefetch(moe_plan* p, int32_t layer, int32_t T, const void* x, co
   r.H = p->cfg.hidden;
   r.E = E;
   r.G = p->cfg.group_size;
-  r.router_blocks = logits_in ? 0 : (E + 7) / 8;
+  r.router_blocks = logits_in ? 0 : router_blocks_for(p->cfg.hidden, p->cfg.act_dtype == MOE_ACT_BF16, E);
+  r.rw = router_split(p->cfg.hidden, p->cfg.act_dtype == MOE_ACT_BF16, E);
   PrefetchArgs a{};
   a.wptr = ly.d_wptr;
   a.is_host = ly.d_is_host;

@@ -100,7 +100,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 // When xsum is given, workgroups past the logits tiles (all of them when
 // tile_blocks is 0) write xsum[t][g] = sum of x[t][gG .. gG+G) for the GEMVs, in
 // element order.
-constexpr int kRouterWaves = 8;
 __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ w,
                                                                    const float* __restrict__ b,

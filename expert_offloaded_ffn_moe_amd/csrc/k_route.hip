@@ -53,86 +53,104 @@ __device__ __forceinline__ float dot16(const u32x4& w, const u32x4& x, float s, 
   return s;
 }
 
-// One wave: logits of expert row e for every token. Lane l owns the 16-byte
-// chunks l, l+64, ... of the row (at most NCH of them, held in registers).
-// Rows of 8 or more chunks per lane (H >= 4096 in bf16) take tokens in pairs
-// whose x chunks are all loaded before the dot products, so a batch of a few
-// tokens costs half as many rounds of loads (DeepSeek-shaped batch 4: routing
-// 25.5 -> 18.7 us). Shorter rows keep one token per round: their loads hide
-// behind the rest of the routing, and the extra registers cost more than they
-// save there. Per token: fp32 sums in chunk order, then a fixed DPP tree across lanes.
+// Router rows, split over RW waves each (RW = 1, 2, 4 or 8, so that a wave holds at
+// most NCH 16-byte chunks of its part of the row in registers and a launch spreads
+// over enough CUs: kRouterWaves waves per workgroup take kRouterWaves / RW rows).
+// Lane l of a part owns chunks c0 + l, c0 + l + 64, ... of it. Per token, in
+// passes of up to kRouterTok tokens whose x chunks are all loaded before the dot
+// products: fp32 sums in chunk order per lane, a fixed DPP tree across the lanes,
+// then the RW parts added in order by the row's first wave.
+// NCH == 0: parts longer than 8 * 64 chunks, a plain strided loop.
+constexpr int kRouterTok = 4;
 
 template <int BF16, int NCH>
-__device__ __forceinline__ void router_row(const RouterArgs& a, int e, int lane) {
+__device__ __forceinline__ void router_rows(const RouterArgs& a, int bid, float (*part)[kRouterTok]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int RW = a.rw;
+  const int e = bid * (kRouterWaves / RW) + wave / RW, pt = wave % RW;
+  const bool row_ok = e < a.E;
   const int esz = BF16 ? 2 : 4;
   const int nchunk = a.H * esz / 16;
-  gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
-  const float bias = a.b ? a.b[e] : 0.f;
-  u32x4 wv[NCH];
+  const int per = (nchunk + RW - 1) / RW;
+  const int c0 = pt * per, c1 = min(nchunk, c0 + per);
+  gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)min(e, a.E - 1) * a.H * esz);
+  const float bias = (row_ok && a.b) ? a.b[e] : 0.f;
+  constexpr int NW = NCH > 0 ? NCH : 1;
+  u32x4 wv[NW];
+  if (NCH > 0) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) wv[i] = wrow[min(lane + 64 * i, nchunk - 1)];
-  constexpr int TOK = NCH >= 8 ? 2 : 1;
-  for (int t0 = 0; t0 < a.T; t0 += TOK) {
-    const int nt = min(TOK, a.T - t0);
-    u32x4 xv[TOK][NCH];
+    for (int i = 0; i < NW; ++i) wv[i] = wrow[min(c0 + lane + 64 * i, nchunk - 1)];
+  }
+  for (int t0 = 0; t0 < a.T; t0 += kRouterTok) {
+    const int nt = min(kRouterTok, a.T - t0);
+    float sum[kRouterTok];
+    if (NCH > 0) {
+      u32x4 xv[kRouterTok][NW];
 #pragma unroll
-    for (int tt = 0; tt < TOK; ++tt) {
-      if (tt < nt) {
-        gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)(t0 + tt) * a.H * esz);
+      for (int tt = 0; tt < kRouterTok; ++tt) {
+        if (tt < nt) {
+          gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)(t0 + tt) * a.H * esz);
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) xv[tt][i] = xrow[min(lane + 64 * i, nchunk - 1)];
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < TOK; ++tt) {
-      if (tt < nt) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const float d = dot16(wv[i], xv[tt][i], 0.f, BF16);
-          s += (lane + 64 * i < nchunk) ? d : 0.f;
+          for (int i = 0; i < NW; ++i) xv[tt][i] = xrow[min(c0 + lane + 64 * i, nchunk - 1)];
         }
-        const float v = wave_sum(s);
-        if (lane == 0) a.logits[(size_t)(t0 + tt) * a.E + e] = v + bias;
+      }
+#pragma unroll
+      for (int tt = 0; tt < kRouterTok; ++tt) {
+        float v = 0.f;
+        if (tt < nt) {
+#pragma unroll
+          for (int i = 0; i < NW; ++i) {
+            const float d = dot16(wv[i], xv[tt][i], 0.f, BF16);
+            v += (c0 + lane + 64 * i < c1) ? d : 0.f;
+          }
+        }
+        sum[tt] = wave_sum(v);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < kRouterTok; ++tt) {
+        float v = 0.f;
+        if (tt < nt) {
+          gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)(t0 + tt) * a.H * esz);
+          for (int c = c0 + lane; c < c1; c += 64) {
+            const u32x4 wc = wrow[c], xc = xrow[c];
+            v = dot16(wc, xc, v, BF16);
+          }
+        }
+        sum[tt] = wave_sum(v);
       }
     }
-  }
-}
-
-// Rows longer than 64 * 16 chunks: plain strided loop.
-template <int BF16>
-__device__ __forceinline__ void router_row_long(const RouterArgs& a, int e, int lane) {
-  const int esz = BF16 ? 2 : 4;
-  const int nchunk = a.H * esz / 16;
-  gu32x4* wrow = (gu32x4*)(static_cast<const char*>(a.w) + (size_t)e * a.H * esz);
-  const float bias = a.b ? a.b[e] : 0.f;
-  for (int t = 0; t < a.T; ++t) {
-    gu32x4* xrow = (gu32x4*)(static_cast<const char*>(a.x) + (size_t)t * a.H * esz);
-    float s = 0.f;
-    for (int c = lane; c < nchunk; c += 64) {
-      const u32x4 wv = wrow[c], xv = xrow[c];
-      s = dot16(wv, xv, s, BF16);
+    if (RW == 1) {
+      if (lane < nt && row_ok) {
+        float v = sum[0];
+#pragma unroll
+        for (int tt = 1; tt < kRouterTok; ++tt) v = lane == tt ? sum[tt] : v;
+        st_shared_dev(a.logits + (size_t)(t0 + lane) * a.E + e, v + bias);
+      }
+    } else {
+      if (lane < kRouterTok) {
+        float v = sum[0];
+#pragma unroll
+        for (int tt = 1; tt < kRouterTok; ++tt) v = lane == tt ? sum[tt] : v;
+        part[wave][lane] = v;
+      }
+      __syncthreads();
+      if (pt == 0 && lane < nt && row_ok) {
+        float v = 0.f;
+        for (int q = 0; q < RW; ++q) v += part[wave + q][lane];
+        st_shared_dev(a.logits + (size_t)(t0 + lane) * a.E + e, v + bias);
+      }
+      __syncthreads();
     }
-    const float v = wave_sum(s);
-    if (lane == 0) a.logits[(size_t)t * a.E + e] = v + bias;
   }
 }
 
-template <int BF16>
-__device__ __forceinline__ void router_row_any(const RouterArgs& a, int e, int lane) {
-  const int nch = (a.H * (BF16 ? 2 : 4) / 16 + 63) / 64;
-  if (nch <= 1)
-    router_row<BF16, 1>(a, e, lane);
-  else if (nch <= 2)
-    router_row<BF16, 2>(a, e, lane);
-  else if (nch <= 4)
-    router_row<BF16, 4>(a, e, lane);
-  else if (nch <= 8)
-    router_row<BF16, 8>(a, e, lane);
-  else if (nch <= 16)
-    router_row<BF16, 16>(a, e, lane);
-  else
-    router_row_long<BF16>(a, e, lane);
+// Chunks per lane of the router's row parts (0: the strided loop).
+inline int router_nch(const RouterArgs& a, int act_bf16) {
+  const int nchunk = a.H * (act_bf16 ? 2 : 4) / 16;
+  const int per = (nchunk + a.rw - 1) / a.rw;
+  const int n = (per + 63) / 64;
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 0;
 }
 
 // sum of x[t][g*G .. (g+1)*G) for flat index gid = t * (H/G) + g (bf16 x)
@@ -156,27 +174,42 @@ __device__ __forceinline__ void xsum_one(const RouterArgs& a, int gid) {
   a.xsum[gid] = s;
 }
 
-// Any T: blocks [0, router_blocks) do 4 expert rows each, the rest the group sums.
-template <int BF16>
-__global__ __launch_bounds__(256) void k_router(RouterArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Any T: blocks [0, router_blocks) take router rows, the rest the group sums.
+template <int BF16, int NCH>
+__global__ __launch_bounds__(512) void k_router(RouterArgs a) {
+  __shared__ float part[kRouterWaves][kRouterTok];
   if ((int)blockIdx.x < a.router_blocks) {
-    const int e = blockIdx.x * 4 + wave;
-    if (e < a.E) router_row_any<BF16>(a, e, lane);
+    router_rows<BF16, NCH>(a, blockIdx.x, part);
   } else if (BF16) {
-    const int gid = (blockIdx.x - a.router_blocks) * 256 + threadIdx.x;
+    const int gid = (blockIdx.x - a.router_blocks) * 512 + threadIdx.x;
     if (gid < a.T * (a.H / a.G)) xsum_one(a, gid);
   }
 }
 
 void launch_router(const RouterArgs& a, int act_bf16, const Timing& tm, hipStream_t s) {
-  const int xs_blocks = (act_bf16 && a.xsum) ? (a.T * (a.H / a.G) + 255) / 256 : 0;
+  const int xs_blocks = (act_bf16 && a.xsum) ? (a.T * (a.H / a.G) + 511) / 512 : 0;
   const int grid = a.router_blocks + xs_blocks;
   if (grid == 0) return;
-  if (act_bf16)
-    launch_timed(k_router<1>, dim3(grid), dim3(256), 0, s, tm, a);
-  else
-    launch_timed(k_router<0>, dim3(grid), dim3(256), 0, s, tm, a);
+  const int nch = router_nch(a, act_bf16);
+#define ROUTER(B, N) launch_timed(k_router<B, N>, dim3(grid), dim3(512), 0, s, tm, a)
+#define ROUTER_NCH(B) \
+  if (nch == 1)       \
+    ROUTER(B, 1);     \
+  else if (nch == 2)  \
+    ROUTER(B, 2);     \
+  else if (nch == 4)  \
+    ROUTER(B, 4);     \
+  else if (nch == 8) \
+    ROUTER(B, 8); \
+  else                \
+    ROUTER(B, 0);
+  if (act_bf16) {
+    ROUTER_NCH(1)
+  } else {
+    ROUTER_NCH(0)
+  }
+#undef ROUTER_NCH
+#undef ROUTER
 }
 
 // ----------------------------------------------------------------------------- align / permute
@@ -205,6 +238,7 @@ struct DecodeShared {
   int is_host[1024];
   const uint8_t* wptr[1024];
   int ids_small[kRouteSmallMaxAssign];
+  float part[kRouterWaves][kRouterTok];  // router row parts
   int a_cnt[kRouteSmallMaxAssign], a_off[kRouteSmallMaxAssign];  // per assignment: its expert's count, offset
   uint64_t m[kRouteSmallMaxAssign / 64][10], vmask[kRouteSmallMaxAssign / 64];
   uint64_t lead[kRouteSmallMaxAssign / 64], hostm[kRouteSmallMaxAssign / 64];
@@ -415,30 +449,12 @@ __global__ __launch_bounds__(512) void k_route_decode(RouteArgs a, RouterArgs r,
     sh.wptr[e] = a.wptr[e];
   }
   if (bid < r.router_blocks) {
-    const int e = bid * 8 + wave;
-    if (e < r.E) {
-      if (NCH > 0)
-        router_row<BF16, (NCH > 0 ? NCH : 1)>(r, e, lane);
-      else
-        router_row_long<BF16>(r, e, lane);
-    }
+    router_rows<BF16, NCH>(r, bid, sh.part);
   } else if (BF16 && r.xsum) {
     const int gid = (bid - r.router_blocks) * 512 + threadIdx.x;
     if (gid < r.T * (r.H / r.G)) xsum_one(r, gid);
   }
-  // every wave drains its stores; one thread publishes the block's writes with a
-  // device-scope release and arrives; the last arrival acquires
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    sh.last = (prev == gridDim.x - 1) ? 1 : 0;
-    if (sh.last) __threadfence();
-  }
-  __syncthreads();
-  if (!sh.last) return;
-  if (threadIdx.x == 0) *counter = 0u;  // ready for the next launch on this stream
+  if (!arrive_last(counter, gridDim.x, &sh.last)) return;
   for (int t = wave; t < a.T; t += 8)
     topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, lane, a.ids + (size_t)t * a.k, a.wts + (size_t)t * a.k,
               sh.ids_small + t * a.k);
@@ -454,19 +470,17 @@ void launch_route_decode(const RouteArgs& a, const RouterArgs& r, int act_bf16, 
                          const Timing& tm, hipStream_t s) {
   const int xs_blocks = (act_bf16 && r.xsum) ? (r.T * (r.H / r.G) + 511) / 512 : 0;
   const int grid = std::max(1, r.router_blocks + xs_blocks);
-  const int nch = (r.H * (act_bf16 ? 2 : 4) / 16 + 63) / 64;
+  const int nch = router_nch(r, act_bf16);
 #define ROUTE_DECODE(B, N) launch_timed(k_route_decode<B, N>, dim3(grid), dim3(512), 0, s, tm, a, r, counter)
 #define ROUTE_DECODE_NCH(B)   \
-  if (nch <= 1)               \
+  if (nch == 1)               \
     ROUTE_DECODE(B, 1);       \
-  else if (nch <= 2)          \
+  else if (nch == 2)          \
     ROUTE_DECODE(B, 2);       \
-  else if (nch <= 4)          \
+  else if (nch == 4)          \
     ROUTE_DECODE(B, 4);       \
-  else if (nch <= 8)          \
-    ROUTE_DECODE(B, 8);       \
-  else if (nch <= 16)         \
-    ROUTE_DECODE(B, 16);      \
+  else if (nch == 8) \
+    ROUTE_DECODE(B, 8); \
   else                        \
     ROUTE_DECODE(B, 0);
   if (act_bf16) {
@@ -497,28 +511,11 @@ __global__ __launch_bounds__(512) void k_predict(PrefetchArgs a, RouterArgs r, u
   __shared__ float wts[kPrefetchMaxCand];
   __shared__ int16_t in_slot[kPrefetchMaxE];  // slot + 1 of an expert the table reads from a slot, else 0
   __shared__ uint8_t chosen[kPrefetchMaxE];
+  __shared__ float part[kRouterWaves][kRouterTok];
   __shared__ int last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if ((int)blockIdx.x < r.router_blocks) {
-    const int e = blockIdx.x * 8 + wave;
-    if (e < r.E) {
-      if (NCH > 0)
-        router_row<BF16, (NCH > 0 ? NCH : 1)>(r, e, lane);
-      else
-        router_row_long<BF16>(r, e, lane);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    last = (prev == gridDim.x - 1) ? 1 : 0;
-    if (last) __threadfence();
-  }
-  __syncthreads();
-  if (!last) return;
-  if (threadIdx.x == 0) *counter = 0u;  // ready for the next launch
+  if ((int)blockIdx.x < r.router_blocks) router_rows<BF16, NCH>(r, blockIdx.x, part);
+  if (!arrive_last(counter, gridDim.x, &last)) return;
   for (int e = threadIdx.x; e < a.E; e += 512) {
     in_slot[e] = 0;
     chosen[e] = 0;
@@ -591,19 +588,17 @@ __global__ __launch_bounds__(kCopyThreads) void k_prefetch_copy(PrefetchArgs a) 
 void launch_prefetch(PrefetchArgs a, const RouterArgs& r, int act_bf16, unsigned* counter, hipStream_t s) {
   a.blocks_per_expert = (int)((a.bytes / 16 + kCopyUnits - 1) / kCopyUnits);
   const int grid = std::max(1, r.router_blocks);
-  const int nch = (r.H * (act_bf16 ? 2 : 4) / 16 + 63) / 64;
+  const int nch = router_nch(r, act_bf16);
 #define PREDICT(B, N) hipLaunchKernelGGL((k_predict<B, N>), dim3(grid), dim3(512), 0, s, a, r, counter)
 #define PREDICT_NCH(B)  \
-  if (nch <= 1)         \
+  if (nch == 1)         \
     PREDICT(B, 1);      \
-  else if (nch <= 2)    \
+  else if (nch == 2)    \
     PREDICT(B, 2);      \
-  else if (nch <= 4)    \
+  else if (nch == 4)    \
     PREDICT(B, 4);      \
-  else if (nch <= 8)    \
-    PREDICT(B, 8);      \
-  else if (nch <= 16)   \
-    PREDICT(B, 16);     \
+  else if (nch == 8) \
+    PREDICT(B, 8); \
   else                  \
     PREDICT(B, 0);
   if (act_bf16) {
@@ -652,19 +647,9 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
   __syncthreads();
   if (tid < nt * k) atomicAdd(&sh.cnt[sh.ids[tid]], 1);
   __syncthreads();
-  if (tid < E) a.hist[(size_t)blockIdx.x * E + tid] = sh.cnt[tid];
-  // publish, arrive; the last block sees every block's counts
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    sh.last = (prev == (unsigned)nb - 1) ? 1 : 0;
-    if (sh.last) __threadfence();
-  }
-  __syncthreads();
-  if (!sh.last) return;
-  if (tid == 0) *counter = 0u;  // ready for the next launch on this stream
+  if (tid < E) st_shared_dev(a.hist + (size_t)blockIdx.x * E + tid, sh.cnt[tid]);
+  // arrive; the last block sees every block's counts
+  if (!arrive_last(counter, (unsigned)nb, &sh.last)) return;
   const int n = a.T * k;
   // expert totals, offsets and per-block bases (written over the counts): J threads
   // per expert, thread (e = tid % E, j = tid / E) summing blocks [j nb / J, (j+1) nb / J)
@@ -678,10 +663,10 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
     for (; b + 8 <= b1; b += 8) {  // eight loads in flight
       int h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = a.hist[(size_t)(b + i) * E + ej];
+      for (int i = 0; i < 8; ++i) h[i] = ld_shared_dev(a.hist + (size_t)(b + i) * E + ej);
       part += ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
     }
-    for (; b < b1; ++b) part += a.hist[(size_t)b * E + ej];
+    for (; b < b1; ++b) part += ld_shared_dev(a.hist + (size_t)b * E + ej);
   }
   int* jpart = sh.off;  // [J][E] partial sums (J * E <= 1024)
   if (sum_thread) jpart[jj * E + ej] = part;
@@ -706,7 +691,7 @@ __global__ __launch_bounds__(1024) void k_topk_count(RouteArgs a, unsigned* coun
     for (int b = b0; b < b1; b += 8) {
       int hb[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hb[i] = (b + i < b1) ? a.hist[(size_t)(b + i) * E + ej] : 0;
+      for (int i = 0; i < 8; ++i) hb[i] = (b + i < b1) ? ld_shared_dev(a.hist + (size_t)(b + i) * E + ej) : 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (b + i < b1) a.hist[(size_t)(b + i) * E + ej] = run;

@@ -34,7 +34,24 @@ struct RouterArgs {
   float* xsum;           // [T][H/G] sums of x over each group (bf16 path), or null
   int T, H, E, G;
   int router_blocks;     // blocks computing logits (the rest compute xsum); MFMA router: > 0 = logits wanted
+  int rw;                // waves per router row (router_split)
 };
+
+// Router rows: kRouterWaves waves per workgroup, rw of them per row. rw (1, 2, 4
+// or 8) is the smallest that keeps a wave's part of a row within 8 x 64 chunks of
+// 16 bytes (the routing launch of a 7168-wide layer, together with the fence-free
+// arrival of route_dev.h: batch 1 13.3 -> 12.2 us, batch 4 18.8 -> 14.7 us against
+// one wave per row; splitting further, to fill more workgroups, gained less).
+constexpr int kRouterWaves = 8;
+inline int router_split(int H, int act_bf16, int E) {
+  const int nchunk = H * (act_bf16 ? 2 : 4) / 16;
+  int rw = 1;
+  while (rw < 8 && (nchunk + rw - 1) / rw > 8 * 64) rw *= 2;
+  return rw;
+}
+inline int router_blocks_for(int H, int act_bf16, int E) {
+  return (E * router_split(H, act_bf16, E) + kRouterWaves - 1) / kRouterWaves;
+}
 
 // One GEMV work item: an active expert of the current forward, written by the
 // grouping step so that the weight kernels reach both the expert's weights and

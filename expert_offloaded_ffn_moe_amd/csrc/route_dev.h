@@ -19,6 +19,39 @@ __device__ __forceinline__ bool skipped(const RouteArgs& a, bool host) {
   return a.skip_host == 2 || (a.skip_host == 1 && host);
 }
 
+// ----------------------------------------------------------------------------- cross-block hand-off
+
+// Data that one workgroup of a launch writes and the last workgroup to arrive reads
+// (router logits, per-block counts) is stored and loaded as agent-scope relaxed
+// atomics: on gfx950 these are write-through stores and loads that miss the XCD's
+// own L2 (the sc1 forms), coherent across the XCDs without the whole-L2 writeback
+// and invalidate that a release or acquire fence costs. Each workgroup waits for
+// its stores to complete (vmcnt 0) before it increments the arrival counter, so
+// they are performed before the increment; the last arrival reads them afterwards.
+template <typename T>
+__device__ __forceinline__ void st_shared_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_shared_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of a workgroup after its hand-off stores: true in the last
+// workgroup of `n` to arrive. The counter is reset for the next launch on the stream.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned n, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores performed
+  __syncthreads();                // every wave's
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == n - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last && threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
 // ----------------------------------------------------------------------------- top-k
 
 // One wave chooses the k experts of one token, in k rounds. Lane l holds the
@@ -35,7 +68,7 @@ __device__ __forceinline__ void topk_wave_nv(const float* __restrict__ lrow, int
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
+    v[i] = (e < E) ? ld_shared_dev(lrow + min(e, E - 1)) : -INFINITY;
   }
   float my_v = 0.f;
   int my_e = 0;

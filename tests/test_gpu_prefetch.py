@@ -141,7 +141,7 @@ def _run_chain(moe, dims, T, S, P, L, steps, seed, cand, act="bf16", update=None
     return st, n_copied
 
 
-@pytest.mark.parametrize("T,act,cand", [(1, "bf16", 0), (3, "bf16", 6), (2, "f32", 0), (5, "bf16", 0)])
+@pytest.mark.parametrize("T,act,cand", [(1, "bf16", 0), (3, "bf16", 6), (2, "f32", 0), (4, "bf16", 0), (6, "f32", 3)])
 def test_prefetch_follows_the_oracle(moe, T, act, cand):
     dims = (512, 256, 32, 4, 128)
     st, n = _run_chain(moe, dims, T, S=18, P=6, L=3, steps=6, seed=41, cand=cand, act=act)
