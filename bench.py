@@ -75,6 +75,8 @@ def parse_args():
     ap.add_argument("--lowbit-runs", default="mixed:1,mixed:4,hbm:1,host:1",
                     help="plan:batch runs of the DeepSeek-style layers at each lower code width")
     ap.add_argument("--qwen3-layers", type=int, default=24)
+    ap.add_argument("--qwen3-batches", default="1,4", help="batch sizes of the Qwen3-shaped decode runs")
+    ap.add_argument("--prefill-tokens", default="2048,1024", help="micro-batch sizes of the prefill runs")
     ap.add_argument("--prefill-layers", type=int, default=4)
     ap.add_argument("--cache-steps", type=int, default=256)
     ap.add_argument("--max-promotions", type=int, default=8, help="cache run: promotions per layer per update")
@@ -407,12 +409,13 @@ def run_qwen3(args, out):
     d = DIMS["qwen3"]
     L = args.qwen3_layers
     layers = gen_layers("qwen3", L)
-    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=4,
+    batches = [int(v) for v in args.qwen3_batches.split(",") if v]
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "bf16", num_layers=L, max_tokens=max(batches),
                           hbm_slots=d["E"])
     plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"]) for ly in layers])
-    y = torch.empty((4, d["H"]), device="cuda")
+    y = torch.empty((max(batches), d["H"]), device="cuda")
     res = {}
-    for B in (1, 4):
+    for B in batches:
         xs, bits = device_inputs("qwen3", B, min(args.warmup + args.steps, 64))
         el, st, pk = time_steps(plan, L, xs, y[:B], args.steps, args.warmup)
         r = layer_result("qwen3", "qwen3_hbm_b%d" % B, B, "hbm", L, args.steps, args.warmup, el, st, pk, d["E"])
@@ -439,7 +442,7 @@ def run_prefill(args, out):
     y = torch.empty((2048, d["H"]), device="cuda")
     res = {}
     steps = max(4, min(args.steps, 40))
-    for T in (2048, 1024):
+    for T in [int(v) for v in args.prefill_tokens.split(",") if v]:
         xs, bits = device_inputs("prefill", T, 4)
         el, st, pk = time_steps(plan, L, xs, y[:T], steps, min(args.warmup, 5))
         r = layer_result("prefill", "prefill_t%d" % T, T, "hbm", L, steps, min(args.warmup, 5), el, st, pk, d["E"])
