@@ -83,6 +83,17 @@ struct NarrowBatch {
   }
 };
 
+// Workgroups are dealt to the 8 XCDs round-robin by block id, and each XCD has its
+// own L2. The four 16-row tiles of a 64-row block share its 128-byte group-scale
+// lines, so they are given to four blocks of one XCD (ids b, b + 8, b + 16, b + 24)
+// rather than to four neighbouring ids on four XCDs, each of which would fetch
+// every shared line from memory. Needs a multiple of 32 tiles, else identity.
+__device__ __forceinline__ int comb16_tile(int b, int n) {
+  if (n & 31) return b;
+  const int x = b & 7, i = b >> 3;
+  return (((i >> 2) << 3) + x) * 4 + (i & 3);
+}
+
 template <int CPG, bool STAGE>
 __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __restrict__ aptr,
                                                       const int32_t* __restrict__ inv,
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, cl = lane >> 4;
-  const int tile = blockIdx.x, t = blockIdx.y;
+  const int tile = comb16_tile(blockIdx.x, gridDim.x), t = blockIdx.y;
   const int j = wave / splits, sp = wave % splits;
   const uint8_t* base = aptr[t * k + j];
   const int lane_off = (tile & 3) * 16 + r;  // place of row r in its 64-row block
