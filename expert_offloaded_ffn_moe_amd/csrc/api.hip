@@ -172,6 +172,8 @@ struct moe_plan {
   float* hs_o = nullptr;        // [Tmax*k][H]
   std::vector<float> hx, hh;    // packed x rows [Tmax*k][H], h rows [Tmax*k][I]
   hipEvent_t ev_route = nullptr;  // the routing results and x are in the host staging
+  hipEvent_t ev_host_o = nullptr; // the last host part's o copies have read hs_o
+  bool host_o_pending = false;
   // predictive prefetch: its stream, router logits and arrival counter (prefetches of
   // all layers run in order on the one stream), and the caller's point it starts after
   hipStream_t pf_stream = nullptr;
@@ -278,6 +280,7 @@ void free_plan(moe_plan* p) {
     if (e) (void)hipEventDestroy(e);
   if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
   if (p->ev_route) (void)hipEventDestroy(p->ev_route);
+  if (p->ev_host_o) (void)hipEventDestroy(p->ev_host_o);
   if (p->pf_stream) (void)hipStreamDestroy(p->pf_stream);
   if (p->ev_caller) (void)hipEventDestroy(p->ev_caller);
   for (Layer& ly : p->layers)
@@ -876,6 +879,11 @@ moe_status host_part(moe_plan* p, Layer& ly, int T, Workspace& w, hipStream_t s)
   const int32_t* sorted = hr + 3 + 2 * E;
   const int n = ly.host_mode == MOE_HOST_COMPUTE_LAYER ? n_act : n_host;
   if (n <= 0) return MOE_OK;
+  // the previous host part's copies out of hs_o (maybe on another stream) are done
+  if (p->host_o_pending) {
+    HIP_TRY(hipEventSynchronize(p->ev_host_o));
+    p->host_o_pending = false;
+  }
   std::vector<const uint8_t*> blobs(n);
   std::vector<int> M(n), xoff(n);
   int rows = 0;
@@ -905,6 +913,8 @@ moe_status host_part(moe_plan* p, Layer& ly, int T, Workspace& w, hipStream_t s)
   for (int i = 0; i < n; ++i)
     HIP_TRY(hipMemcpyAsync(w.o + (size_t)offsets[active[i]] * H, p->hs_o + (size_t)xoff[i] * H,
                            sizeof(float) * M[i] * H, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipEventRecord(p->ev_host_o, s));
+  p->host_o_pending = true;
   ly.host_computed += n;
   (void)T;
   return MOE_OK;
@@ -1481,9 +1491,10 @@ moe_status moe_plan_set_host_compute(moe_plan* p, int32_t layer, int32_t mode, i
       st = host_alloc(p, &v, sizeof(float) * A * c.hidden, 0);
       if (st != MOE_OK) return st;
       p->hs_o = static_cast<float*>(v);
-      if (!p->ev_route && hipEventCreateWithFlags(&p->ev_route, hipEventDisableTiming) != hipSuccess) {
+      if ((!p->ev_route && hipEventCreateWithFlags(&p->ev_route, hipEventDisableTiming) != hipSuccess) ||
+          (!p->ev_host_o && hipEventCreateWithFlags(&p->ev_host_o, hipEventDisableTiming) != hipSuccess)) {
         (void)hipGetLastError();
-        return fail(MOE_E_HIP, "creating the host-part event failed");
+        return fail(MOE_E_HIP, "creating the host-part events failed");
       }
       try {
         p->hx.assign(A * c.hidden, 0.f);
