@@ -262,9 +262,13 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS>& bt, co
   }
 }
 
-// K loop of one wave over groups [g0, g1) (CPG chunks each) for MT token rows.
-// rows[m]: element offset of token m's activation row in `in`; sum_rows[m]: offset
-// of its per-group (gate/up) or per-chunk (down) sums in insum (bf16 path).
+// K loop of wave `part` of the `parts` waves that split a row tile's K, over the
+// load batches part, part + parts, ... (GB groups of CPG chunks each) of `groups`
+// groups, for MT token rows. rows[m]: element offset of token m's activation row in
+// `in`; sum_rows[m]: offset of its per-group (gate/up) or per-chunk (down) sums in
+// insum (bf16 path). Interleaving the batches makes the waves of a workgroup read
+// neighbouring kilobytes at the same time instead of one distant range each, which
+// the memory serves faster (7168-wide layer, batch 1: gate/up 23.7 -> 21.1 us).
 // Each batch issues all of its loads before its arithmetic. (Issuing the next
 // batch's loads ahead of the current batch's arithmetic measured slower here:
 // the second register set costs more occupancy than the overlap gains; 7168-wide
@@ -273,9 +277,11 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS>& bt, co
 template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4>
 static __device__ __forceinline__ void k_loop(guint4* codes, guint2* his, gushort* scales, const void* __restrict__ in,
                                               const float* __restrict__ insum, const int64_t* rows,
-                                              const int64_t* sum_rows, int mc, int g0, int g1, float* acc) {
+                                              const int64_t* sum_rows, int mc, int part, int parts, int groups,
+                                              float* acc) {
   constexpr int GB = Batch<CPG, BITS>::GB;
-  for (int gb = g0; gb < g1; gb += GB) {
+  const int g1 = groups;
+  for (int gb = part * GB; gb < g1; gb += GB * parts) {
     Batch<CPG, BITS> A;
     A.load(codes, his, scales, gb, g1);
     batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS, BITS>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
@@ -304,7 +310,6 @@ static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, in
                                                      const void* __restrict__ x, const float* __restrict__ xsum,
                                                      void* __restrict__ h, float* __restrict__ hpart, int groups,
                                                      int H, int I, int k) {
-  const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
   for (int m0 = 0; m0 < M; m0 += MT) {
     const int mc = min(MT, M - m0);
     int64_t rows[MT], sum_rows[MT];
@@ -328,9 +333,10 @@ static __device__ __forceinline__ void gateup_expert(float* __restrict__ red, in
       }
       stage_rows(x, src16, mc, len16);
       __syncthreads();
-      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, moe_dyn_lds, xsum, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, moe_dyn_lds, xsum, rows, sum_rows, mc, wave, W, groups,
+                                             acc);
     } else {
-      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, x, xsum, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, false, XS, BITS>(codes, his, scales, x, xsum, rows, sum_rows, mc, wave, W, groups, acc);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[(wave * MT + m) * 64 + lane] = acc[m];
@@ -416,7 +422,6 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   guint2* his = (guint2*)(base + off_hi) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
-  const int g0 = (groups * wave) / W, g1 = (groups * (wave + 1)) / W;
 
   for (int m0 = 0; m0 < M; m0 += MT) {
     const int mc = min(MT, M - m0);
@@ -440,9 +445,10 @@ __global__ __launch_bounds__(kMaxThreads<MT>) void k_down(const WorkDesc* __rest
       }
       stage_rows(h, src16, mc, len16);
       __syncthreads();
-      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, moe_dyn_lds, hpart, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, moe_dyn_lds, hpart, rows, sum_rows, mc, wave, W, groups,
+                                            acc);
     } else {
-      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, h, hpart, rows, sum_rows, mc, g0, g1, acc);
+      k_loop<BF16, MT, CPG, true, XS, BITS>(codes, his, scales, h, hpart, rows, sum_rows, mc, wave, W, groups, acc);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];

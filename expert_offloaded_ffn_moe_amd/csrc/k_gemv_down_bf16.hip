@@ -32,10 +32,9 @@ __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __rest
   p = __builtin_amdgcn_readfirstlane(p);    // and the row stays wave-uniform (scalar loads of h)
   guint4* codes = (guint4*)(base + off_codes) + (size_t)tile * chunks * 64 + lane;
   gushort* scales = (gushort*)(base + off_scales) + (size_t)tile * groups * 64 + lane;
-  const int g0 = (groups * sp) / splits, g1 = (groups * (sp + 1)) / splits;
   int64_t rows[1] = {(int64_t)p * I}, sum_rows[1] = {(int64_t)p * (I / 32)};
   float acc[1] = {0.f};
-  k_loop<1, 1, CPG, true, 0>(codes, nullptr, scales, h, hpart, rows, sum_rows, 1, g0, g1, acc);
+  k_loop<1, 1, CPG, true, 0>(codes, nullptr, scales, h, hpart, rows, sum_rows, 1, sp, splits, groups, acc);
   part[wave][lane] = acc[0];
   __syncthreads();
   if (wave == 0) {
