@@ -48,9 +48,10 @@ DIMS = {
     "qwen3": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.8, seed=1),
     "prefill": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.0, seed=4),
     "cache": dict(H=2048, I=768, E=128, k=8, G=128, alpha=0.8, seed=3),
+    "tiny": dict(H=256, I=128, E=8, k=2, G=32, alpha=0.0, seed=0),
 }
 NAMES = {"deepseek": "DeepSeek-style layer", "qwen3": "Qwen3-30B-A3B-shaped layer",
-         "prefill": "Qwen3-30B-A3B-shaped prefill", "cache": "expert-cache run"}
+         "prefill": "Qwen3-30B-A3B-shaped prefill", "cache": "expert-cache run", "tiny": "tiny layer (fp32 activations)"}
 
 
 def log(*a):
@@ -62,7 +63,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100, help="timed steps per decode/prefill measurement")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="deepseek,qwen3,prefill,cache",
+    ap.add_argument("--only", default="deepseek,qwen3,prefill,cache,tiny",
                     help="comma list of the workloads to run (the first one run gives the top-level line)")
     ap.add_argument("--deepseek-layers", type=int, default=4)
     ap.add_argument("--deepseek-runs", default="mixed:1,mixed:4,mixed:16,hbm:1,hbm:4,hbm:16,host:1,host:4,host:16",
@@ -276,12 +277,13 @@ def cpu_cores():
 
 
 def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwards=1, label=None, threads=None,
-                 bits=4):
+                 bits=4, act="bf16"):
     """The CPU oracle (float64 NumPy, unmodified) on a bounded sample of the same
     workload: forwards of the given batches through the first two layers, until
     `seconds` have passed (at least one). tokens: evaluate y only for these token rows of
     each batch (routing still covers all), with the rate scaled to those rows. BLAS
     threads are pinned to the cores this process may run on (or to `threads`)."""
+    import numpy as np
     import threadpoolctl
     from oracle import moe_oracle as O
     d = DIMS[wl]
@@ -292,8 +294,9 @@ def cpu_baseline(wl, layers, batches_bits, seconds, tokens=None, per_step_forwar
         while n == 0 or time.perf_counter() - t0 < seconds:
             ly = layers[n % n_l]
             xb = batches_bits[n % len(batches_bits)]
-            O.layer_forward(O.bf16_bits_to_f64(xb), O.bf16_bits_to_f64(ly["Wr"]), ly["b"], ly["blobs"], d["H"],
-                            d["I"], d["E"], d["k"], d["G"], "bf16", tokens=tokens, bits=bits)
+            widen = O.bf16_bits_to_f64 if act == "bf16" else (lambda v: v.astype(np.float64))
+            O.layer_forward(widen(xb), widen(ly["Wr"]), ly["b"], ly["blobs"], d["H"], d["I"], d["E"], d["k"], d["G"],
+                            act, tokens=tokens, bits=bits)
             done_tokens += len(tokens) if tokens is not None else xb.shape[0]
             n += 1
     el = time.perf_counter() - t0
@@ -412,6 +415,32 @@ def run_deepseek(args, out):
                 res[key]["cpu_baseline"] = cb
     out.update(res)
     return {"plan_info": info}
+
+
+def run_tiny(args, out):
+    """The tiny layer (H256 I128 E8 k2 G32, fp32 activations, 16 tokens, all resident):
+    a correctness-sized case, timed with the CPU oracle on all of its tokens beside it."""
+    import torch
+    import expert_offloaded_ffn_moe_amd as moe
+    import synth
+    d = DIMS["tiny"]
+    T = 16
+    ly = dict(Wr=synth.router_weight(d["seed"], 0, d["E"], d["H"], "f32"),
+              b=synth.router_bias(d["seed"], 0, d["E"], d["alpha"]),
+              blobs=synth.expert_blobs(d["seed"], 0, 0, d["E"], d["H"], d["I"], d["G"]))
+    cfg = moe.make_config(d["H"], d["I"], d["E"], d["k"], d["G"], "f32", max_tokens=T, hbm_slots=d["E"])
+    plan = moe.Plan(cfg, layers=[(ly["Wr"], ly["b"], ly["blobs"])])
+    bits = [synth.activations(d["seed"], 1000 + i, T, d["H"], "f32") for i in range(8)]
+    xs = [torch.from_numpy(b.copy()).cuda() for b in bits]
+    y = torch.empty((T, d["H"]), device="cuda")
+    el, st, pk = time_steps(plan, 1, xs, y, args.steps, args.warmup)
+    plan.destroy()
+    r = layer_result("tiny", "tiny_t16", T, "hbm", 1, args.steps, args.warmup, el, st, pk, d["E"])
+    log("tiny T16: %.0f layer-tokens/s" % r["value"])
+    if not args.no_cpu:
+        r["cpu_baseline"] = cpu_baseline("tiny", [ly], bits[:4], args.cpu_seconds, act="f32",
+                                         label="every token of each 16-token batch")
+    out["tiny_t16"] = r
 
 
 def run_qwen3(args, out):
@@ -602,8 +631,14 @@ def topology():
         numa = [ln.strip() for ln in txt.splitlines() if "Numa" in ln or "NUMA" in ln]
     except Exception as e:  # rocm-smi is only informative here
         numa = ["rocm-smi --showtopo unavailable: %s" % e]
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        clocks = [ln.strip() for ln in txt.splitlines() if "clk" in ln.lower()]
+    except Exception as e:  # informative only
+        clocks = ["rocm-smi --showclocks unavailable: %s" % e]
     nodes = sorted(glob.glob("/sys/devices/system/node/node[0-9]*"))
-    return {"host_numa_nodes": len(nodes), "rocm_smi_numa": numa[:8], "cpu_cores_available": cpu_cores()}
+    return {"host_numa_nodes": len(nodes), "rocm_smi_numa": numa[:8], "rocm_smi_clocks_at_start": clocks[:8],
+            "cpu_cores_available": cpu_cores()}
 
 
 def main():
@@ -644,12 +679,13 @@ def main():
     configs = {}
     order = [w.strip() for w in args.only.split(",") if w.strip()]
     for wl in order:
-        r = {"deepseek": run_deepseek, "qwen3": run_qwen3, "prefill": run_prefill, "cache": run_cache}[wl](
+        r = {"deepseek": run_deepseek, "qwen3": run_qwen3, "prefill": run_prefill, "cache": run_cache,
+             "tiny": run_tiny}[wl](
             args, configs)
         if r:
             extra.update(r)
     head_key = {"deepseek": "deepseek_mixed_b1", "qwen3": "qwen3_hbm_b1", "prefill": "prefill_t2048",
-                "cache": "cache_48_layers"}[order[0]]
+                "cache": "cache_48_layers", "tiny": "tiny_t16"}[order[0]]
     if head_key not in configs:  # a subset of runs: the first one measured heads the line
         head_key = next(iter(configs))
     head = configs[head_key]
