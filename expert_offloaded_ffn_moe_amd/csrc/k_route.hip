@@ -437,12 +437,13 @@ __device__ __forceinline__ void align_small(const RouteArgs& a, DecodeShared& sh
 }
 
 
-// Decode routing in one launch. Blocks [0, router_blocks): 8 expert rows each
-// (one per wave); then xsum blocks; every block then arrives on the counter,
-// and the last one (which sees every other block's logits after the
-// device-scope fences) picks the top-k of every token (one wave per token) and
-// groups the assignments with all of its threads.
-// NCH: 16-byte chunks of a router row per lane (1, 2, 4, 8, 16; 0 = longer rows).
+// Decode routing in one launch. Blocks [0, router_blocks): kRouterWaves / rw expert
+// rows each (rw waves per row); then xsum blocks; every block then arrives on the
+// counter, and the last one (which reads every other block's logits with loads that
+// miss its L2, after their write-through stores: no fences) picks the top-k of
+// every token (one wave per token) and groups the assignments with its waves.
+// NCH: 16-byte chunks per lane of a wave's part of a router row (1, 2, 4, 8; 0 =
+// longer parts).
 // One instance per row length, so the kernel's registers are those of its own
 // router path (the longest rows' path needs more of them than the tail).
 template <int BF16, int NCH>
