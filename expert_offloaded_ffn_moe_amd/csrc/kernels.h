@@ -43,6 +43,7 @@ struct RouterArgs {
 // arrival of route_dev.h: batch 1 13.3 -> 12.2 us, batch 4 18.8 -> 14.7 us against
 // one wave per row; splitting further, to fill more workgroups, gained less).
 constexpr int kRouterWaves = 8;
+constexpr int kMfmaRouterMinTiles = 64;  // logits tiles (32 x 32) from which the MFMA router is used
 inline int router_split(int H, int act_bf16, int E) {
   const int nchunk = H * (act_bf16 ? 2 : 4) / 16;
   int rw = 1;
