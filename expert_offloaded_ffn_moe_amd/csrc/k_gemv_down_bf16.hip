@@ -60,21 +60,28 @@ __global__ __launch_bounds__(1024) void k_down_comb(const uint8_t* const* __rest
 // staged once per workgroup in LDS (their global loads issued together with the
 // first code loads); shorter rows are read straight from global memory, where
 // they stay in cache (measured: I = 768, batch 1: 8.4 -> 7.5 us without the
-// staging; I = 2048: 16.9 -> 15.3 us with it). Per chunk:
+// staging; I = 2048: 16.9 -> 15.3 us with it; reading the k sorted positions once
+// and issuing the chunk-sum loads with the h loads: 15.6 -> 14.5 us on the
+// 7168-wide layer, batch 1). Each lane keeps IT chunk loads in flight besides the
+// IT it computes on: IT = 2, or 1 where a lane has at most four chunk iterations.
+// More measured slower (7168-wide layer, batch 1, 8 iterations: 14.5 us at four,
+// 13.2 us at two, 17.3 us with all eight issued before the staging; 2048-wide,
+// batch 4, 6 iterations: 10.6 us at four, 9.1 at two, 9.5 at one; batch 1, 3
+// iterations: 7.2 us at two, 6.6 at one). Per chunk:
 //   part += 16 s (sum v h - 1.5 sum h),  v = 1 + n/16,
 // then the four chunk lanes of a row are added (lanes r, r+16, r+32, r+48, in
 // a fixed tree), the S waves of a slot and the k slots meet in LDS, and
 //   y[t][r] = sum over j = 0..k-1, in order, of w_j * (sum over s of part[j][s][r]).
-constexpr int kNarrowIt = 4;     // chunks per lane whose code loads are issued together
-constexpr int kNarrowStage = 8;  // h units (16 bytes) per thread staged from registers
+constexpr int kNarrowStage = 2;  // h units (16 bytes) per thread and pass staged from registers
 
-template <int CPG>
+// IT: chunks per lane whose code loads are issued together
+template <int CPG, int IT>
 struct NarrowBatch {
-  u32x4 wv[kNarrowIt];
-  uint16_t sc[kNarrowIt];
+  u32x4 wv[IT];
+  uint16_t sc[IT];
   __device__ __forceinline__ void load(guint4* codes, gushort* scales, int cfirst, int c1) {
 #pragma unroll
-    for (int i = 0; i < kNarrowIt; ++i) {
+    for (int i = 0; i < IT; ++i) {
       const int c = min(cfirst + 4 * i, c1 - 1);
       wv[i] = codes[(size_t)c * 64];
       sc[i] = scales[(size_t)(c / CPG) * 64];
@@ -93,7 +100,7 @@ __device__ __forceinline__ int comb16_tile(int b, int n) {
   return (((i >> 2) << 3) + x) * 4 + (i & 3);
 }
 
-template <int CPG, bool STAGE>
+template <int CPG, bool STAGE, int IT>
 __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __restrict__ aptr,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ wts, const void* __restrict__ h,
@@ -114,24 +121,31 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
   const int c0 = (chunks * sp) / splits, c1 = (chunks * (sp + 1)) / splits;
   const int n_it = (c1 - c0 + 3) >> 2;  // chunk iterations of the wave (lanes past c1 count 0)
 
-  NarrowBatch<CPG> cur;
+  // the first load batch goes out before the h staging, each next one while the
+  // previous one computes
+  NarrowBatch<CPG, IT> cur;
   if (n_it > 0) cur.load(codes, scales, c0 + cl, c1);
 
   const uint4* hrow;
   const float* hs_row;
   if (STAGE) {
-    // stage h rows [k][I] (bf16, 16-byte units) and chunk sums [k][I/32] of token t
-    const int units = I / 8, n_units = k * units, nsum = I / 32;
+    // stage h rows [k][I] (bf16, 16-byte units) and chunk sums [k][I/32] of token t:
+    // the k sorted positions are read once (one lane each) and shared by shuffles,
+    // then the h and chunk-sum loads of the first pass go out together
+    const int units = I / 8, n_units = k * units, nsum = I / 32, n_sums = k * nsum;
     uint4* hl = moe_dyn_lds;
     float* hsl = reinterpret_cast<float*>(moe_dyn_lds + n_units);
     const uint4* h4 = static_cast<const uint4*>(h);
     const int nthr = blockDim.x;
+    const int pos = inv[t * k + min(lane, k - 1)];
+    const int si = min((int)threadIdx.x, n_sums - 1);
+    const float hs0 = hpart[(size_t)__shfl(pos, si / nsum, 64) * nsum + si % nsum];
     for (int u0 = 0; u0 < n_units; u0 += kNarrowStage * nthr) {
       uint4 hv[kNarrowStage];
 #pragma unroll
       for (int i = 0; i < kNarrowStage; ++i) {
         const int u = min(u0 + (int)threadIdx.x + i * nthr, n_units - 1);
-        hv[i] = h4[(size_t)inv[t * k + u / units] * units + u % units];
+        hv[i] = h4[(size_t)__shfl(pos, u / units, 64) * units + u % units];
       }
 #pragma unroll
       for (int i = 0; i < kNarrowStage; ++i) {
@@ -139,8 +153,9 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
         if (u < n_units) hl[u] = hv[i];
       }
     }
-    for (int i = threadIdx.x; i < k * nsum; i += nthr)
-      hsl[i] = hpart[(size_t)inv[t * k + i / nsum] * nsum + i % nsum];
+    if ((int)threadIdx.x < n_sums) hsl[threadIdx.x] = hs0;
+    for (int i = threadIdx.x + nthr; i < n_sums; i += nthr)
+      hsl[i] = hpart[(size_t)__shfl(pos, i / nsum, 64) * nsum + i % nsum];
     __syncthreads();
     hrow = hl + j * units;
     hs_row = hsl + j * nsum;
@@ -150,11 +165,10 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
     hs_row = hpart + (size_t)p * (I / 32);
   }
   float acc = 0.f;
-  for (int ib = 0; ib < n_it; ib += kNarrowIt) {
-    NarrowBatch<CPG> nxt;
-    if (ib + kNarrowIt < n_it) nxt.load(codes, scales, c0 + cl + 4 * (ib + kNarrowIt), c1);
+  // chunk iterations ib .. ib + IT - 1 of batch bt
+  auto math = [&](const NarrowBatch<CPG, IT>& bt, int ib) {
 #pragma unroll
-    for (int i = 0; i < kNarrowIt; ++i) {
+    for (int i = 0; i < IT; ++i) {
       const int c = c0 + cl + 4 * (ib + i);
       const int cc = min(c, c1 - 1);
       uint32_t xw[16];
@@ -166,10 +180,15 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
         xw[4 * q + 2] = v.z;
         xw[4 * q + 3] = v.w;
       }
-      const float d = chunk_dot_bf16(cur.wv[i], xw, 0.f);
-      const float sc = (c < c1) ? 16.f * half_bits(cur.sc[i]) : 0.f;
+      const float d = chunk_dot_bf16(bt.wv[i], xw, 0.f);
+      const float sc = (c < c1) ? 16.f * half_bits(bt.sc[i]) : 0.f;
       acc = fmaf(sc, d - 1.5f * hs_row[cc], acc);
     }
+  };
+  for (int ib = 0; ib < n_it; ib += IT) {
+    NarrowBatch<CPG, IT> nxt;
+    if (ib + IT < n_it) nxt.load(codes, scales, c0 + cl + 4 * (ib + IT), c1);
+    math(cur, ib);
     cur = nxt;
   }
   acc += __shfl_xor(acc, 16, 64);
@@ -195,13 +214,18 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
   const dim3 grid(a.H / 16, a.T), block(64 * a.k * a.splits);
   const bool stage = a.I > 1024;
   const size_t lds = stage ? down_combine16_lds(a.k, a.I) : 0;
-#define DOWN_COMB16(C)                                                                                               \
-  if (stage)                                                                                                         \
-    launch_timed(k_down_comb16<C, true>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, a.xout, \
-                 a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);                            \
-  else                                                                                                               \
-    launch_timed(k_down_comb16<C, false>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, a.xout, \
-                 a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits);
+  // one chunk load per lane in flight when a lane has at most four chunk iterations,
+  // else two
+  const int per_wave = (a.chunks + a.splits - 1) / a.splits;
+  const bool one = (per_wave + 3) / 4 <= 4;
+#define DOWN_COMB16_K(C, ST, IT)                                                                                  \
+  launch_timed(k_down_comb16<C, ST, IT>, grid, block, lds, s, tm, a.aptr, a.inv, a.wts, a.h, a.hpart, a.y, a.xres, \
+               a.xout, a.off_codes, a.off_scales, a.chunks, a.groups, a.H, a.I, a.k, a.splits)
+#define DOWN_COMB16(C)                                         \
+  if (stage)                                                   \
+    one ? DOWN_COMB16_K(C, true, 1) : DOWN_COMB16_K(C, true, 2);  \
+  else                                                         \
+    one ? DOWN_COMB16_K(C, false, 1) : DOWN_COMB16_K(C, false, 2);
   switch (a.G / 32) {
     case 1: DOWN_COMB16(1); break;
     case 2: DOWN_COMB16(2); break;
@@ -209,6 +233,7 @@ void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t 
     default: DOWN_COMB16(8); break;
   }
 #undef DOWN_COMB16
+#undef DOWN_COMB16_K
 }
 
 void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s) {

@@ -107,6 +107,8 @@ SMALL = [
     (512, 256, 16, 4, 128, "f32", 2, 0.0, 22),    # fp32 rows, experts holding 2 tokens (4-token kernel)
     (1024, 2048, 16, 4, 128, "bf16", 1, 0.5, 23),  # 16-row fused down + combine with h staged in LDS (I > 1024)
     (512, 1280, 8, 2, 64, "bf16", 3, 0.0, 24),    # the same, G = 64, 5 chunks per wave (ragged chunk quarters)
+    (1024, 2048, 16, 6, 128, "bf16", 1, 0.5, 25),  # staged, both 4-chunk load batches issued before the staging
+    (1024, 2048, 16, 10, 128, "bf16", 1, 0.5, 26),  # staged, 16 chunk iterations per lane: batches pipelined
 ]
 
 
