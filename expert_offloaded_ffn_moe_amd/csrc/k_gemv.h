@@ -189,9 +189,9 @@ static __device__ __forceinline__ float chunk_dot_f32_src(const u32x4& wv, const
 // One batch: kBatch code chunks (GB groups) and their scales (and, for 3-bit codes,
 // the chunks' high-plane words), loaded unconditionally with indices clamped to the
 // wave's last chunk/group (repeats hit in cache).
-template <int CPG, int BITS = 4>
+template <int CPG, int BITS = 4, int NBATCH = kBatch>
 struct Batch {
-  static constexpr int NB = CPG > kBatch ? CPG : kBatch;
+  static constexpr int NB = CPG > NBATCH ? CPG : NBATCH;
   static constexpr int GB = NB / CPG;
   u32x4 wv[NB];
   u32x2 hv[BITS == 3 ? NB : 1];
@@ -214,13 +214,13 @@ struct Batch {
 
 // Arithmetic of one batch starting at group gb: groups past g1 repeat the last
 // group and count with weight 0 (no branch, so loads issued earlier stay ahead).
-template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4>
-static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS>& bt, const void* __restrict__ in,
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4, int NBATCH = kBatch>
+static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS, NBATCH>& bt, const void* __restrict__ in,
                                                   const float* __restrict__ insum, const int64_t* rows,
                                                   const int64_t* sum_rows, int mc, int gb, int g1, float* acc) {
   constexpr int SPG = CPG * kChunkK<BITS> / 32;  // 32-value sums (down: h chunk sums) per group
 #pragma unroll
-  for (int q = 0; q < Batch<CPG, BITS>::GB; ++q) {
+  for (int q = 0; q < Batch<CPG, BITS, NBATCH>::GB; ++q) {
     const int g = min(gb + q, g1 - 1);
     const float keep = (gb + q < g1) ? 1.f : 0.f;
     float accg[MT];
@@ -274,17 +274,17 @@ static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS>& bt, co
 // the second register set costs more occupancy than the overlap gains; 7168-wide
 // layer, batch 1, gate/up: 23.3 -> 26.8 us. Batches of 16 chunks for one token
 // also lost: 23.9 -> 24.8 us there, and 6.7 -> 9.0 us on a 2048-wide layer.)
-template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4>
+template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4, int NBATCH = kBatch>
 static __device__ __forceinline__ void k_loop(guint4* codes, guint2* his, gushort* scales, const void* __restrict__ in,
                                               const float* __restrict__ insum, const int64_t* rows,
                                               const int64_t* sum_rows, int mc, int part, int parts, int groups,
                                               float* acc) {
-  constexpr int GB = Batch<CPG, BITS>::GB;
+  constexpr int GB = Batch<CPG, BITS, NBATCH>::GB;
   const int g1 = groups;
   for (int gb = part * GB; gb < g1; gb += GB * parts) {
-    Batch<CPG, BITS> A;
+    Batch<CPG, BITS, NBATCH> A;
     A.load(codes, his, scales, gb, g1);
-    batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS, BITS>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
+    batch_math<BF16, MT, CPG, SUMS_PER_CHUNK, XS, BITS, NBATCH>(A, in, insum, rows, sum_rows, mc, gb, g1, acc);
   }
 }
 
