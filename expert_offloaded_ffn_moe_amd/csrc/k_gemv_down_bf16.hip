@@ -169,6 +169,7 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
     hs_row = hpart + (size_t)p * (I / 32);
   }
   float acc = 0.f;
+  const PairConsts pk;
   // chunk iterations ib .. ib + IT - 1 of batch bt
   auto math = [&](const NarrowBatch<CPG, IT>& bt, int ib) {
 #pragma unroll
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(1024) void k_down_comb16(const uint8_t* const* __re
         xw[4 * q + 2] = v.z;
         xw[4 * q + 3] = v.w;
       }
-      const float d = chunk_dot_bf16(bt.wv[i], xw, 0.f);
+      const float d = chunk_dot_bf16(bt.wv[i], xw, 0.f, pk);
       const float sc = (c < c1) ? 16.f * half_bits(bt.sc[i]) : 0.f;
       acc = fmaf(sc, d - 1.5f * hs_row[cc], acc);
     }

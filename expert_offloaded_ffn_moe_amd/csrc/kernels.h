@@ -205,7 +205,7 @@ void launch_down_combine(const DownCombArgs& a, const Timing& tm, hipStream_t s)
 void launch_down_combine16(const DownCombArgs& a, const Timing& tm, hipStream_t s);  // bf16, k * splits <= 16
 size_t down_combine16_lds(int k, int I);  // dynamic LDS bytes of launch_down_combine16
 constexpr size_t kDownComb16MaxLds = 48 * 1024;
-constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count, at least
+constexpr int kDownComb16WavesPerCU = 24;  // resident waves per CU at its register count (20-32 by variant)
 void launch_stage(StageArgs a, const Timing& tm, hipStream_t s);
 // router (unless r.router_blocks == 0) + prediction, then the copies and the table entries
 void launch_prefetch(PrefetchArgs a, const RouterArgs& r, int act_bf16, unsigned* counter, hipStream_t s);
