@@ -56,13 +56,23 @@ static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // kernel builds them once, before its K loop, and passes them down: the compiler does
 // not merge separate constructions, and then would not share one pair's conversion
 // among the token rows that use it.
-struct PairConsts {
-  uint32_t m, c;
-  __device__ __forceinline__ PairConsts() {
-    asm("v_mov_b32 %0, 0x00780078" : "=v"(m));
+// The 2- and 3-bit codes use the same form with their own masks: m selects the low two
+// bits of both halves' codes at their mantissa places, mh the third bit of 3-bit codes.
+template <int BITS>
+struct CodeConsts {
+  uint32_t m, c, mh;
+  __device__ __forceinline__ CodeConsts() {
+    if (BITS == 4)
+      asm("v_mov_b32 %0, 0x00780078" : "=v"(m));
+    else if (BITS == 3)
+      asm("v_mov_b32 %0, 0x00300030" : "=v"(m));
+    else
+      asm("v_mov_b32 %0, 0x00600060" : "=v"(m));
     asm("v_mov_b32 %0, 0x3f803f80" : "=v"(c));
+    asm("v_mov_b32 %0, 0x00400040" : "=v"(mh));
   }
 };
+typedef CodeConsts<4> PairConsts;
 
 // bf16 pair (1 + n_lo/16, 1 + n_hi/16) of pair j of a code dword
 static __device__ __forceinline__ uint32_t pair0(uint32_t d, const PairConsts& k) { return ((d << 3) & k.m) | k.c; }
@@ -139,7 +149,8 @@ static __device__ __forceinline__ uint32_t shift_by(uint32_t x, int sh) { return
 // (values 16d+2j, 16d+2j+1) against x pair 8d+j; for 3-bit codes the third bit of
 // that pair is bit i = 8 (d & 1) + j (and 16 + i) of high-plane dword d >> 1.
 template <int BITS, typename P>
-static __device__ __forceinline__ float chunk_dot_bf16_low(const u32x4& wv, const u32x2& hv, const P& xr, float acc) {
+static __device__ __forceinline__ float chunk_dot_bf16_low(const u32x4& wv, const u32x2& hv, const P& xr, float acc,
+                                                           const CodeConsts<BITS>& k) {
   const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
   const uint32_t h[2] = {hv.x, hv.y};
   constexpr int kDst = BITS == 2 ? 5 : 4;  // mantissa bit of the code's lowest bit
@@ -147,8 +158,8 @@ static __device__ __forceinline__ float chunk_dot_bf16_low(const u32x4& wv, cons
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t v = (shift_by(w[d], kDst - 2 * j) & ((3u << kDst) | (3u << (16 + kDst)))) | 0x3F803F80u;
-      if (BITS == 3) v |= shift_by(h[d >> 1], 6 - (8 * (d & 1) + j)) & 0x00400040u;
+      uint32_t v = (shift_by(w[d], kDst - 2 * j) & k.m) | k.c;  // k.m = (3 << kDst) | (3 << (16 + kDst))
+      if (BITS == 3) v |= shift_by(h[d >> 1], 6 - (8 * (d & 1) + j)) & k.mh;
       acc = dot2(v, xr[8 * d + j], acc);
     }
   }
@@ -175,19 +186,19 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 // memory (wave-uniform address, scalar loads), XS == 1 from the LDS copy.
 template <int XS, int BITS = 4>
 static __device__ __forceinline__ float chunk_dot_bf16_src(const u32x4& wv, const u32x2& hv, const void* in,
-                                                           int64_t row, int c, float acc, const PairConsts& k) {
+                                                           int64_t row, int c, float acc, const CodeConsts<BITS>& k) {
   constexpr int NX = kChunkK<BITS> / 2;  // x pairs per lane word
   if (XS) {
     lds_u32* xr = (lds_u32*)in + row / 2 + c * NX;
     uint32_t v[NX];
 #pragma unroll
     for (int i = 0; i < NX; ++i) v[i] = xr[i];
-    if (BITS == 4) return chunk_dot_bf16(wv, v, acc, k);
-    return chunk_dot_bf16_low<BITS>(wv, hv, v, acc);
+    if constexpr (BITS == 4) return chunk_dot_bf16(wv, v, acc, k);
+    else return chunk_dot_bf16_low<BITS>(wv, hv, v, acc, k);
   }
   const uint32_t* xg = static_cast<const uint32_t*>(in) + row / 2 + c * NX;
-  if (BITS == 4) return chunk_dot_bf16(wv, xg, acc, k);
-  return chunk_dot_bf16_low<BITS>(wv, hv, xg, acc);
+  if constexpr (BITS == 4) return chunk_dot_bf16(wv, xg, acc, k);
+  else return chunk_dot_bf16_low<BITS>(wv, hv, xg, acc, k);
 }
 
 template <int XS>
@@ -235,7 +246,7 @@ template <int BF16, int MT, int CPG, bool SUMS_PER_CHUNK, int XS, int BITS = 4, 
 static __device__ __forceinline__ void batch_math(const Batch<CPG, BITS, NBATCH>& bt, const void* __restrict__ in,
                                                   const float* __restrict__ insum, const int64_t* rows,
                                                   const int64_t* sum_rows, int mc, int gb, int g1, float* acc,
-                                                  const PairConsts& k) {
+                                                  const CodeConsts<BITS>& k) {
   constexpr int SPG = CPG * kChunkK<BITS> / 32;  // 32-value sums (down: h chunk sums) per group
 #pragma unroll
   for (int q = 0; q < Batch<CPG, BITS, NBATCH>::GB; ++q) {
@@ -299,7 +310,7 @@ static __device__ __forceinline__ void k_loop(guint4* codes, guint2* his, gushor
                                               float* acc) {
   constexpr int GB = Batch<CPG, BITS, NBATCH>::GB;
   const int g1 = groups;
-  const PairConsts k;
+  const CodeConsts<BITS> k;
   for (int gb = part * GB; gb < g1; gb += GB * parts) {
     Batch<CPG, BITS, NBATCH> A;
     A.load(codes, his, scales, gb, g1);
