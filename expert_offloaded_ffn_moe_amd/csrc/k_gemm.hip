@@ -39,9 +39,9 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 }
 
 // The nibble mask 0x00780078 and the bf16 pair 1.0, 1.0 = 0x3F803F80, in vector registers.
-struct CodeConsts {
+struct GemmCodeConsts {
   uint32_t m, c;
-  __device__ __forceinline__ CodeConsts() {
+  __device__ __forceinline__ GemmCodeConsts() {
     asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(m));
     asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(c));
   }
@@ -50,7 +50,7 @@ struct CodeConsts {
 // 8 codes of one dword (K offsets 8d .. 8d+7 in order) -> bf16x8 of 1 + n/16:
 // pair j of the dword moved to mantissa bits 3..6 of both halves, then masked
 // and or-ed into 1.0
-__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d, const CodeConsts& k) {
+__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d, const GemmCodeConsts& k) {
   u32x4 p;
   p.x = and_or(d << 3, k.m, k.c);
   p.y = and_or(d >> 1, k.m, k.c);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* const* __restric
     const int64_t row = GATEUP ? (int64_t)(sorted[p0 + m0 + r] / k) : (int64_t)(p0 + m0 + r);
     src[q] = reinterpret_cast<const uint4*>(a_src + row * K) + spiece;
   }
-  const CodeConsts kc;
+  const GemmCodeConsts kc;
 
   const uint8_t* base = wptr[e];
   gu32x4* codes = (gu32x4*)(base + off_codes) + (size_t)(active_wave ? nt : 0) * chunks * 64 + lane;
